@@ -1,0 +1,405 @@
+// Host side of libfs: argument validation, launch planning, workspace layout
+// and the extern "C" entry points declared in include/fs.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "fs.h"
+#include "fs_internal.h"
+
+namespace {
+
+using namespace fs;
+
+constexpr int kDefaultTileV = 128;
+constexpr int kMaxTopK = 64;
+constexpr int kMultinomialChunk = 2048;
+constexpr int kMaxB = 1 << 20;
+constexpr size_t kAlign = 256;
+
+struct DeviceInfo {
+    bool ok = false;      // a gfx950 device
+    int cus = 0;
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[64];
+bool g_dev_init[64];
+
+// Workgroups per compute unit along the vocabulary; FS_WG_PER_CU overrides
+// the default for tuning experiments.
+int wg_per_cu() {
+    static int v = [] {
+        const char* e = std::getenv("FS_WG_PER_CU");
+        int x = e ? std::atoi(e) : 0;
+        return (x >= 1 && x <= 16) ? x : 2;
+    }();
+    return v;
+}
+
+bool current_device(DeviceInfo& out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return false;
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_dev_init[dev]) {
+        DeviceInfo info;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            info.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            info.cus = prop.multiProcessorCount;
+        } else {
+            (void)hipGetLastError();
+        }
+        g_dev[dev] = info;
+        g_dev_init[dev] = true;
+    }
+    out = g_dev[dev];
+    return out.ok && out.cus > 0;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Validated shape of one call and its launch plan.
+struct Plan {
+    int B, d, V, n_valid, v_offset, tile_v, tile_mb, T, nmb, G;
+    Stage1Config cfg;
+    int grid_y;
+    uint32_t k0, k1;
+};
+
+fs_status check_params(const fs_params* p) {
+    if (!p) return FS_ERR_INVALID_ARG;
+    if (p->B < 0 || p->d < 0 || p->V < 0 || p->v_offset < 0 || p->tile_v < 0)
+        return FS_ERR_INVALID_ARG;
+    if (p->B > kMaxB) return FS_ERR_UNSUPPORTED;
+    if ((int64_t)p->v_offset + p->V > INT32_MAX) return FS_ERR_INVALID_ARG;
+    if (p->d % 8 != 0) return FS_ERR_UNSUPPORTED;
+    if (p->v_offset % kMBlock != 0) return FS_ERR_UNSUPPORTED;
+    if (p->tile_v % kMBlock != 0) return FS_ERR_UNSUPPORTED;
+    if (p->flags & ~kFlagNoNoise) return FS_ERR_INVALID_ARG;
+    return FS_OK;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+Stage1Config pick_config(int variant, int B) {
+    if (variant == kVarTopk) return B <= 16 ? Stage1Config{1, 4} : Stage1Config{2, 4};
+    if (B <= 16) return Stage1Config{1, 4};
+    if (B <= 32) return Stage1Config{2, 4};
+    return Stage1Config{4, 2};
+}
+
+void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
+    pl.B = p->B;
+    pl.d = p->d;
+    pl.V = p->V;
+    pl.n_valid = p->n_valid;
+    pl.v_offset = p->v_offset;
+    pl.tile_v = p->tile_v ? p->tile_v : kDefaultTileV;
+    pl.T = (p->V + pl.tile_v - 1) / pl.tile_v;
+    pl.nmb = (p->V + kMBlock - 1) / kMBlock;
+    pl.tile_mb = (variant == kVarGrouped) ? pl.tile_v / kMBlock : INT32_MAX / 2;
+    pl.G = std::max(1, std::min(pl.nmb, cus * wg_per_cu()));
+    pl.cfg = pick_config(variant, p->B);
+    pl.grid_y = (p->B + 16 * pl.cfg.nb - 1) / (16 * pl.cfg.nb);
+    pl.k0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
+    pl.k1 = (uint32_t)(p->seed >> 32);
+}
+
+// Workspace layout per variant (each array 256-byte aligned).
+struct Workspace {
+    float* pm = nullptr;
+    int32_t* pidx = nullptr;
+    float* pL = nullptr;
+    float* cx = nullptr;
+    float* cs = nullptr;
+    int32_t* cidx = nullptr;
+    float* mm = nullptr;
+    float* ms = nullptr;
+    uint64_t* mkey = nullptr;
+};
+
+size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* r = base ? base + off : nullptr;
+        off = align_up(off + bytes);
+        return r;
+    };
+    const size_t B = (size_t)pl.B;
+    if (variant == FS_VARIANT_FLAT || variant == FS_VARIANT_GROUPED) {
+        const size_t P = variant == FS_VARIANT_FLAT ? (size_t)pl.G : (size_t)pl.G + pl.T - 1;
+        char* a = take(P * B * 4);
+        char* b = take(P * B * 4);
+        char* c = variant == FS_VARIANT_GROUPED ? take(P * B * 4) : nullptr;
+        if (w) { w->pm = (float*)a; w->pidx = (int32_t*)b; w->pL = (float*)c; }
+    } else if (variant == FS_VARIANT_TOPK) {
+        const size_t n = (size_t)pl.G * B * (size_t)k;
+        char* a = take(n * 4);
+        char* b = take(n * 4);
+        char* c = take(n * 4);
+        if (w) { w->cx = (float*)a; w->cs = (float*)b; w->cidx = (int32_t*)c; }
+    } else if (variant == FS_VARIANT_MULTINOMIAL) {
+        const size_t nchunk = (size_t)(pl.V + kMultinomialChunk - 1) / kMultinomialChunk;
+        char* a = take(nchunk * B * 4);
+        char* b = take(nchunk * B * 4);
+        char* c = take(nchunk * B * 8);
+        if (w) { w->mm = (float*)a; w->ms = (float*)b; w->mkey = (uint64_t*)c; }
+    }
+    return off;
+}
+
+fs_status from_hip(hipError_t e) { return e == hipSuccess ? FS_OK : FS_ERR_HIP; }
+
+Stage1Args stage1_args(const Plan& pl, const fs_params* p, const void* H, const void* W,
+                       const float* temp, const uint32_t* allow) {
+    Stage1Args a{};
+    a.H = static_cast<const uint16_t*>(H);
+    a.W = static_cast<const uint16_t*>(W);
+    a.temp = temp;
+    a.allow = allow;
+    a.B = pl.B;
+    a.d = pl.d;
+    a.V = pl.V;
+    a.n_valid = pl.n_valid;
+    a.v_offset = pl.v_offset;
+    a.nmb = pl.nmb;
+    a.G = pl.G;
+    a.tile_mb = pl.tile_mb;
+    a.k0 = pl.k0;
+    a.k1 = pl.k1;
+    a.step = p->step;
+    a.flags = p->flags;
+    return a;
+}
+
+// Checks shared by the fused entry points once B > 0 and V > 0.
+fs_status check_operands(const fs_params* p, const void* H, const void* W) {
+    if (p->d > 0 && (!H || !W)) return FS_ERR_INVALID_ARG;
+    if (p->d > 0 && (!aligned16(H) || !aligned16(W))) return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fs_status_string(fs_status s) {
+    switch (s) {
+        case FS_OK: return "FS_OK";
+        case FS_ERR_INVALID_ARG: return "FS_ERR_INVALID_ARG";
+        case FS_ERR_UNSUPPORTED: return "FS_ERR_UNSUPPORTED";
+        case FS_ERR_WORKSPACE: return "FS_ERR_WORKSPACE";
+        case FS_ERR_HIP: return "FS_ERR_HIP";
+    }
+    return "FS_ERR_UNKNOWN";
+}
+
+const char* fs_version(void) { return "libfs 0.1 (gfx950)"; }
+
+int32_t fs_num_tiles(const fs_params* p) {
+    if (check_params(p) != FS_OK) return -1;
+    const int tv = p->tile_v ? p->tile_v : kDefaultTileV;
+    return (p->V + tv - 1) / tv;
+}
+
+size_t fs_workspace_bytes(const fs_params* p, int variant, int32_t k) {
+    if (check_params(p) != FS_OK) return 0;
+    if (variant < FS_VARIANT_FLAT || variant > FS_VARIANT_MULTINOMIAL) return 0;
+    if (variant == FS_VARIANT_TOPK && (k < 1 || k > kMaxTopK)) return 0;
+    DeviceInfo dev;
+    if (!current_device(dev)) return 0;
+    Plan pl;
+    make_plan(p, variant == FS_VARIANT_GROUPED ? kVarGrouped
+                 : variant == FS_VARIANT_TOPK  ? kVarTopk
+                                               : kVarFlat,
+              dev.cus, pl);
+    return layout(variant, pl, k, nullptr, nullptr);
+}
+
+// Shared front half of fs_sample and fs_sample_stage1: validation, plan,
+// workspace carve-up and the stage-1 launch.  `done` is set when nothing is
+// left to do (B == 0, or V == 0 after filling the outputs).
+static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, const float* temp,
+                             const uint32_t* allow, int32_t* out_idx, float* out_score,
+                             void* ws, size_t ws_bytes, hipStream_t s, bool need_out,
+                             Plan& pl, Workspace& w, bool& done) {
+    done = true;
+    fs_status st = check_params(p);
+    if (st != FS_OK) return st;
+    if (p->B == 0) return FS_OK;
+    if (need_out && !out_idx) return FS_ERR_INVALID_ARG;
+    if (p->V > 0 && (st = check_operands(p, H, W)) != FS_OK) return st;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    if (p->V == 0)
+        return need_out ? from_hip(launch_fill_idx(out_idx, p->B, -1, out_score, s)) : FS_OK;
+    make_plan(p, kVarFlat, dev.cus, pl);
+    const size_t need = layout(FS_VARIANT_FLAT, pl, 0, nullptr, nullptr);
+    if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
+    layout(FS_VARIANT_FLAT, pl, 0, static_cast<char*>(ws), &w);
+    Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
+    a.pm = w.pm;
+    a.pidx = w.pidx;
+    if (launch_stage1(kVarFlat, a, pl.grid_y, pl.cfg, s) != hipSuccess) return FS_ERR_HIP;
+    done = false;
+    return FS_OK;
+}
+
+fs_status fs_sample(const fs_params* p, const void* H, const void* W, const float* temp,
+                    const uint32_t* allow, int32_t* out_idx, float* out_score, void* ws,
+                    size_t ws_bytes, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Plan pl;
+    Workspace w;
+    bool done;
+    fs_status st = flat_stage1(p, H, W, temp, allow, out_idx, out_score, ws, ws_bytes, s, true,
+                               pl, w, done);
+    if (st != FS_OK || done) return st;
+    return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.G, pl.B, out_idx, out_score, s));
+}
+
+fs_status fs_sample_stage1(const fs_params* p, const void* H, const void* W, const float* temp,
+                           const uint32_t* allow, void* ws, size_t ws_bytes, void* stream) {
+    Plan pl;
+    Workspace w;
+    bool done;
+    return flat_stage1(p, H, W, temp, allow, nullptr, nullptr, ws, ws_bytes,
+                       static_cast<hipStream_t>(stream), false, pl, w, done);
+}
+
+fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
+                            const float* temp, const uint32_t* allow, float* tile_max,
+                            int32_t* tile_idx, float* tile_logmass, int32_t* out_idx, void* ws,
+                            size_t ws_bytes, void* stream) {
+    fs_status st = check_params(p);
+    if (st != FS_OK) return st;
+    if (p->B == 0) return FS_OK;
+    if (p->V > 0 && (!tile_max || !tile_idx || !tile_logmass)) return FS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->V > 0 && (st = check_operands(p, H, W)) != FS_OK) return st;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    if (p->V == 0) return out_idx ? from_hip(launch_fill_idx(out_idx, p->B, -1, nullptr, s)) : FS_OK;
+    Plan pl;
+    make_plan(p, kVarGrouped, dev.cus, pl);
+    Workspace w;
+    const size_t need = layout(FS_VARIANT_GROUPED, pl, 0, nullptr, nullptr);
+    if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
+    layout(FS_VARIANT_GROUPED, pl, 0, static_cast<char*>(ws), &w);
+    Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
+    a.pm = w.pm;
+    a.pidx = w.pidx;
+    a.pL = w.pL;
+    hipError_t e = launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);
+    if (e != hipSuccess) return FS_ERR_HIP;
+    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.B, pl.T, pl.G, pl.nmb,
+                                          pl.tile_mb, temp, p->flags, pl.k0, pl.k1, p->step,
+                                          tile_max, tile_idx, tile_logmass, out_idx, s));
+}
+
+fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const float* temp,
+                         const uint32_t* allow, int32_t k, int32_t* out_idx, void* ws,
+                         size_t ws_bytes, void* stream) {
+    fs_status st = check_params(p);
+    if (st != FS_OK) return st;
+    if (k < 1) return FS_ERR_INVALID_ARG;
+    if (k > kMaxTopK) return FS_ERR_UNSUPPORTED;
+    if (p->B == 0) return FS_OK;
+    if (!out_idx) return FS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->V > 0 && (st = check_operands(p, H, W)) != FS_OK) return st;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    if (p->V == 0) return from_hip(launch_fill_idx(out_idx, p->B, -1, nullptr, s));
+    Plan pl;
+    make_plan(p, kVarTopk, dev.cus, pl);
+    Workspace w;
+    const size_t need = layout(FS_VARIANT_TOPK, pl, k, nullptr, nullptr);
+    if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
+    layout(FS_VARIANT_TOPK, pl, k, static_cast<char*>(ws), &w);
+    Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
+    a.topk = k;
+    a.cx = w.cx;
+    a.cs = w.cs;
+    a.cidx = w.cidx;
+    hipError_t e = launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
+    if (e != hipSuccess) return FS_ERR_HIP;
+    return from_hip(launch_stage2_topk(w.cx, w.cs, w.cidx, pl.G, pl.B, k, out_idx, s));
+}
+
+fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L,
+                          const float* temp, uint64_t seed, uint32_t step, uint32_t flags,
+                          int32_t* out_idx, float* out_L, void* stream) {
+    if (B < 0 || C < 0) return FS_ERR_INVALID_ARG;
+    if (flags & ~kFlagNoNoise) return FS_ERR_INVALID_ARG;
+    if (B == 0) return FS_OK;
+    if (!out_idx || (C > 0 && (!z || !L))) return FS_ERR_INVALID_ARG;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    return from_hip(launch_merge_online(B, C, z, L, temp, (uint32_t)(seed & 0xFFFFFFFFu),
+                                        (uint32_t)(seed >> 32), step, flags, out_idx, out_L,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* logits,
+                    void* stream) {
+    fs_status st = check_params(p);
+    if (st != FS_OK) return st;
+    if (p->B == 0 || p->V == 0) return FS_OK;
+    if (!logits) return FS_ERR_INVALID_ARG;
+    if ((st = check_operands(p, H, W)) != FS_OK) return st;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    Plan pl;
+    make_plan(p, kVarLogits, dev.cus, pl);
+    Stage1Args a = stage1_args(pl, p, H, W, nullptr, nullptr);
+    a.logits = logits;
+    return from_hip(launch_stage1(kVarLogits, a, pl.grid_y, pl.cfg,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+fs_status fs_multinomial(const fs_params* p, const float* logits, const float* temp,
+                         const uint32_t* allow, int32_t* out_idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+    fs_status st = check_params(p);
+    if (st != FS_OK) return st;
+    if (p->B == 0) return FS_OK;
+    if (!out_idx || (p->V > 0 && !logits)) return FS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    if (p->V == 0) return from_hip(launch_fill_idx(out_idx, p->B, -1, nullptr, s));
+    Plan pl;
+    make_plan(p, kVarFlat, dev.cus, pl);
+    Workspace w;
+    const size_t need = layout(FS_VARIANT_MULTINOMIAL, pl, 0, nullptr, nullptr);
+    if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
+    layout(FS_VARIANT_MULTINOMIAL, pl, 0, static_cast<char*>(ws), &w);
+    const int nchunk = (p->V + kMultinomialChunk - 1) / kMultinomialChunk;
+    return from_hip(launch_multinomial(logits, temp, allow, p->B, p->V, p->n_valid, p->v_offset,
+                                       pl.k0, pl.k1, p->step, p->flags, nchunk,
+                                       kMultinomialChunk, w.mm, w.ms, w.mkey, out_idx, s));
+}
+
+fs_status fs_debug_noise(uint64_t seed, uint32_t step, uint32_t stream_id, int32_t b0,
+                         int32_t nb, int64_t i0, int32_t ni, uint32_t* words, float* gumbel,
+                         void* stream) {
+    if (nb < 0 || ni < 0 || i0 < 0 || b0 < 0) return FS_ERR_INVALID_ARG;
+    if (nb == 0 || ni == 0 || (!words && !gumbel)) return FS_OK;
+    if (nb > 65535) return FS_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    return from_hip(launch_debug_noise((uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32),
+                                       step, stream_id, b0, nb, i0, ni, words, gumbel,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Device helpers of libfs: Philox-4x32-10, the Gumbel transform, packed
+// argmax keys, and the bf16 MFMA operand types for gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum NoiseStream : uint32_t {
+    kStreamToken = 0,        // per-id Gumbel noise
+    kStreamGroup = 1,        // per-group Gumbel of the hierarchical resample
+    kStreamMerge = 2,        // Bernoulli uniforms of the online merge
+    kStreamMultinomial = 3,  // inverse-CDF uniform of the unfused baseline
+};
+
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11, section 3): ten rounds
+// of two 32x32->64-bit products; between rounds the key advances by the Weyl
+// constants.  Each 64-bit product is one v_mad_u64_u32 on CDNA.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                       (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    }
+    return c;
+}
+
+// Standard Gumbel from one 32-bit word, in FP32.  With v = (r + 1/2) 2^-32 and
+// u = 1 - v, g = -log(-log u).  For r < 2^31 the exponential variate -log u is
+// taken as -log1p(-v), exact where u -> 1 (the largest g); otherwise u itself
+// is formed from the complement word (~r + 1/2) 2^-32, so neither branch
+// subtracts nearly equal numbers and g stays finite for every word.
+__device__ __forceinline__ float gumbel_from_word(uint32_t r) {
+    float e;
+    if (r < 0x80000000u) {
+        const float v = fmaf((float)r, 0x1p-32f, 0x1p-33f);
+        e = -log1pf(-v);
+    } else {
+        const float u = fmaf((float)(~r), 0x1p-32f, 0x1p-33f);
+        e = -logf(u);
+    }
+    return -logf(e);
+}
+
+// Uniform on (0, 1) from one word: (r + 1/2) 2^-32, rounded to FP32.
+__device__ __forceinline__ float uniform_from_word(uint32_t r) {
+    return fmaf((float)r, 0x1p-32f, 0x1p-33f);
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t float_to_ordered(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ordered_to_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Packed (score, index) key: the maximum key holds the largest score and,
+// among equal scores, the lowest index.  Index -1 packs to the low word 0.
+__device__ __forceinline__ uint64_t pack_key(float s, int32_t idx) {
+    return ((uint64_t)float_to_ordered(s) << 32) | (uint32_t)(~(uint32_t)idx);
+}
+__device__ __forceinline__ float key_score(uint64_t k) { return ordered_to_float((uint32_t)(k >> 32)); }
+__device__ __forceinline__ int32_t key_index(uint64_t k) { return (int32_t)(~(uint32_t)k); }
+
+__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, mask, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Online log-sum-exp state: value = mx + log(sm).
+struct Lse {
+    float mx, sm;
+};
+__device__ __forceinline__ Lse lse_empty() { return Lse{-INFINITY, 0.f}; }
+__device__ __forceinline__ Lse lse_add(Lse a, float x) {
+    if (!(x > -INFINITY)) return a;
+    if (x > a.mx) {
+        a.sm = a.sm * __expf(a.mx - x) + 1.f;
+        a.mx = x;
+    } else {
+        a.sm += __expf(x - a.mx);
+    }
+    return a;
+}
+__device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
+    if (!(b.mx > -INFINITY)) return a;
+    if (!(a.mx > -INFINITY)) return b;
+    if (a.mx >= b.mx) return Lse{a.mx, a.sm + b.sm * __expf(b.mx - a.mx)};
+    return Lse{b.mx, b.sm + a.sm * __expf(a.mx - b.mx)};
+}
+__device__ __forceinline__ float lse_value(Lse a) {
+    return (a.mx > -INFINITY) ? a.mx + __logf(a.sm) : -INFINITY;
+}
+
+}  // namespace fs

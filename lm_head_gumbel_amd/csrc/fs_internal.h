@@ -1,0 +1,86 @@
+// Internal interfaces between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fs {
+
+constexpr int kMBlock = 16;        // vocab rows per MFMA block (M of 16x16x32)
+constexpr int kThreads = 256;      // threads per stage-1 workgroup (4 waves)
+constexpr int kWaves = kThreads / 64;
+constexpr uint32_t kFlagNoNoise = 1u;
+
+enum Stage1Variant { kVarFlat = 0, kVarGrouped = 1, kVarLogits = 2, kVarTopk = 3 };
+
+// Balanced split of `nmb` vocab blocks over `G` workgroups: workgroup w owns
+// blocks [begin(w), begin(w+1)).  Every workgroup owns at least one block
+// when G <= nmb.
+__host__ __device__ inline int part_begin(int w, int nmb, int G) {
+    return (int)(((int64_t)w * nmb) / G);
+}
+// The workgroup owning block m.
+__host__ __device__ inline int part_owner(int m, int nmb, int G) {
+    return (int)((((int64_t)m + 1) * G - 1) / nmb);
+}
+
+struct Stage1Args {
+    const uint16_t* H;      // [B, d] bf16
+    const uint16_t* W;      // [V, d] bf16
+    const float* temp;      // [B] or null
+    const uint32_t* allow;  // [B, ceil(V/32)] or null
+    int B, d, V, n_valid, v_offset;
+    int nmb;                // ceil(V / 16)
+    int G;                  // workgroups along the vocabulary (gridDim.x)
+    int tile_mb;            // blocks per record tile (flat: one segment)
+    uint32_t k0, k1, step, flags;
+    int topk;               // k of the top-k variant
+    // partial records [P][B] (P = G for flat, G + T - 1 for grouped)
+    float* pm;
+    int32_t* pidx;
+    float* pL;
+    // top-k candidates [G][B][k]
+    float* cx;
+    float* cs;
+    int32_t* cidx;
+    // unfused baseline output [B, V]
+    float* logits;
+};
+
+struct Stage1Config {
+    int nb;   // 16-wide batch blocks per workgroup
+    int mpi;  // vocab blocks per iteration
+};
+
+hipError_t launch_stage1(int variant, const Stage1Args& a, int grid_y, const Stage1Config& cfg,
+                         hipStream_t stream);
+
+hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
+                              int32_t* out_idx, float* out_score, hipStream_t stream);
+
+hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int B,
+                                 int T, int G, int nmb, int tile_mb, const float* temp,
+                                 uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
+                                 float* tile_max, int32_t* tile_idx, float* tile_L,
+                                 int32_t* out_idx, hipStream_t stream);
+
+hipError_t launch_stage2_topk(const float* cx, const float* cs, const int32_t* cidx, int G,
+                              int B, int k, int32_t* out_idx, hipStream_t stream);
+
+hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
+                               uint32_t k0, uint32_t k1, uint32_t step, uint32_t flags,
+                               int32_t* out_idx, float* out_L, hipStream_t stream);
+
+hipError_t launch_multinomial(const float* logits, const float* temp, const uint32_t* allow,
+                              int B, int V, int n_valid, int v_offset, uint32_t k0, uint32_t k1,
+                              uint32_t step, uint32_t flags, int nchunk, int chunk,
+                              float* ws_m, float* ws_s, uint64_t* ws_key, int32_t* out_idx,
+                              hipStream_t stream);
+
+hipError_t launch_fill_idx(int32_t* out, int n, int32_t value, float* score, hipStream_t stream);
+
+hipError_t launch_debug_noise(uint32_t k0, uint32_t k1, uint32_t step, uint32_t stream_id,
+                              int b0, int nb, int64_t i0, int ni, uint32_t* words, float* gumbel,
+                              hipStream_t stream);
+
+}  // namespace fs

@@ -1,0 +1,472 @@
+// Stage 2 of fused LM-head sampling and the small kernels around it:
+//  * flat reduction: argmax over per-workgroup winners (FlashSampling
+//    explainer on aitrends.kr, Stage 2 paragraph);
+//  * grouped reduction: per-tile records from the partial records, then the
+//    hierarchical resample t* = argmax_t (L_t + G_t) (explainer,
+//    tensor-parallel and Group-Gumbel-Max paragraphs);
+//  * top-k: global top-k by x over the workgroup candidates, then argmax s;
+//  * online binary merge of group summaries (Group-Gumbel-Max paragraph);
+//  * unfused baseline: inverse-CDF draw from written logits;
+//  * a noise dump used by the tests.
+#include "fs_device.h"
+#include "fs_internal.h"
+
+namespace fs {
+
+constexpr int kRedThreads = 256;
+
+// Block-wide maximum of a packed key (256 threads); every thread gets it.
+__device__ uint64_t block_max_key(uint64_t k) {
+    __shared__ uint64_t part[kRedThreads / 64];
+    for (int m = 32; m >= 1; m >>= 1) k = key_max(k, shfl_xor_u64(k, m));
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) part[wave] = k;
+    __syncthreads();
+    uint64_t r = part[0];
+    for (int i = 1; i < kRedThreads / 64; ++i) r = key_max(r, part[i]);
+    return r;
+}
+
+__global__ __launch_bounds__(kRedThreads) void stage2_flat_kernel(const float* pm,
+                                                                  const int32_t* pidx, int P,
+                                                                  int B, int32_t* out_idx,
+                                                                  float* out_score) {
+    const int b = blockIdx.x;
+    uint64_t best = pack_key(-INFINITY, -1);
+    for (int p = threadIdx.x; p < P; p += kRedThreads) {
+        const int32_t id = pidx[(size_t)p * B + b];
+        if (id >= 0) best = key_max(best, pack_key(pm[(size_t)p * B + b], id));
+    }
+    best = block_max_key(best);
+    if (threadIdx.x == 0) {
+        const int32_t id = key_index(best);
+        out_idx[b] = id;
+        if (out_score) out_score[b] = id >= 0 ? key_score(best) : -INFINITY;
+    }
+}
+
+__device__ __forceinline__ bool row_is_greedy(const float* temp, int b, uint32_t flags) {
+    if (flags & kFlagNoNoise) return true;
+    const float T = temp ? temp[b] : 1.f;
+    return !(T > 0.f);
+}
+
+__global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
+    const float* pm, const int32_t* pidx, const float* pL, int B, int T, int G, int nmb,
+    int tile_mb, const float* temp, uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
+    float* tile_max, int32_t* tile_idx, float* tile_L, int32_t* out_idx) {
+    const int b = blockIdx.x;
+    const bool greedy = row_is_greedy(temp, b, flags);
+    uint64_t best = pack_key(-INFINITY, -1);
+    for (int t = threadIdx.x; t < T; t += kRedThreads) {
+        const int first = t * tile_mb;
+        const int last = min(nmb, (t + 1) * tile_mb) - 1;
+        const int wf = part_owner(first, nmb, G);
+        const int wl = part_owner(last, nmb, G);
+        uint64_t k = pack_key(-INFINITY, -1);
+        Lse l = lse_empty();
+        for (int w = wf; w <= wl; ++w) {   // partial record (w, t) lives at index w + t
+            const size_t o = (size_t)(w + t) * B + b;
+            const int32_t id = pidx[o];
+            if (id >= 0) k = key_max(k, pack_key(pm[o], id));
+            const float Lp = pL[o];
+            if (greedy)
+                l.mx = fmaxf(l.mx, Lp);
+            else
+                l = lse_merge(l, Lse{Lp, 1.f});
+        }
+        const int32_t id = key_index(k);
+        const float L = greedy ? l.mx : lse_value(l);
+        const size_t ot = (size_t)b * T + t;
+        tile_max[ot] = id >= 0 ? key_score(k) : -INFINITY;
+        tile_idx[ot] = id;
+        tile_L[ot] = L;
+        if (out_idx && id >= 0 && L > -INFINITY) {
+            float sc = L;
+            if (!greedy) {
+                const uint4 rw = philox4x32_10(
+                    make_uint4((uint32_t)t >> 2, (uint32_t)b, step, kStreamGroup), k0, k1);
+                const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
+                sc += gumbel_from_word(words[t & 3]);
+            }
+            // tiles hold ascending id ranges, so the lowest id also means the lowest tile
+            best = key_max(best, pack_key(sc, id));
+        }
+    }
+    if (out_idx) {
+        best = block_max_key(best);
+        if (threadIdx.x == 0) out_idx[b] = key_index(best);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// top-k: candidates [G][B][k] (x, s, id), each workgroup list sorted by x.
+// Radix select of the k-th largest packed (x, id) key over the row's G*k
+// candidates (8 passes of 8 bits), then argmax s over the keys >= it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRedThreads) void stage2_topk_kernel(const float* cx,
+                                                                  const float* cs,
+                                                                  const int32_t* cidx, int G,
+                                                                  int B, int k,
+                                                                  int32_t* out_idx) {
+    const int b = blockIdx.x;
+    __shared__ uint32_t hist[256];
+    __shared__ uint64_t s_prefix;
+    __shared__ int s_need;
+    const int n = G * k;
+    auto cand_key = [&](int e, uint64_t& key) -> bool {
+        const int w = e / k, r = e % k;
+        const size_t o = ((size_t)w * B + b) * k + r;
+        const int32_t id = cidx[o];
+        if (id < 0) return false;
+        key = pack_key(cx[o], id);
+        return true;
+    };
+    // count valid candidates
+    uint32_t cnt = 0;
+    for (int e = threadIdx.x; e < n; e += kRedThreads) {
+        uint64_t key;
+        cnt += cand_key(e, key) ? 1u : 0u;
+    }
+    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
+    if (threadIdx.x == 0) { s_prefix = 0; s_need = 0; }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) atomicAdd(&s_need, (int)cnt);
+    __syncthreads();
+    const int total = s_need;
+    __syncthreads();
+    uint64_t thresh = 0;   // keep keys >= thresh
+    if (total > k) {
+        // find the k-th largest key, digit by digit from the top
+        uint64_t prefix = 0;
+        int need = k;
+        for (int pass = 0; pass < 8; ++pass) {
+            const int shift = 56 - 8 * pass;
+            for (int i = threadIdx.x; i < 256; i += kRedThreads) hist[i] = 0;
+            __syncthreads();
+            const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+            for (int e = threadIdx.x; e < n; e += kRedThreads) {
+                uint64_t key;
+                if (cand_key(e, key) && (key & hi_mask) == prefix)
+                    atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int acc = 0;
+                int digit = 255;
+                for (; digit > 0; --digit) {
+                    if (acc + (int)hist[digit] >= need) break;
+                    acc += hist[digit];
+                }
+                s_prefix = prefix | ((uint64_t)digit << shift);
+                s_need = need - acc;
+            }
+            __syncthreads();
+            prefix = s_prefix;
+            need = s_need;
+            __syncthreads();
+        }
+        thresh = prefix;   // keys are distinct, so exactly k keys are >= prefix
+    }
+    uint64_t best = pack_key(-INFINITY, -1);
+    for (int e = threadIdx.x; e < n; e += kRedThreads) {
+        uint64_t key;
+        if (cand_key(e, key) && key >= thresh) {
+            const int w = e / k, r = e % k;
+            const size_t o = ((size_t)w * B + b) * k + r;
+            best = key_max(best, pack_key(cs[o], cidx[o]));
+        }
+    }
+    best = block_max_key(best);
+    if (threadIdx.x == 0) out_idx[b] = key_index(best);
+}
+
+// ---------------------------------------------------------------------------
+// online binary merge: one thread per row, chunks in order
+// ---------------------------------------------------------------------------
+__global__ void merge_online_kernel(int B, int C, const int32_t* z, const float* L,
+                                    const float* temp, uint32_t k0, uint32_t k1, uint32_t step,
+                                    uint32_t flags, int32_t* out_idx, float* out_L) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const bool greedy = row_is_greedy(temp, b, flags);
+    int32_t zz = C > 0 ? z[(size_t)b * C] : -1;
+    float A = C > 0 ? L[(size_t)b * C] : -INFINITY;
+    for (int c = 1; c < C; ++c) {
+        const float Lc = L[(size_t)b * C + c];
+        const int32_t zc = z[(size_t)b * C + c];
+        if (greedy) {
+            if (Lc > A) { zz = zc; A = Lc; }
+            continue;
+        }
+        if (!(Lc > -INFINITY)) continue;
+        const float hi = fmaxf(A, Lc);
+        const float A_new = hi + log1pf(expf(-fabsf(A - Lc)));   // logaddexp(A, L_c)
+        const float p = expf(Lc - A_new);
+        const uint4 rw = philox4x32_10(
+            make_uint4((uint32_t)c >> 2, (uint32_t)b, step, kStreamMerge), k0, k1);
+        const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
+        const float u = uniform_from_word(words[c & 3]);
+        if (u < p) zz = zc;
+        A = A_new;
+    }
+    out_idx[b] = zz;
+    if (out_L) out_L[b] = A;
+}
+
+// ---------------------------------------------------------------------------
+// unfused multinomial baseline
+//  pass 1 (grid nchunk x B): per chunk of a row, the max of x, the sum of
+//          exp(x - max) and the argmax key (for greedy rows);
+//  pass 2 (grid B): total mass Z, target u*Z, the chunk holding it, then an
+//          in-chunk inclusive scan to find the first id whose cumulative
+//          mass exceeds the target.
+// ---------------------------------------------------------------------------
+struct XArgs {
+    const float* logits;
+    const float* temp;
+    const uint32_t* allow;
+    int B, V, n_valid, v_offset;
+    uint32_t flags;
+};
+
+__device__ __forceinline__ float x_of(const XArgs& a, int b, int i, float inv_t) {
+    if (i >= a.V || a.v_offset + i >= a.n_valid) return -INFINITY;
+    if (a.allow) {
+        const int words = (a.V + 31) >> 5;
+        if (!((a.allow[(size_t)b * words + (i >> 5)] >> (i & 31)) & 1u)) return -INFINITY;
+    }
+    const float x = a.logits[(size_t)b * a.V + i] * inv_t;
+    return x == x ? x : -INFINITY;
+}
+
+__device__ __forceinline__ float inv_temp(const XArgs& a, int b, bool& greedy) {
+    greedy = row_is_greedy(a.temp, b, a.flags);
+    return greedy ? 1.f : 1.f / (a.temp ? a.temp[b] : 1.f);
+}
+
+__global__ __launch_bounds__(kRedThreads) void multinomial_pass1(XArgs a, int chunk, int nchunk,
+                                                                 float* ws_m, float* ws_s,
+                                                                 uint64_t* ws_key) {
+    const int c = blockIdx.x, b = blockIdx.y;
+    bool greedy;
+    const float inv_t = inv_temp(a, b, greedy);
+    const int i0 = c * chunk, i1 = min(a.V, i0 + chunk);
+    Lse l = lse_empty();
+    uint64_t best = pack_key(-INFINITY, -1);
+    for (int i = i0 + threadIdx.x; i < i1; i += kRedThreads) {
+        const float x = x_of(a, b, i, inv_t);
+        l = lse_add(l, x);
+        if (x > -INFINITY) best = key_max(best, pack_key(x, a.v_offset + i));
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+        l = lse_merge(l, Lse{__shfl_xor(l.mx, m, 64), __shfl_xor(l.sm, m, 64)});
+        best = key_max(best, shfl_xor_u64(best, m));
+    }
+    __shared__ float smx[4], ssm[4];
+    __shared__ uint64_t skey[4];
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { smx[wave] = l.mx; ssm[wave] = l.sm; skey[wave] = best; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Lse r = Lse{smx[0], ssm[0]};
+        uint64_t k = skey[0];
+        for (int i = 1; i < 4; ++i) { r = lse_merge(r, Lse{smx[i], ssm[i]}); k = key_max(k, skey[i]); }
+        const size_t o = (size_t)b * nchunk + c;
+        ws_m[o] = r.mx;
+        ws_s[o] = r.sm;
+        ws_key[o] = k;
+    }
+}
+
+// Pass 2 of the multinomial baseline.  The chunk is split into 256
+// contiguous runs of `chunk / 256` ids, one per thread; one block scan over
+// the run masses finds the run holding the target, whose thread then walks
+// its ids in order.
+__global__ __launch_bounds__(kRedThreads) void multinomial_pass2(XArgs a, int chunk, int nchunk,
+                                                                 const float* ws_m,
+                                                                 const float* ws_s,
+                                                                 const uint64_t* ws_key,
+                                                                 uint32_t k0, uint32_t k1,
+                                                                 uint32_t step,
+                                                                 int32_t* out_idx) {
+    const int b = blockIdx.x;
+    bool greedy;
+    const float inv_t = inv_temp(a, b, greedy);
+    __shared__ float s_M, s_base, s_target;
+    __shared__ int s_chunk, s_found, s_last;
+    __shared__ float scan[kRedThreads];
+    if (threadIdx.x == 0) {
+        // sequential over the row's chunks: global max, total mass, target chunk
+        float M = -INFINITY;
+        uint64_t k = pack_key(-INFINITY, -1);
+        for (int c = 0; c < nchunk; ++c) {
+            M = fmaxf(M, ws_m[(size_t)b * nchunk + c]);
+            k = key_max(k, ws_key[(size_t)b * nchunk + c]);
+        }
+        s_chunk = -1;
+        s_found = 0x7FFFFFFF;
+        s_last = -1;
+        if (greedy || !(M > -INFINITY)) {
+            out_idx[b] = key_index(k);
+        } else {
+            float Z = 0.f;
+            for (int c = 0; c < nchunk; ++c) {
+                const float m = ws_m[(size_t)b * nchunk + c];
+                if (m > -INFINITY) Z += ws_s[(size_t)b * nchunk + c] * __expf(m - M);
+            }
+            const uint4 rw =
+                philox4x32_10(make_uint4(0u, (uint32_t)b, step, kStreamMultinomial), k0, k1);
+            const float target = uniform_from_word(rw.x) * Z;
+            float acc = 0.f, acc_last = 0.f;
+            int last = -1, sel = -1;
+            for (int c = 0; c < nchunk; ++c) {
+                const float m = ws_m[(size_t)b * nchunk + c];
+                if (!(m > -INFINITY)) continue;
+                const float cm = ws_s[(size_t)b * nchunk + c] * __expf(m - M);
+                last = c;
+                acc_last = acc;
+                if (target < acc + cm) { sel = c; break; }
+                acc += cm;
+            }
+            if (sel < 0) { sel = last; acc = acc_last; }   // rounding: the last chunk with mass
+            s_chunk = sel;
+            s_base = acc;
+            s_target = target;
+            s_M = M;
+        }
+    }
+    __syncthreads();
+    const int c = s_chunk;
+    if (c < 0) return;   // greedy or empty row: already written
+    const float M = s_M, target = s_target;
+    const int per = chunk / kRedThreads;
+    const int j0 = c * chunk + threadIdx.x * per;
+    const int j1 = min(a.V, j0 + per);
+    float mass = 0.f;
+    int my_last = -1;
+    for (int i = j0; i < j1; ++i) {
+        const float x = x_of(a, b, i, inv_t);
+        if (x > -INFINITY) { mass += __expf(x - M); my_last = i; }
+    }
+    scan[threadIdx.x] = mass;
+    __syncthreads();
+    for (int off = 1; off < kRedThreads; off <<= 1) {   // inclusive scan of run masses
+        const float v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0.f;
+        __syncthreads();
+        scan[threadIdx.x] += v;
+        __syncthreads();
+    }
+    const float incl = s_base + scan[threadIdx.x];
+    const float excl = incl - mass;
+    if (my_last >= 0) atomicMax(&s_last, my_last);
+    if (mass > 0.f && excl <= target && target < incl) {
+        float acc = excl;
+        int pick = my_last;
+        for (int i = j0; i < j1; ++i) {
+            const float x = x_of(a, b, i, inv_t);
+            if (!(x > -INFINITY)) continue;
+            acc += __expf(x - M);
+            if (target < acc) { pick = i; break; }
+        }
+        atomicMin(&s_found, pick);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // rounding can leave the target past the chunk's scanned mass: the
+        // draw then belongs to the chunk's last valid id
+        const int i = s_found != 0x7FFFFFFF ? s_found : s_last;
+        out_idx[b] = i >= 0 ? a.v_offset + i : -1;
+    }
+}
+
+__global__ void fill_idx_kernel(int32_t* out, int n, int32_t value, float* score) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        out[i] = value;
+        if (score) score[i] = -INFINITY;
+    }
+}
+
+__global__ void debug_noise_kernel(uint32_t k0, uint32_t k1, uint32_t step, uint32_t stream_id,
+                                   int b0, int nb, int64_t i0, int ni, uint32_t* words,
+                                   float* gumbel) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    const int r = blockIdx.y;
+    if (j >= ni || r >= nb) return;
+    const uint64_t i = (uint64_t)i0 + j;
+    const uint4 rw = philox4x32_10(
+        make_uint4((uint32_t)(i >> 2), (uint32_t)(b0 + r), step, stream_id), k0, k1);
+    const uint32_t wv[4] = {rw.x, rw.y, rw.z, rw.w};
+    const uint32_t word = wv[i & 3];
+    if (words) words[(size_t)r * ni + j] = word;
+    if (gumbel) gumbel[(size_t)r * ni + j] = gumbel_from_word(word);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
+                              int32_t* out_idx, float* out_score, hipStream_t stream) {
+    hipLaunchKernelGGL(stage2_flat_kernel, dim3(B), dim3(kRedThreads), 0, stream, pm, pidx, P,
+                       B, out_idx, out_score);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int B,
+                                 int T, int G, int nmb, int tile_mb, const float* temp,
+                                 uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
+                                 float* tile_max, int32_t* tile_idx, float* tile_L,
+                                 int32_t* out_idx, hipStream_t stream) {
+    hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kRedThreads), 0, stream, pm, pidx,
+                       pL, B, T, G, nmb, tile_mb, temp, flags, k0, k1, step, tile_max, tile_idx,
+                       tile_L, out_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage2_topk(const float* cx, const float* cs, const int32_t* cidx, int G,
+                              int B, int k, int32_t* out_idx, hipStream_t stream) {
+    hipLaunchKernelGGL(stage2_topk_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cs, cidx,
+                       G, B, k, out_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
+                               uint32_t k0, uint32_t k1, uint32_t step, uint32_t flags,
+                               int32_t* out_idx, float* out_L, hipStream_t stream) {
+    hipLaunchKernelGGL(merge_online_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, B, C, z, L,
+                       temp, k0, k1, step, flags, out_idx, out_L);
+    return hipGetLastError();
+}
+
+hipError_t launch_multinomial(const float* logits, const float* temp, const uint32_t* allow,
+                              int B, int V, int n_valid, int v_offset, uint32_t k0, uint32_t k1,
+                              uint32_t step, uint32_t flags, int nchunk, int chunk,
+                              float* ws_m, float* ws_s, uint64_t* ws_key, int32_t* out_idx,
+                              hipStream_t stream) {
+    XArgs a{logits, temp, allow, B, V, n_valid, v_offset, flags};
+    hipLaunchKernelGGL(multinomial_pass1, dim3(nchunk, B), dim3(kRedThreads), 0, stream, a, chunk,
+                       nchunk, ws_m, ws_s, ws_key);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(multinomial_pass2, dim3(B), dim3(kRedThreads), 0, stream, a, chunk, nchunk,
+                       ws_m, ws_s, ws_key, k0, k1, step, out_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_idx(int32_t* out, int n, int32_t value, float* score, hipStream_t stream) {
+    hipLaunchKernelGGL(fill_idx_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, out, n, value,
+                       score);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_noise(uint32_t k0, uint32_t k1, uint32_t step, uint32_t stream_id,
+                              int b0, int nb, int64_t i0, int ni, uint32_t* words, float* gumbel,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(debug_noise_kernel, dim3((ni + 255) / 256, nb), dim3(256), 0, stream, k0,
+                       k1, step, stream_id, b0, nb, i0, ni, words, gumbel);
+    return hipGetLastError();
+}
+
+}  // namespace fs

@@ -1,0 +1,323 @@
+"""GPU parity of libfs against the CPU oracle on small shapes (several tiles,
+ragged tails, masks, greedy rows, every entry point).  Acceptance:
+Philox words bit-exact; per-tile max and log-mass within 2e-3; sampled
+indices identical wherever the oracle's top-two noisy scores differ by more
+than 1e-2 (elsewhere a valid near-maximiser); sample histograms pass
+chi-square (p > 0.01) against the oracle's softmax; repeated calls
+bit-identical."""
+import math
+
+import numpy as np
+import pytest
+
+import lm_head_gumbel_amd as fs
+from lm_head_gumbel_amd.inputs import (f32_to_bf16_bits, hidden_bf16, normal_f32,
+                                       tiny_reference, weights_bf16)
+from oracle import fs_oracle as O
+from oracle import philox as px
+from gpu_util import (Inputs, TOL_GAP, TOL_VALUE, check_index_rows, check_values, log,
+                      run_flat, run_grouped, run_logits, run_merge, run_multinomial, run_topk,
+                      torch)
+from stats_util import chi_square_p, chi_square_rows_p, softmax
+
+pytestmark = pytest.mark.gpu
+
+SEED = 1234
+MULTI_TOL = 1e-4   # CDF-boundary margin below which a multinomial draw is not pinned
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    t = torch()
+    assert t.cuda.is_available(), "GPU tests need a device"
+    assert fs.fs_version()
+    yield
+
+
+# ---------------------------------------------------------------------------
+# noise
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, SEED, 0xDEADBEEF12345678])
+@pytest.mark.parametrize("stream_id", [0, 1, 2, 3])
+def test_noise_words_bit_exact(seed, stream_id):
+    t = torch()
+    log(f"noise seed={seed:#x} stream={stream_id}")
+    nb, ni = 3, 4099
+    for i0 in (0, 151936 - 2048, (1 << 31) - 1024):
+        words = t.zeros((nb, ni), dtype=t.int32, device="cuda")
+        g = t.zeros((nb, ni), dtype=t.float32, device="cuda")
+        fs.check(fs.fs_debug_noise(seed, 77, stream_id, 5, nb, i0, ni, words, g), "noise")
+        t.cuda.synchronize()
+        w = words.cpu().numpy().view(np.uint32)
+        ids = i0 + np.arange(ni, dtype=np.int64)
+        ref = px.noise_words(seed, 5 + np.arange(nb)[:, None], ids[None, :], 77, stream_id)
+        assert np.array_equal(w, ref)
+        gref = O.gumbel_from_word(ref)
+        err = np.abs(g.cpu().numpy().astype(np.float64) - gref)
+        # FP32 transform: error of a few ulps of |g| <= 22.9 plus the rounding of v
+        assert err.max() < 2e-5, err.max()
+
+
+def test_gumbel_extreme_words():
+    t = torch()
+    # find ids whose words are near 0 and near 2^32 among a long range, and check g there
+    ni = 1 << 20
+    words = t.zeros((1, ni), dtype=t.int32, device="cuda")
+    g = t.zeros((1, ni), dtype=t.float32, device="cuda")
+    fs.check(fs.fs_debug_noise(SEED, 0, 0, 0, 1, 0, ni, words, g), "noise")
+    t.cuda.synchronize()
+    w = words.cpu().numpy().view(np.uint32)[0]
+    gv = g.cpu().numpy()[0].astype(np.float64)
+    assert np.all(np.isfinite(gv))
+    sel = np.concatenate([np.argsort(w)[:64], np.argsort(w)[-64:]])
+    ref = O.gumbel_from_word(w[sel])
+    assert np.abs(gv[sel] - ref).max() < 2e-5
+
+
+# ---------------------------------------------------------------------------
+# one full comparison of every entry point on one problem
+# ---------------------------------------------------------------------------
+def compare_all(Hb, Wb, temp=None, n_valid=None, allow=None, tile_v=128, v_offset=0,
+                seed=SEED, steps=(0,), flags=0, topk=(1, 7, 40), check_logits=True):
+    B, d = Hb.shape
+    V = Wb.shape[0]
+    x_in = Inputs(Hb, Wb, temp, allow)
+    l = O.logits_bf16(Hb, Wb)
+    nv = v_offset + V if n_valid is None else n_valid
+    if check_logits:
+        p = x_in.params(n_valid=nv, v_offset=v_offset, tile_v=tile_v, seed=seed, flags=flags)
+        gl, gl_dev = run_logits(x_in, p)
+        scale = np.abs(O.bf16_bits_to_f64(Hb)).sum(1)[:, None] * \
+            np.abs(O.bf16_bits_to_f64(Wb)).max() + 1e-30
+        # FP32 accumulation: |error| <= d * 2^-24 * sum |H_k W_ik| (loose bound)
+        assert np.all(np.abs(gl - l) <= max(d, 1) * 2.0 ** -24 * scale + 1e-30)
+    for step in steps:
+        p = x_in.params(n_valid=nv, v_offset=v_offset, tile_v=tile_v, seed=seed, step=step,
+                        flags=flags)
+        r = O.run_call(l, temp, nv, allow, seed, step, flags, tile_v, v_offset)
+        # flat
+        gi, gs = run_flat(x_in, p)
+        npin = check_index_rows(gi, r["flat_idx"], r["flat_gap"], r["s"], v_offset,
+                                what="flat")
+        check_values(gs, r["flat_max"], what="flat score")
+        # grouped
+        m, ti, L, go = run_grouped(x_in, p)
+        check_values(m, r["tile_m"], what="tile max")
+        check_values(L, r["tile_L"], what="tile log-mass")
+        for t in range(m.shape[1]):
+            c0 = t * tile_v
+            check_index_rows(ti[:, t], r["tile_idx"][:, t], r["tile_gap"][:, t],
+                             r["s"][:, c0:c0 + tile_v], v_offset + c0, what=f"tile {t} idx")
+        pinned = r["grp_gap"] > TOL_GAP
+        for b in range(B):
+            t = r["grp_tile"][b]
+            if t >= 0 and r["tile_gap"][b, t] <= TOL_GAP:
+                pinned[b] = False
+        bad = np.nonzero(pinned & (go != r["grp_idx"]))[0]
+        assert bad.size == 0, f"grouped sample rows {bad}"
+        for b in np.nonzero(~pinned)[0]:
+            assert go[b] == -1 or go[b] in set(ti[b].tolist())
+        # top-k
+        greedy = O.greedy_rows(temp, B, flags)
+        for k in topk:
+            tk = run_topk(x_in, p, k)
+            oi, ogap, omarg = O.topk_sample(r["x"], r["s"], k, v_offset)
+            pin = (ogap > TOL_GAP) & (omarg > 1e-3)
+            bad = np.nonzero(pin & (tk != oi))[0]
+            assert bad.size == 0, f"top-{k} rows {bad} got {tk[bad]} want {oi[bad]}"
+            for b in range(B):
+                if oi[b] < 0:
+                    assert tk[b] == -1
+                else:
+                    assert np.isfinite(r["x"][b, tk[b] - v_offset])
+        # unfused baseline on the GPU's own logits
+        if check_logits:
+            mi = run_multinomial(x_in, p, gl_dev)
+            oi, omarg = O.multinomial(r["x"], temp, seed, step, flags, v_offset)
+            pin = omarg > MULTI_TOL
+            bad = np.nonzero(pin & (mi != oi))[0]
+            assert bad.size == 0, f"multinomial rows {bad} got {mi[bad]} want {oi[bad]}"
+        log(f"  B={B} d={d} V={V} tile={tile_v} step={step}: {npin}/{B} flat rows pinned")
+    return x_in
+
+
+CASES = [
+    # (B, d, V, tile_v, n_valid_cut, v_offset, temp kind, allow)
+    (1, 64, 1000, 128, 10, 0, "one", False),       # V not a multiple of 16, ragged tail
+    (5, 136, 3001, 64, 11, 32, "mixed", True),      # d not a multiple of 32, offset ids
+    (16, 256, 2048, 512, 0, 0, "range", False),     # exactly one N-block
+    (17, 96, 2500, 256, 285, 0, "range", True),     # two N-blocks, partial
+    (40, 128, 1500, 48, 3, 16, "mixed", False),     # four N-blocks, odd tile size
+    (3, 512, 4096, 16, 0, 0, "one", False),         # smallest tile
+]
+
+
+def make_case(B, d, V, temp_kind, allow_on, seed=0):
+    rng = np.random.default_rng(100 + B + d + V)
+    Hb = hidden_bf16(B, d, seed=11 + seed)
+    Wb = weights_bf16(V, d, std=0.05, seed=12 + seed)
+    if temp_kind == "one":
+        temp = np.ones(B, np.float32)
+    elif temp_kind == "range":
+        temp = rng.uniform(0.3, 1.5, B).astype(np.float32)
+    else:
+        temp = rng.uniform(0.3, 1.5, B).astype(np.float32)
+        temp[0] = 0.0
+        if B > 2:
+            temp[2] = -1.0
+        if B > 3:
+            temp[3] = np.nan
+    allow = None
+    if allow_on:
+        words = (V + 31) // 32
+        allow = rng.integers(0, 2 ** 32, size=(B, words), dtype=np.uint64).astype(np.uint32)
+        allow |= rng.integers(0, 2 ** 32, size=(B, words), dtype=np.uint64).astype(np.uint32)
+    return Hb, Wb, temp, allow
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_d{c[1]}_V{c[2]}_t{c[3]}")
+def test_parity_small(case):
+    B, d, V, tile_v, cut, v_off, tk, al = case
+    log(f"parity case {case}")
+    Hb, Wb, temp, allow = make_case(B, d, V, tk, al)
+    compare_all(Hb, Wb, temp, n_valid=v_off + V - cut, allow=allow, tile_v=tile_v,
+                v_offset=v_off, steps=(0, 1))
+
+
+def test_tiny_reference_config():
+    wl, H, W = tiny_reference()
+    log("tiny reference: B=4 d=256 V=4096 tile 512")
+    Hb, Wb = f32_to_bf16_bits(H), f32_to_bf16_bits(W)
+    compare_all(Hb, Wb, np.ones(4, np.float32), tile_v=512, steps=(0,))
+
+
+def test_no_noise_is_greedy():
+    Hb, Wb, temp, _ = make_case(9, 128, 1234, "range", False)
+    log("no-noise flag")
+    x = Inputs(Hb, Wb, temp)
+    p = x.params(seed=SEED, flags=fs.FS_NO_NOISE, tile_v=64)
+    l = O.logits_bf16(Hb, Wb)
+    want = np.argmax(l, axis=1)
+    gap = np.sort(l, axis=1)[:, -1] - np.sort(l, axis=1)[:, -2]
+    ok = gap > 1e-4
+    gi, _ = run_flat(x, p)
+    assert np.array_equal(gi[ok], want[ok])
+    _, _, _, go = run_grouped(x, p)
+    assert np.array_equal(go[ok], want[ok])
+    for k in (1, 5):
+        assert np.array_equal(run_topk(x, p, k)[ok], want[ok])
+
+
+def test_masked_rows_and_empty_shapes():
+    t = torch()
+    Hb, Wb, temp, _ = make_case(4, 64, 700, "one", False)
+    x = Inputs(Hb, Wb, temp, np.zeros((4, (700 + 31) // 32), np.uint32))
+    p = x.params(seed=SEED, tile_v=128)
+    gi, gs = run_flat(x, p)
+    assert np.all(gi == -1) and np.all(np.isneginf(gs))
+    m, ti, L, go = run_grouped(x, p)
+    assert np.all(ti == -1) and np.all(np.isneginf(m)) and np.all(np.isneginf(L))
+    assert np.all(go == -1)
+    assert np.all(run_topk(x, p, 3) == -1)
+    x2 = Inputs(Hb, Wb, temp)
+    gi, _ = run_flat(x2, x2.params(n_valid=0, seed=SEED))
+    assert np.all(gi == -1)
+    # V = 0: every row -1
+    idx = t.full((4,), 5, dtype=t.int32, device="cuda")
+    ws = t.empty(1 << 20, dtype=t.uint8, device="cuda")
+    fs.check(fs.fs_sample(fs.params(4, 64, 0), x.H, x.W, None, None, idx, None, ws), "V=0")
+    t.cuda.synchronize()
+    assert np.all(idx.cpu().numpy() == -1)
+    # B = 0: nothing is written
+    fs.check(fs.fs_sample(fs.params(0, 64, 700), x.H, x.W, None, None, idx, None, ws), "B=0")
+    # undersized workspace is reported, not run
+    p = x.params(seed=SEED)
+    n = fs.fs_workspace_bytes(p, fs.FS_VARIANT_FLAT)
+    assert fs.fs_sample(p, x.H, x.W, None, None, idx, None, ws, n - 1) == fs.FS_ERR_WORKSPACE
+
+
+def test_nan_logits_never_win():
+    Hb, Wb, temp, _ = make_case(3, 64, 500, "one", False)
+    Wb = Wb.copy()
+    Wb[17, 5] = 0x7FC0   # NaN weight: id 17 has a NaN logit in every row
+    x = Inputs(Hb, Wb, temp)
+    p = x.params(seed=SEED, tile_v=16)
+    l = O.logits_bf16(Hb, Wb)
+    assert np.all(np.isnan(l[:, 17]))
+    r = O.run_call(l, temp, None, None, SEED, 0, 0, 16)
+    gi, _ = run_flat(x, p)
+    check_index_rows(gi, r["flat_idx"], r["flat_gap"], r["s"])
+    assert not np.any(gi == 17)
+    m, ti, L, _ = run_grouped(x, p)
+    check_values(L, r["tile_L"], what="tile log-mass with NaN")
+
+
+def test_repeated_calls_bit_identical():
+    Hb, Wb, temp, allow = make_case(33, 256, 5000, "mixed", True)
+    x = Inputs(Hb, Wb, temp, allow)
+    p = x.params(seed=SEED, step=3, tile_v=256)
+    a = run_flat(x, p)
+    b = run_flat(x, p)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.int64), b[1].view(np.int64))
+    g1 = run_grouped(x, p)
+    g2 = run_grouped(x, p)
+    for u, v in zip(g1, g2):
+        assert np.array_equal(np.asarray(u), np.asarray(v))
+    assert np.array_equal(run_topk(x, p, 40), run_topk(x, p, 40))
+
+
+def test_online_merge_matches_oracle():
+    # chunks of 320 ids over V = 2560 (8 chunks), records from the grouped entry point
+    Hb, Wb, temp, _ = make_case(12, 128, 2560, "mixed", False)
+    x = Inputs(Hb, Wb, temp)
+    l = O.logits_bf16(Hb, Wb)
+    for step in (0, 5):
+        p = x.params(seed=SEED, step=step, tile_v=320)
+        m, ti, L, _ = run_grouped(x, p, with_sample=False)
+        gz, gA = run_merge(ti, L, temp, SEED, step)
+        # oracle merge on the oracle's own chunk records
+        r = O.run_call(l, temp, None, None, SEED, step, 0, 320)
+        oz, oA, omarg = O.online_merge(r["tile_idx"], r["tile_L"], temp, SEED, step)
+        check_values(gA, oA, tol=TOL_VALUE, what="merged log-mass")
+        chunk_pinned = (r["tile_gap"] > TOL_GAP).all(axis=1)
+        pin = (omarg > 1e-2) & chunk_pinned
+        bad = np.nonzero(pin & (gz != oz))[0]
+        assert bad.size == 0, f"merge rows {bad}"
+        # the same merge on the GPU's records must follow the GPU's chunk winners
+        oz2, _, om2 = O.online_merge(ti, L, temp, SEED, step)
+        pin2 = om2 > 1e-2
+        assert np.array_equal(gz[pin2], oz2[pin2])
+
+
+def test_flat_histogram_chi_square():
+    # one hidden state repeated over 10 rows, 500 decode steps: 5000 draws
+    t = torch()
+    V, d = 64, 64
+    H1 = hidden_bf16(1, d, seed=3)
+    Hb = np.repeat(H1, 10, axis=0)
+    Wb = weights_bf16(V, d, std=0.15, seed=4)
+    temp = np.full(10, 0.8, np.float32)
+    x = Inputs(Hb, Wb, temp)
+    l = O.logits_bf16(H1, Wb)[0]
+    prob = softmax(l / 0.8)
+    flat, grp, top = [], [], []
+    for step in range(500):
+        p = x.params(seed=SEED, step=step, tile_v=16)
+        flat.append(run_flat(x, p)[0])
+        grp.append(run_grouped(x, p)[3])
+    flat = np.concatenate(flat)
+    grp = np.concatenate(grp)
+    pf = chi_square_p(flat, prob)
+    pg = chi_square_p(grp, prob)
+    log(f"chi-square p: flat {pf:.3f} grouped {pg:.3f}")
+    assert pf > 0.01 and pg > 0.01
+    # top-k 8: renormalised over the 8 largest logits
+    keep = np.argsort(-l, kind="stable")[:8]
+    pk = np.zeros(V)
+    pk[keep] = softmax(l[keep] / 0.8)
+    for step in range(500):
+        p = x.params(seed=SEED, step=step)
+        top.append(run_topk(x, p, 8))
+    ptk = chi_square_p(np.concatenate(top), pk)
+    log(f"chi-square p: top-8 {ptk:.3f}")
+    assert ptk > 0.01
