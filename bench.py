@@ -104,10 +104,12 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
         logits = torch.empty((B, V), dtype=torch.float32, device="cuda")
         mws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_MULTINOMIAL),
                           dtype=torch.uint8, device="cuda")
+        lws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_LOGITS),
+                          dtype=torch.uint8, device="cuda")
 
         def base(i):
             p.step = i
-            fs.check(fs.fs_logits(p, H, W, logits), "fs_logits")
+            fs.check(fs.fs_logits(p, H, W, logits, lws), "fs_logits")
             fs.check(fs.fs_multinomial(p, logits, None, None, idx, mws), "fs_multinomial")
 
         for i in range(max(2, warmup // 2)):

@@ -82,7 +82,8 @@ enum {
     FS_VARIANT_FLAT = 0,
     FS_VARIANT_GROUPED = 1,
     FS_VARIANT_TOPK = 2,
-    FS_VARIANT_MULTINOMIAL = 3
+    FS_VARIANT_MULTINOMIAL = 3,
+    FS_VARIANT_LOGITS = 4
 };
 
 typedef struct {
@@ -176,9 +177,10 @@ fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L
 /* fs_logits -- unfused baseline, step 1: writes l[b, j] (FP32, no
  * temperature, no mask) to device logits [B, V] row-major.  This is the
  * tensor the fused path never materialises (FlashSampling explainer,
- * problem statement). */
+ * problem statement).  ws: fs_workspace_bytes(p, FS_VARIANT_LOGITS, 0) bytes
+ * (partial sums of the vocabulary blocks split between workers). */
 fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* logits,
-                    void* stream);
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* fs_multinomial -- unfused baseline, step 2: reads device logits [B, V]
  * (row-major FP32, as written by fs_logits), applies temperature and masks as
@@ -197,6 +199,18 @@ fs_status fs_multinomial(const fs_params* p, const float* logits, const float* t
 fs_status fs_debug_noise(uint64_t seed, uint32_t step, uint32_t stream_id, int32_t b0,
                          int32_t nb, int64_t i0, int32_t ni, uint32_t* words, float* gumbel,
                          void* stream);
+
+/* fs_debug_read_probe -- reads `bytes` (a multiple of 16) of device memory at
+ * `src` (16-byte aligned) once with 16-byte loads from `grid` workgroups of
+ * 256 threads, folding the data into sink (device uint32 [grid * 256]).  The
+ * practical HBM read ceiling that stage 1 is compared with. */
+fs_status fs_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                              void* stream);
+
+/* fs_debug_copy -- plain device copy of `bytes` (a multiple of 16; both
+ * pointers 16-byte aligned, no overlap) from `grid` workgroups of 256 threads:
+ * a kernel of known traffic for calibrating hardware byte counters. */
+fs_status fs_debug_copy(void* dst, const void* src, size_t bytes, int32_t grid, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(PKG, "libfs.so")
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_UNSUPPORTED, FS_ERR_WORKSPACE, FS_ERR_HIP = range(5)
 FS_NO_NOISE = 1
-FS_VARIANT_FLAT, FS_VARIANT_GROUPED, FS_VARIANT_TOPK, FS_VARIANT_MULTINOMIAL = range(4)
+(FS_VARIANT_FLAT, FS_VARIANT_GROUPED, FS_VARIANT_TOPK, FS_VARIANT_MULTINOMIAL,
+ FS_VARIANT_LOGITS) = range(5)
 
 
 class fs_params(ctypes.Structure):
@@ -59,12 +60,15 @@ _SIGS = {
     "fs_merge_online": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, _P, _P,
                                        _P]),
-    "fs_logits": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P]),
+    "fs_logits": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, ctypes.c_size_t,
+                                 _P]),
     "fs_multinomial": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
     "fs_debug_noise": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                       ctypes.c_int32, _P, _P, _P]),
+    "fs_debug_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
+    "fs_debug_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, ctypes.c_int32, _P]),
 }
 
 
@@ -164,8 +168,10 @@ def fs_merge_online(B, C, z, L, temp, seed, step, flags, out_idx, out_L=None, st
                                  _ptr(out_idx), _ptr(out_L), _stream(stream))
 
 
-def fs_logits(p, H, W, logits, stream=None):
-    return lib().fs_logits(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(logits), _stream(stream))
+def fs_logits(p, H, W, logits, ws=None, ws_bytes=None, stream=None):
+    w, n = _ws(ws, ws_bytes)
+    return lib().fs_logits(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(logits), w, n,
+                           _stream(stream))
 
 
 def fs_multinomial(p, logits, temp, allow, out_idx, ws=None, ws_bytes=None, stream=None):
@@ -177,6 +183,14 @@ def fs_multinomial(p, logits, temp, allow, out_idx, ws=None, ws_bytes=None, stre
 def fs_debug_noise(seed, step, stream_id, b0, nb, i0, ni, words=None, gumbel=None, stream=None):
     return lib().fs_debug_noise(seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, stream_id, b0, nb,
                                 i0, ni, _ptr(words), _ptr(gumbel), _stream(stream))
+
+
+def fs_debug_read_probe(src, nbytes, sink, grid, stream=None):
+    return lib().fs_debug_read_probe(_ptr(src), nbytes, _ptr(sink), grid, _stream(stream))
+
+
+def fs_debug_copy(dst, src, nbytes, grid, stream=None):
+    return lib().fs_debug_copy(_ptr(dst), _ptr(src), nbytes, grid, _stream(stream))
 
 
 def check(status, where=""):

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -36,7 +37,7 @@ int wg_per_cu() {
     static int v = [] {
         const char* e = std::getenv("FS_WG_PER_CU");
         int x = e ? std::atoi(e) : 0;
-        return (x >= 1 && x <= 16) ? x : 2;
+        return (x >= 1 && x <= 16) ? x : 1;
     }();
     return v;
 }
@@ -66,10 +67,20 @@ bool current_device(DeviceInfo& out) {
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Stage-1 kernels: resident (H slice in registers; the default for the
+// common shapes), stream (independent worker waves, H reloaded per stage) and
+// coop (workgroup-cooperative, H reloaded per stage; top-k and the shapes the
+// others do not cover).
+enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2 };
+
 // Validated shape of one call and its launch plan.
 struct Plan {
     int B, d, V, n_valid, v_offset, tile_v, tile_mb, T, nmb, G;
+    int kind;      // Stage1Kind
+    bool stream;   // kind == kStream
+    int P;         // record slots per row
     Stage1Config cfg;
+    ResidentConfig rcfg;
     int grid_y;
     uint32_t k0, k1;
 };
@@ -89,11 +100,48 @@ fs_status check_params(const fs_params* p) {
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-Stage1Config pick_config(int variant, int B) {
-    if (variant == kVarTopk) return B <= 16 ? Stage1Config{1, 4} : Stage1Config{2, 4};
-    if (B <= 16) return Stage1Config{1, 4};
-    if (B <= 32) return Stage1Config{2, 4};
-    return Stage1Config{4, 2};
+// Stage-1 shape per batch size; FS_STAGE1_CFG="nb,mpi,ks" overrides it for
+// tuning experiments (an unknown shape makes the launch fail with FS_ERR_HIP).
+Stage1Config pick_config(bool stream, int B) {
+    static const char* env = std::getenv("FS_STAGE1_CFG");
+    if (env && stream) {
+        Stage1Config c{0, 0, 0};
+        if (std::sscanf(env, "%d,%d,%d", &c.nb, &c.mpi, &c.ks) == 3) return c;
+    }
+    if (stream) {
+        if (B <= 16) return Stage1Config{1, 4, 2};
+        if (B <= 32) return Stage1Config{2, 4, 1};
+        return Stage1Config{4, 2, 2};
+    }
+    return B <= 16 ? Stage1Config{1, 4, 2} : Stage1Config{2, 4, 1};
+}
+
+// Resident-H shape for a batch and hidden size (nw == 0: none instantiated).
+// FS_RES_CFG="nb,mpi,ks,nw" overrides it for tuning experiments.
+ResidentConfig pick_resident(int B, int nks) {
+    static const char* env = std::getenv("FS_RES_CFG");
+    if (env) {
+        ResidentConfig c{0, 0, 0, 0, 0};
+        if (std::sscanf(env, "%d,%d,%d,%d", &c.nb, &c.mpi, &c.ks, &c.nw) == 4 && c.nw > 0 &&
+            nks % c.nw == 0) {
+            c.hk = nks / c.nw;
+            return c;
+        }
+        return ResidentConfig{0, 0, 0, 0, 0};
+    }
+    return resident_default(B <= 16 ? 1 : 2, nks);
+}
+
+// FS_STAGE1_KIND=coop|stream forces a kernel family for tuning experiments.
+int forced_kind() {
+    static const int k = [] {
+        const char* e = std::getenv("FS_STAGE1_KIND");
+        if (!e) return -1;
+        if (!std::strcmp(e, "coop")) return (int)kCoop;
+        if (!std::strcmp(e, "stream")) return (int)kStream;
+        return -1;
+    }();
+    return k;
 }
 
 void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
@@ -106,9 +154,30 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     pl.T = (p->V + pl.tile_v - 1) / pl.tile_v;
     pl.nmb = (p->V + kMBlock - 1) / kMBlock;
     pl.tile_mb = (variant == kVarGrouped) ? pl.tile_v / kMBlock : INT32_MAX / 2;
-    pl.G = std::max(1, std::min(pl.nmb, cus * wg_per_cu()));
-    pl.cfg = pick_config(variant, p->B);
-    pl.grid_y = (p->B + 16 * pl.cfg.nb - 1) / (16 * pl.cfg.nb);
+    const int nks = (p->d + 31) / 32;
+    pl.kind = kCoop;
+    if (variant != kVarTopk) {
+        pl.rcfg = pick_resident(p->B, nks);
+        if (pl.rcfg.nw > 0 && resident_supported(pl.rcfg))
+            pl.kind = kResident;
+        else if (pl.nmb >= 4)
+            pl.kind = kStream;
+        const int forced = forced_kind();
+        if (forced == kCoop || (forced == kStream && pl.nmb >= 4)) pl.kind = forced;
+    }
+    pl.stream = pl.kind == kStream;
+    if (pl.kind == kStream) {
+        // four worker waves per workgroup, at most one worker per block
+        pl.G = std::max(1, std::min(pl.nmb / 4, cus * wg_per_cu()));
+        pl.P = 4 * pl.G;
+    } else {
+        pl.G = std::max(1, std::min(pl.nmb, cus * wg_per_cu()));
+        pl.P = pl.G;
+    }
+    if (variant == kVarGrouped) pl.P += pl.T - 1;
+    pl.cfg = pick_config(pl.stream, p->B);
+    const int nb = pl.kind == kResident ? pl.rcfg.nb : pl.cfg.nb;
+    pl.grid_y = (p->B + 16 * nb - 1) / (16 * nb);
     pl.k0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
     pl.k1 = (uint32_t)(p->seed >> 32);
 }
@@ -124,7 +193,14 @@ struct Workspace {
     float* mm = nullptr;
     float* ms = nullptr;
     uint64_t* mkey = nullptr;
+    void* part = nullptr;   // streaming stage 1: parked partial sums of split blocks
 };
+
+// Partial sums parked by the streaming kernel: per y-block, worker and side
+// (head, tail), nb 16x16 FP32 tiles.
+size_t part_bytes(const Plan& pl) {
+    return (size_t)pl.grid_y * (4 * pl.G) * 2 * pl.cfg.nb * 1024;
+}
 
 size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
     size_t off = 0;
@@ -135,17 +211,21 @@ size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
     };
     const size_t B = (size_t)pl.B;
     if (variant == FS_VARIANT_FLAT || variant == FS_VARIANT_GROUPED) {
-        const size_t P = variant == FS_VARIANT_FLAT ? (size_t)pl.G : (size_t)pl.G + pl.T - 1;
+        const size_t P = (size_t)pl.P;
         char* a = take(P * B * 4);
         char* b = take(P * B * 4);
         char* c = variant == FS_VARIANT_GROUPED ? take(P * B * 4) : nullptr;
-        if (w) { w->pm = (float*)a; w->pidx = (int32_t*)b; w->pL = (float*)c; }
+        char* d = pl.stream ? take(part_bytes(pl)) : nullptr;
+        if (w) { w->pm = (float*)a; w->pidx = (int32_t*)b; w->pL = (float*)c; w->part = d; }
     } else if (variant == FS_VARIANT_TOPK) {
         const size_t n = (size_t)pl.G * B * (size_t)k;
         char* a = take(n * 4);
         char* b = take(n * 4);
         char* c = take(n * 4);
         if (w) { w->cx = (float*)a; w->cs = (float*)b; w->cidx = (int32_t*)c; }
+    } else if (variant == FS_VARIANT_LOGITS) {
+        char* a = pl.stream ? take(part_bytes(pl)) : nullptr;
+        if (w) w->part = a;
     } else if (variant == FS_VARIANT_MULTINOMIAL) {
         const size_t nchunk = (size_t)(pl.V + kMultinomialChunk - 1) / kMultinomialChunk;
         char* a = take(nchunk * B * 4);
@@ -212,16 +292,17 @@ int32_t fs_num_tiles(const fs_params* p) {
 
 size_t fs_workspace_bytes(const fs_params* p, int variant, int32_t k) {
     if (check_params(p) != FS_OK) return 0;
-    if (variant < FS_VARIANT_FLAT || variant > FS_VARIANT_MULTINOMIAL) return 0;
+    if (variant < FS_VARIANT_FLAT || variant > FS_VARIANT_LOGITS) return 0;
     if (variant == FS_VARIANT_TOPK && (k < 1 || k > kMaxTopK)) return 0;
     DeviceInfo dev;
     if (!current_device(dev)) return 0;
     Plan pl;
-    make_plan(p, variant == FS_VARIANT_GROUPED ? kVarGrouped
-                 : variant == FS_VARIANT_TOPK  ? kVarTopk
-                                               : kVarFlat,
+    make_plan(p, variant == FS_VARIANT_GROUPED  ? kVarGrouped
+                 : variant == FS_VARIANT_TOPK   ? kVarTopk
+                 : variant == FS_VARIANT_LOGITS ? kVarLogits
+                                                : kVarFlat,
               dev.cus, pl);
-    return layout(variant, pl, k, nullptr, nullptr);
+    return std::max(kAlign, layout(variant, pl, k, nullptr, nullptr));
 }
 
 // Shared front half of fs_sample and fs_sample_stage1: validation, plan,
@@ -248,7 +329,11 @@ static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, c
     Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
     a.pm = w.pm;
     a.pidx = w.pidx;
-    if (launch_stage1(kVarFlat, a, pl.grid_y, pl.cfg, s) != hipSuccess) return FS_ERR_HIP;
+    const hipError_t e =
+        pl.kind == kResident ? launch_resident(kVarFlat, a, pl.grid_y, pl.rcfg, s)
+        : pl.stream          ? launch_stream(kVarFlat, a, pl.grid_y, pl.cfg, w.part, need_out, s)
+                             : launch_stage1(kVarFlat, a, pl.grid_y, pl.cfg, s);
+    if (e != hipSuccess) return FS_ERR_HIP;
     done = false;
     return FS_OK;
 }
@@ -263,7 +348,7 @@ fs_status fs_sample(const fs_params* p, const void* H, const void* W, const floa
     fs_status st = flat_stage1(p, H, W, temp, allow, out_idx, out_score, ws, ws_bytes, s, true,
                                pl, w, done);
     if (st != FS_OK || done) return st;
-    return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.G, pl.B, out_idx, out_score, s));
+    return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.P, pl.B, out_idx, out_score, s));
 }
 
 fs_status fs_sample_stage1(const fs_params* p, const void* H, const void* W, const float* temp,
@@ -298,10 +383,18 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     a.pm = w.pm;
     a.pidx = w.pidx;
     a.pL = w.pL;
-    hipError_t e = launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);
+    hipError_t e =
+        pl.kind == kResident ? launch_resident(kVarGrouped, a, pl.grid_y, pl.rcfg, s)
+        : pl.stream          ? launch_stream(kVarGrouped, a, pl.grid_y, pl.cfg, w.part, true, s)
+                             : launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
-    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.B, pl.T, pl.G, pl.nmb,
-                                          pl.tile_mb, temp, p->flags, pl.k0, pl.k1, p->step,
+    // record slot (worker w, tile t) is w + t; the streaming kernel's workers
+    // own ranges of (block, quarter) units, the cooperative kernel's of blocks
+    const int workers = pl.stream ? 4 * pl.G : pl.G;
+    const int units = pl.stream ? 4 * pl.nmb : pl.nmb;
+    const int tile_units = pl.stream ? 4 * pl.tile_mb : pl.tile_mb;
+    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.B, pl.T, workers, units,
+                                          tile_units, temp, p->flags, pl.k0, pl.k1, p->step,
                                           tile_max, tile_idx, tile_logmass, out_idx, s));
 }
 
@@ -350,7 +443,7 @@ fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L
 }
 
 fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* logits,
-                    void* stream) {
+                    void* ws, size_t ws_bytes, void* stream) {
     fs_status st = check_params(p);
     if (st != FS_OK) return st;
     if (p->B == 0 || p->V == 0) return FS_OK;
@@ -362,7 +455,18 @@ fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* log
     make_plan(p, kVarLogits, dev.cus, pl);
     Stage1Args a = stage1_args(pl, p, H, W, nullptr, nullptr);
     a.logits = logits;
-    return from_hip(launch_stage1(kVarLogits, a, pl.grid_y, pl.cfg,
+    if (pl.kind == kResident)
+        return from_hip(launch_resident(kVarLogits, a, pl.grid_y, pl.rcfg,
+                                        static_cast<hipStream_t>(stream)));
+    if (!pl.stream)
+        return from_hip(launch_stage1(kVarLogits, a, pl.grid_y, pl.cfg,
+                                      static_cast<hipStream_t>(stream)));
+    // the split blocks' partial sums travel through the caller's workspace
+    Workspace w;
+    if (!ws || ws_bytes < layout(FS_VARIANT_LOGITS, pl, 0, nullptr, nullptr))
+        return FS_ERR_WORKSPACE;
+    layout(FS_VARIANT_LOGITS, pl, 0, static_cast<char*>(ws), &w);
+    return from_hip(launch_stream(kVarLogits, a, pl.grid_y, pl.cfg, w.part, true,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -400,6 +504,23 @@ fs_status fs_debug_noise(uint64_t seed, uint32_t step, uint32_t stream_id, int32
     return from_hip(launch_debug_noise((uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32),
                                        step, stream_id, b0, nb, i0, ni, words, gumbel,
                                        static_cast<hipStream_t>(stream)));
+}
+
+fs_status fs_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                              void* stream) {
+    if (!src || !sink || grid < 1 || bytes % 16 != 0) return FS_ERR_INVALID_ARG;
+    if (!aligned16(src)) return FS_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    return from_hip(launch_read_probe(src, bytes, sink, grid, static_cast<hipStream_t>(stream)));
+}
+
+fs_status fs_debug_copy(void* dst, const void* src, size_t bytes, int32_t grid, void* stream) {
+    if (!src || !dst || grid < 1 || bytes % 16 != 0) return FS_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(dst)) return FS_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    return from_hip(launch_copy(dst, src, bytes, grid, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

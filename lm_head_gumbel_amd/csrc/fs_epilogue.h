@@ -1,0 +1,111 @@
+// Epilogue of the stage-1 kernels, shared by all of them: per-column
+// temperature and mask, Philox-Gumbel noise for one MFMA lane's four rows,
+// folding into a column's running winner and log-mass, the cross-lane column
+// reduction and the record writes ("FlashSampling" explainer on aitrends.kr,
+// Stage 1 and tensor-parallel paragraphs).
+#pragma once
+
+#include "fs_device.h"
+#include "fs_internal.h"
+
+namespace fs {
+
+// Per-column constants of the epilogue.
+struct ColCtx {
+    int col;
+    bool ok;
+    bool greedy;
+    float inv_t;
+    const uint32_t* allow_row;
+};
+
+__device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
+    ColCtx c;
+    c.col = col;
+    c.ok = col < a.B;
+    c.greedy = true;
+    c.inv_t = 1.f;
+    if (c.ok) {
+        const float T = a.temp ? a.temp[col] : 1.f;
+        c.greedy = (a.flags & kFlagNoNoise) || !(T > 0.f);
+        c.inv_t = c.greedy ? 1.f : 1.f / T;
+    }
+    c.allow_row = (a.allow && c.ok) ? a.allow + (size_t)col * ((a.V + 31) >> 5) : nullptr;
+    return c;
+}
+
+// Tempered, masked logits x and noisy scores s of four consecutive rows
+// row0..row0+3 (local W rows) of one column.
+__device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c, f32x4 v,
+                                            int row0, bool blk_ok, float (&x)[4],
+                                            float (&s)[4]) {
+    const int gid0 = a.v_offset + row0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = row0 + r;
+        bool ok = blk_ok && c.ok && (i < a.V) && (gid0 + r < a.n_valid);
+        if (ok && c.allow_row) ok = (c.allow_row[i >> 5] >> (i & 31)) & 1u;
+        const float xv = v[r] * c.inv_t;
+        x[r] = (ok && xv == xv) ? xv : -INFINITY;
+        s[r] = x[r];
+    }
+    if (!c.greedy && blk_ok && c.ok) {
+        const uint4 rw = philox4x32_10(
+            make_uint4((uint32_t)gid0 >> 2, (uint32_t)c.col, a.step, kStreamToken), a.k0, a.k1);
+        s[0] += gumbel_from_word(rw.x);
+        s[1] += gumbel_from_word(rw.y);
+        s[2] += gumbel_from_word(rw.z);
+        s[3] += gumbel_from_word(rw.w);
+    }
+}
+
+// Folds four (x, s) pairs into a column's running winner and log-mass.
+template <int VAR>
+__device__ __forceinline__ void fold(uint64_t& best, Lse& lse, const float (&x)[4],
+                                     const float (&s)[4], int gid0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (x[r] > -INFINITY) {
+            best = key_max(best, pack_key(s[r], gid0 + r));
+            if constexpr (VAR == kVarGrouped) lse = lse_add(lse, x[r]);
+        }
+    }
+}
+
+// Combines the four lanes that share a column (lanes l, l^16, l^32, l^48).
+template <int VAR>
+__device__ __forceinline__ void column_reduce(uint64_t& best, Lse& lse) {
+    best = key_max(best, shfl_xor_u64(best, 16));
+    best = key_max(best, shfl_xor_u64(best, 32));
+    if constexpr (VAR == kVarGrouped) {
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1)
+            lse = lse_merge(lse, Lse{__shfl_xor(lse.mx, m, 64), __shfl_xor(lse.sm, m, 64)});
+    }
+}
+
+// Writes (or, with MERGE, merges into) the record of column c.col at slot p.
+template <int VAR, bool MERGE>
+__device__ __forceinline__ void put_record(const Stage1Args& a, int p, const ColCtx& c,
+                                           uint64_t best, Lse lse) {
+    if (!c.ok) return;
+    const size_t o = (size_t)p * a.B + c.col;
+    float L = c.greedy ? lse.mx : lse_value(lse);
+    if constexpr (MERGE) {
+        const int32_t old_id = a.pidx[o];
+        if (old_id >= 0) best = key_max(best, pack_key(a.pm[o], old_id));
+        if constexpr (VAR == kVarGrouped) {
+            const float Lo = a.pL[o];
+            if (c.greedy)
+                L = fmaxf(L, Lo);
+            else
+                L = lse_value(lse_merge(Lse{Lo, 1.f}, Lse{L, 1.f}));
+        }
+    }
+    const int32_t id = key_index(best);
+    a.pm[o] = id >= 0 ? key_score(best) : -INFINITY;
+    a.pidx[o] = id;
+    if constexpr (VAR == kVarGrouped) a.pL[o] = L;
+}
+
+}  // namespace fs

@@ -24,6 +24,29 @@ __host__ __device__ inline int part_owner(int m, int nmb, int G) {
     return (int)((((int64_t)m + 1) * G - 1) / nmb);
 }
 
+// Streaming stage 1: a unit is (16-row block, hidden-dimension quarter); worker
+// wk of W owns units [wk*U/W, (wk+1)*U/W) of U = 4*nmb.  With W <= nmb every
+// range holds >= 4 units, so a block is split between at most two workers.
+struct WorkerRange {
+    int u0, u1;    // unit range
+    int hb, hq;    // head partial block and its first quarter (hq == 0: none)
+    int fb0, fb1;  // whole blocks [fb0, fb1)
+    int tb, tq;    // tail partial block and its quarter count (tq == 0: none)
+};
+__host__ __device__ inline WorkerRange worker_range(int wk, int W, int nmb) {
+    const int64_t U = 4ll * nmb;
+    WorkerRange r;
+    r.u0 = (int)(wk * U / W);
+    r.u1 = (int)((wk + 1) * U / W);
+    r.hb = r.u0 / 4;
+    r.hq = r.u0 % 4;
+    r.fb0 = (r.u0 + 3) / 4;
+    r.fb1 = r.u1 / 4;
+    r.tb = r.u1 / 4;
+    r.tq = r.u1 % 4;
+    return r;
+}
+
 struct Stage1Args {
     const uint16_t* H;      // [B, d] bf16
     const uint16_t* W;      // [V, d] bf16
@@ -49,11 +72,30 @@ struct Stage1Args {
 
 struct Stage1Config {
     int nb;   // 16-wide batch blocks per workgroup
-    int mpi;  // vocab blocks per iteration
+    int mpi;  // vocab blocks per group
+    int ks;   // 32-element k-steps per pipeline stage
 };
 
 hipError_t launch_stage1(int variant, const Stage1Args& a, int grid_y, const Stage1Config& cfg,
                          hipStream_t stream);
+
+// Resident-H stage 1: nw waves split the hidden dimension, hk k-steps each
+// (nks == nw * hk), mpi blocks per group, ks k-steps per pipeline stage.
+struct ResidentConfig {
+    int nb, mpi, ks, nw, hk;
+};
+bool resident_supported(const ResidentConfig& c);
+// Preferred instantiated shape for nb batch blocks and nks k-steps (nw == 0:
+// none).
+ResidentConfig resident_default(int nb, int nks);
+hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
+                           hipStream_t stream);
+
+// Streaming stage 1 (flat, grouped or logits) over a.G workgroups of four
+// worker waves; `part` holds grid_y * 4 * a.G * 2 * nb KiB of partial sums.
+// with_fixup also launches the kernel finishing the split blocks.
+hipError_t launch_stream(int variant, const Stage1Args& a, int grid_y, const Stage1Config& cfg,
+                         void* part, bool with_fixup, hipStream_t stream);
 
 hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
                               int32_t* out_idx, float* out_score, hipStream_t stream);
@@ -82,5 +124,9 @@ hipError_t launch_fill_idx(int32_t* out, int n, int32_t value, float* score, hip
 hipError_t launch_debug_noise(uint32_t k0, uint32_t k1, uint32_t step, uint32_t stream_id,
                               int b0, int nb, int64_t i0, int ni, uint32_t* words, float* gumbel,
                               hipStream_t stream);
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
+                             hipStream_t stream);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t stream);
 
 }  // namespace fs

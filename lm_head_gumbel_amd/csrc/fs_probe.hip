@@ -1,0 +1,53 @@
+// Memory probes: a streaming read (the practical HBM read ceiling that the
+// sampler's stage 1 is compared with) and a plain copy (a kernel of known
+// traffic, used to calibrate hardware byte counters).
+#include "fs_internal.h"
+
+namespace fs {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+// Each thread reads `unroll` 16-byte words per trip of a grid-stride loop and
+// folds them into one word, written once per thread so nothing is elided.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* src, size_t n16,
+                                                         uint32_t* sink) {
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    size_t i = tid;
+    for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+        u32x4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = *(const global_u32x4*)(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = *(const global_u32x4*)(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    sink[tid] = acc;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(u32x4* dst, const u32x4* src, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = *(const global_u32x4*)(src + i);
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel<8>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, stream, static_cast<u32x4*>(dst),
+                       static_cast<const u32x4*>(src), bytes / 16);
+    return hipGetLastError();
+}
+
+}  // namespace fs

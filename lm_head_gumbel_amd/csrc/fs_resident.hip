@@ -1,0 +1,272 @@
+// Stage 1 of fused LM-head sampling with the hidden states resident in
+// registers (gfx950).  A workgroup of NW waves owns a balanced, contiguous
+// range of 16-row vocabulary blocks; the waves split the hidden dimension, and
+// each wave loads its slice of H (HK k-steps of 32 elements, all 16*NB batch
+// rows) into registers once.  The only loads left in the contraction loop are
+// the W stream, which leaves the vector-memory pipeline to W alone.  Logits of
+// MPI blocks at a time meet in LDS in a fixed wave order, and the epilogue
+// (temperature, masks, Philox-Gumbel noise, per-tile winners and log-mass)
+// follows ("FlashSampling: Fast and Memory-Efficient Exact Sampling",
+// Abstract; FlashSampling explainer on aitrends.kr, Stage 1 and
+// tensor-parallel paragraphs).
+//
+// The per-group loop is unrolled at compile time (HK k-steps per wave, HK/KS
+// stages), so register indices into the resident H are static and every load
+// is unconditional; the next group's first stage is prefetched before the
+// last MFMAs of the current group and stays in flight through the reduction
+// and the epilogue.  Requires nks == NW * HK (the host checks).
+#include "fs_device.h"
+#include "fs_epilogue.h"
+#include "fs_internal.h"
+#include "fs_mfma.h"
+
+namespace fs {
+
+template <int MPI, int KS>
+struct WStage {
+    bf16x8 w[MPI][KS];
+};
+
+// W fragments of stage `it` (k-steps ks0 + it*KS ..) of the rows in wrow.
+template <int MPI, int KS>
+__device__ __forceinline__ void load_w(WStage<MPI, KS>& s, const uint16_t* (&wrow)[MPI], int it,
+                                       int ks0, int kg, int d) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        const int k = (ks0 + it * KS + kk) * 32 + kg * 8;
+        const int kc = k < d ? k : d - 8;   // the matching H fragment is zero
+#pragma unroll
+        for (int j = 0; j < MPI; ++j) s.w[j][kk] = load_bf16x8(wrow[j] + kc);
+    }
+}
+
+template <int NB, int MPI, int KS, int HK>
+__device__ __forceinline__ void mfma_w(f32x4 (&acc)[MPI][NB], const WStage<MPI, KS>& s,
+                                       const bf16x8 (&h)[NB][HK], int it) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.w[j][kk], h[n][it * KS + kk],
+                                                                    acc[j][n], 0, 0, 0);
+}
+
+template <int NB, int MPI, int NW>
+struct ResidentSmem {
+    f32x4 red[2][NW][MPI][NB][64];   // partial tiles of the waves, double-buffered
+    uint64_t fkey[NW][16];
+    float fmx[NW][16];
+    float fsm[NW][16];
+};
+
+template <int NB, int MPI, int KS, int NW, int HK, int VAR>
+__global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
+    static_assert(NW % NB == 0, "NB must divide the wave count");
+    static_assert(HK % (2 * KS) == 0, "stages are processed in pairs");
+    static_assert(VAR == kVarFlat || VAR == kVarGrouped || VAR == kVarLogits, "variant");
+    constexpr int NIT = HK / KS;
+    __shared__ ResidentSmem<NB, MPI, NW> sm;
+
+    const int w = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    const int mb0 = part_begin(w, a.nmb, a.G);
+    const int mb1 = part_begin(w + 1, a.nmb, a.G);
+    const int bbase = blockIdx.y * 16 * NB;
+    const int ks0 = wave * HK;
+
+    // this wave's slice of H, resident for the whole kernel (rows past B reuse
+    // row B - 1, their columns are discarded; k past d reads zeros)
+    bf16x8 hres[NB][HK];
+    {
+        const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero16);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const int b = bbase + n * 16 + r16;
+            const uint16_t* hrow = a.H + (size_t)(b < a.B ? b : a.B - 1) * a.d;
+#pragma unroll
+            for (int s = 0; s < HK; ++s) {
+                const int k = (ks0 + s) * 32 + kg * 8;
+                hres[n][s] = load_bf16x8(k < a.d ? hrow + k : zero);
+            }
+        }
+    }
+
+    // epilogue column of this thread: N-block wave % NB, column lane & 15
+    const int ncol = wave % NB;
+    const ColCtx cc = col_ctx(a, bbase + ncol * 16 + r16);
+
+    WStage<MPI, KS> sa, sb;
+    const uint16_t* wrow[MPI];
+    const uint16_t* wnext[MPI];
+    Group cur = group_at<MPI>(mb0, mb1, a.tile_mb);
+    group_rows<MPI>(wrow, a.W, cur, r16, a.V, a.d);
+    load_w<MPI, KS>(sa, wrow, 0, ks0, kg, a.d);
+
+    uint64_t best = pack_key(-INFINITY, -1);
+    Lse lse = lse_empty();
+    int buf = 0;
+    while (true) {
+        const int gnext = cur.g + cur.nvm;
+        const bool more = gnext < mb1;
+        // after the last group the prefetch re-reads this group's first stage
+        // (cache hits, never used), keeping every load unconditional
+        const Group nxt = more ? group_at<MPI>(gnext, mb1, a.tile_mb) : cur;
+        group_rows<MPI>(wnext, a.W, nxt, r16, a.V, a.d);
+
+        f32x4 acc[MPI][NB];
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // sched_barrier keeps the prefetch ahead of the MFMAs it overlaps
+#pragma unroll
+        for (int it = 0; it < NIT; it += 2) {
+            load_w<MPI, KS>(sb, wrow, it + 1, ks0, kg, a.d);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_w<NB, MPI, KS, HK>(acc, sa, hres, it);
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 2 < NIT)
+                load_w<MPI, KS>(sa, wrow, it + 2, ks0, kg, a.d);
+            else
+                load_w<MPI, KS>(sa, wnext, 0, ks0, kg, a.d);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_w<NB, MPI, KS, HK>(acc, sb, hres, it + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- the waves' partial tiles meet in LDS, summed in wave order ----
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) sm.red[buf][wave][j][n][lane] = acc[j][n];
+        __syncthreads();
+
+#pragma unroll
+        for (int q = 0; q < (MPI * NB + NW - 1) / NW; ++q) {
+            const int jn = wave + NW * q;      // uniform across the wave
+            if (jn >= MPI * NB) break;
+            const int n = jn % NB;             // == ncol
+            const int j = jn / NB;
+            if (j >= cur.nvm) continue;        // uniform
+            f32x4 v = sm.red[buf][0][j][n][lane];
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww) v += sm.red[buf][ww][j][n][lane];
+            const int row0 = (cur.g + j) * kMBlock + 4 * kg;
+            if constexpr (VAR == kVarLogits) {
+                if (cc.ok) {
+                    float* dst = a.logits + (size_t)cc.col * a.V;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + r < a.V) dst[row0 + r] = v[r];
+                }
+            } else {
+                float x[4], s[4];
+                lane_scores(a, cc, v, row0, true, x, s);
+                fold<VAR>(best, lse, x, s, a.v_offset + row0);
+            }
+        }
+        // the next group writes the other buffer; this one is rewritten two
+        // groups on, after every wave has passed the next group's barrier
+        buf ^= 1;
+
+        if constexpr (VAR != kVarLogits) {
+            if (cur.g + cur.nvm == cur.seg_end) {   // a record segment ends here
+                column_reduce<VAR>(best, lse);
+                if (lane < 16) {
+                    sm.fkey[wave][lane] = best;
+                    sm.fmx[wave][lane] = lse.mx;
+                    sm.fsm[wave][lane] = lse.sm;
+                }
+                __syncthreads();
+                if (threadIdx.x < 16 * NB) {
+                    const int n = threadIdx.x >> 4;
+                    const ColCtx c = col_ctx(a, bbase + n * 16 + (threadIdx.x & 15));
+                    uint64_t k = pack_key(-INFINITY, -1);
+                    Lse l = lse_empty();
+                    for (int ww = n; ww < NW; ww += NB) {
+                        k = key_max(k, sm.fkey[ww][threadIdx.x & 15]);
+                        l = lse_merge(l, Lse{sm.fmx[ww][threadIdx.x & 15],
+                                             sm.fsm[ww][threadIdx.x & 15]});
+                    }
+                    put_record<VAR, false>(a, VAR == kVarGrouped ? w + cur.t : w, c, k, l);
+                }
+                __syncthreads();
+                best = pack_key(-INFINITY, -1);
+                lse = lse_empty();
+            }
+        }
+
+        if (!more) break;
+        cur = nxt;
+#pragma unroll
+        for (int j = 0; j < MPI; ++j) wrow[j] = wnext[j];
+    }
+}
+
+template <int NB, int MPI, int KS, int NW, int HK, int VAR>
+static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream) {
+    hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, VAR>), dim3(a.G, grid_y),
+                       dim3(64 * NW), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Instantiated shapes (nb, mpi, ks, nw, hk), in order of preference for a
+// given (nb, hk).  Each fits 256 registers per lane without spilling.
+#define FS_RESIDENT_SHAPES(X) \
+    X(1, 2, 4, 8, 16)         \
+    X(1, 4, 2, 8, 16)         \
+    X(1, 2, 4, 4, 32)         \
+    X(1, 2, 4, 8, 8)          \
+    X(1, 2, 2, 8, 20)         \
+    X(1, 2, 2, 8, 4)          \
+    X(1, 2, 1, 8, 2)          \
+    X(2, 1, 4, 8, 16)         \
+    X(2, 1, 2, 8, 16)         \
+    X(2, 2, 2, 8, 16)         \
+    X(2, 2, 4, 8, 8)          \
+    X(2, 2, 2, 8, 4)          \
+    X(2, 2, 1, 8, 2)
+
+template <int VAR>
+static hipError_t launch_res_var(const Stage1Args& a, int grid_y, const ResidentConfig& c,
+                                 hipStream_t stream) {
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_)                                          \
+    if (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_) \
+        return launch_res<NB_, MPI_, KS_, NW_, HK_, VAR>(a, grid_y, stream);
+    FS_RESIDENT_SHAPES(FS_RES)
+#undef FS_RES
+    return hipErrorInvalidValue;
+}
+
+bool resident_supported(const ResidentConfig& c) {
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_) \
+    if (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_) return true;
+    FS_RESIDENT_SHAPES(FS_RES)
+#undef FS_RES
+    return false;
+}
+
+ResidentConfig resident_default(int nb, int nks) {
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_) \
+    if (nb == NB_ && nks == NW_ * HK_) return ResidentConfig{NB_, MPI_, KS_, NW_, HK_};
+    FS_RESIDENT_SHAPES(FS_RES)
+#undef FS_RES
+    return ResidentConfig{0, 0, 0, 0, 0};
+}
+
+hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
+                           hipStream_t stream) {
+    switch (variant) {
+        case kVarFlat: return launch_res_var<kVarFlat>(a, grid_y, c, stream);
+        case kVarGrouped: return launch_res_var<kVarGrouped>(a, grid_y, c, stream);
+        case kVarLogits: return launch_res_var<kVarLogits>(a, grid_y, c, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fs

@@ -23,24 +23,15 @@
 //    block (counter id >> 2) serves exactly one lane's four ids for a row.
 #include "fs_device.h"
 #include "fs_internal.h"
+#include "fs_mfma.h"
 
 #include <type_traits>
 
 namespace fs {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-}
-
 template <int NB, int MPI>
 struct Stage1Smem {
-    f32x4 red[kWaves][MPI][NB][64];     // partial tiles of the four waves
+    f32x4 red[2][kWaves][MPI][NB][64];  // partial tiles of the four waves, double-buffered
     uint64_t fkey[kWaves][16];          // segment flush: per-wave column winners
     float fmx[kWaves][16];
     float fsm[kWaves][16];
@@ -83,9 +74,10 @@ __device__ void topk_sort(TopkSmem<NB>& t) {
     }
 }
 
-template <int NB, int MPI, int VAR>
+template <int NB, int MPI, int KS, int VAR>
 __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     static_assert(4 % NB == 0, "NB must divide the wave count");
+    static_assert(VAR != kVarTopk || MPI == 4, "top-k stages 64 new rows per group");
     __shared__ Stage1Smem<NB, MPI> sm;
     using TkSmem = typename std::conditional<VAR == kVarTopk, TopkSmem<NB>, NoTopkSmem>::type;
     __shared__ TkSmem tk;
@@ -104,14 +96,13 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     const int ks0 = wave * nks / kWaves;
     const int ks1 = (wave + 1) * nks / kWaves;
 
-    // H rows this lane feeds to the MFMA B operand (one per N-block)
+    // H rows this lane feeds to the MFMA B operand (one per N-block); rows
+    // past B reuse row B - 1 and their columns are discarded
     const uint16_t* hrow[NB];
-    bool hok[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
         const int b = bbase + n * 16 + r16;
-        hok[n] = b < a.B;
-        hrow[n] = a.H + (size_t)(hok[n] ? b : 0) * a.d;
+        hrow[n] = a.H + (size_t)(b < a.B ? b : a.B - 1) * a.d;
     }
 
     // epilogue column of this thread (fixed: N-block wave % NB, column lane & 15)
@@ -136,174 +127,185 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
         __syncthreads();
     }
 
-    int mb = mb0;
-    while (mb < mb1) {
-        const int t = mb / a.tile_mb;
-        const int64_t tile_end = (int64_t)(t + 1) * a.tile_mb;
-        const int seg_end = tile_end < mb1 ? (int)tile_end : mb1;
+    // Software pipeline over the flattened (group, k-stage) stream of this
+    // wave: the loads of the next stage (the next group's first stage at the
+    // end of a group) are issued before the MFMAs of the current one, so they
+    // stay in flight across the LDS reduction and the epilogue.
+    const int n_it = ((ks1 - ks0 + KS - 1) / KS + 1) & ~1;   // even: ping-pong A/B
+    const bool has_k = ks1 > ks0;
+    Operands<NB, MPI, KS> opA, opB;
+    const uint16_t* wrow[MPI];
+    const uint16_t* wnext[MPI];
+    Group cur = group_at<MPI>(mb0, mb1, a.tile_mb);
+    group_rows<MPI>(wrow, a.W, cur, r16, a.V, a.d);
+    if (has_k) load_operands<NB, MPI, KS>(opA, wrow, hrow, 0, ks0, ks1, kg, a.d);
+    const uint16_t* wsel[MPI];
 
-        uint64_t best = pack_key(-INFINITY, -1);
-        Lse lse = lse_empty();
+    uint64_t best = pack_key(-INFINITY, -1);
+    Lse lse = lse_empty();
+    int buf = 0;
+    while (true) {
+        const int gnext = cur.g + cur.nvm;
+        const bool more = gnext < mb1;
+        // after the last group the prefetch re-reads this group's first stage
+        // (cache hits, never used): keeping every load unconditional keeps the
+        // wait counts exact, so no wait drains the pipeline early
+        const Group nxt = more ? group_at<MPI>(gnext, mb1, a.tile_mb) : cur;
+        group_rows<MPI>(wnext, a.W, nxt, r16, a.V, a.d);
 
-        for (int g = mb; g < seg_end; g += MPI) {
-            const int nvm = min(MPI, seg_end - g);   // valid blocks in this group
-            f32x4 acc[MPI][NB];
-            const uint16_t* wrow[MPI];
-            bool wok[MPI];
+        // ---- contraction of this group over the wave's k-range ----
+        f32x4 acc[MPI][NB];
 #pragma unroll
-            for (int j = 0; j < MPI; ++j) {
-                const int row = (g + j) * kMBlock + r16;
-                wok[j] = (j < nvm) && (row < a.V);
-                wrow[j] = a.W + (size_t)(wok[j] ? row : 0) * a.d;
+        for (int j = 0; j < MPI; ++j)
 #pragma unroll
-                for (int n = 0; n < NB; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < NB; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (has_k) {
+            // sched_barrier keeps the compiler from sinking the prefetch below
+            // the MFMAs, which would let the in-flight loads drain every stage
+            for (int it = 0; it < n_it; it += 2) {
+                load_operands<NB, MPI, KS>(opB, wrow, hrow, it + 1, ks0, ks1, kg, a.d);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_operands<NB, MPI, KS>(acc, opA);
+                __builtin_amdgcn_sched_barrier(0);
+                const bool same = it + 2 < n_it;
+#pragma unroll
+                for (int j = 0; j < MPI; ++j) wsel[j] = same ? wrow[j] : wnext[j];
+                load_operands<NB, MPI, KS>(opA, wsel, hrow, same ? it + 2 : 0, ks0, ks1, kg, a.d);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_operands<NB, MPI, KS>(acc, opB);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
 
-            constexpr int KS = 4;
-            for (int ks = ks0; ks < ks1; ks += KS) {
-                bf16x8 wf[MPI][KS];
-                bf16x8 hf[NB][KS];
+        // ---- the four waves' partial tiles meet in LDS (fixed order) ----
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk) {
-                    const int k = (ks + kk) * 32 + kg * 8;
-                    const bool kok = (ks + kk < ks1) && (k < a.d);
+        for (int j = 0; j < MPI; ++j)
 #pragma unroll
-                    for (int j = 0; j < MPI; ++j)
-                        wf[j][kk] = (kok && wok[j]) ? load_bf16x8(wrow[j] + k) : zero_bf16x8();
+            for (int n = 0; n < NB; ++n) sm.red[buf][wave][j][n][lane] = acc[j][n];
+        __syncthreads();
+
+        // ---- epilogue: a unit is four rows of one column (one MFMA lane's share) ----
 #pragma unroll
-                    for (int n = 0; n < NB; ++n)
-                        hf[n][kk] = (kok && hok[n]) ? load_bf16x8(hrow[n] + k) : zero_bf16x8();
+        for (int q = 0; q < (MPI * NB + kWaves - 1) / kWaves; ++q) {
+            const int jn = wave + kWaves * q;      // uniform across the wave
+            if (jn >= MPI * NB) break;
+            const int n = jn % NB;                 // == ncol
+            const int j = jn / NB;
+            const bool blk_ok = j < cur.nvm;
+            f32x4 v = sm.red[buf][0][j][n][lane];
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) v += sm.red[buf][ww][j][n][lane];
+            const int row0 = (cur.g + j) * kMBlock + 4 * kg;   // local W row of v[0]
+
+            if constexpr (VAR == kVarLogits) {
+                if (blk_ok && col_ok) {
+                    float* dst = a.logits + (size_t)col * a.V;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + r < a.V) dst[row0 + r] = v[r];
                 }
+            } else {
+                float x[4];
+                const int gid0 = a.v_offset + row0;
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-                    for (int j = 0; j < MPI; ++j)
-#pragma unroll
-                        for (int n = 0; n < NB; ++n)
-                            acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                wf[j][kk], hf[n][kk], acc[j][n], 0, 0, 0);
-            }
-
-#pragma unroll
-            for (int j = 0; j < MPI; ++j)
-#pragma unroll
-                for (int n = 0; n < NB; ++n) sm.red[wave][j][n][lane] = acc[j][n];
-            __syncthreads();
-
-            // epilogue: unit u covers four rows of one column (an MFMA lane's share)
-#pragma unroll
-            for (int q = 0; q < (MPI * NB + kWaves - 1) / kWaves; ++q) {
-                const int jn = wave + kWaves * q;      // uniform across the wave
-                if (jn >= MPI * NB) break;
-                const int n = jn % NB;                 // == ncol
-                const int j = jn / NB;
-                const bool blk_ok = j < nvm;
-                f32x4 v = sm.red[0][j][n][lane];
-#pragma unroll
-                for (int ww = 1; ww < kWaves; ++ww) v += sm.red[ww][j][n][lane];
-                const int row0 = (g + j) * kMBlock + 4 * kg;   // local W row of v[0]
-
-                if constexpr (VAR == kVarLogits) {
-                    if (blk_ok && col_ok) {
-                        float* dst = a.logits + (size_t)col * a.V;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (row0 + r < a.V) dst[row0 + r] = v[r];
-                    }
-                } else {
-                    float x[4];
-                    const int gid0 = a.v_offset + row0;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = row0 + r;
+                    bool ok = blk_ok && col_ok && (i < a.V) && (gid0 + r < a.n_valid);
+                    if (ok && allow_row) ok = (allow_row[i >> 5] >> (i & 31)) & 1u;
+                    const float xv = v[r] * inv_t;
+                    x[r] = (ok && xv == xv) ? xv : -INFINITY;
+                }
+                float s[4] = {x[0], x[1], x[2], x[3]};
+                if (!greedy && blk_ok && col_ok) {
+                    const uint4 rw = philox4x32_10(
+                        make_uint4((uint32_t)gid0 >> 2, (uint32_t)col, a.step, kStreamToken),
+                        a.k0, a.k1);
+                    s[0] += gumbel_from_word(rw.x);
+                    s[1] += gumbel_from_word(rw.y);
+                    s[2] += gumbel_from_word(rw.z);
+                    s[3] += gumbel_from_word(rw.w);
+                }
+                if constexpr (VAR == kVarTopk) {
+                    // stage this group's values in the new half of the column list
+                    const int slot = 64 + (j * 16 + 4 * kg) % 64;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int i = row0 + r;
-                        bool ok = blk_ok && col_ok && (i < a.V) && (gid0 + r < a.n_valid);
-                        if (ok && allow_row) ok = (allow_row[i >> 5] >> (i & 31)) & 1u;
-                        float xv = v[r] * inv_t;
-                        x[r] = (ok && xv == xv) ? xv : -INFINITY;
+                        const bool live = x[r] > -INFINITY;
+                        tk.key[ncol * 16 + r16][slot + r] = live ? pack_key(x[r], gid0 + r) : 0ull;
+                        tk.s[ncol * 16 + r16][slot + r] = live ? s[r] : -INFINITY;
                     }
-                    float s[4] = {x[0], x[1], x[2], x[3]};
-                    if (!greedy && blk_ok && col_ok) {
-                        const uint4 rw = philox4x32_10(
-                            make_uint4((uint32_t)gid0 >> 2, (uint32_t)col, a.step, kStreamToken),
-                            a.k0, a.k1);
-                        s[0] += gumbel_from_word(rw.x);
-                        s[1] += gumbel_from_word(rw.y);
-                        s[2] += gumbel_from_word(rw.z);
-                        s[3] += gumbel_from_word(rw.w);
-                    }
-                    if constexpr (VAR == kVarTopk) {
-                        // stage this group's values in the new half of the column list
-                        const int slot = 64 + (j * 16 + 4 * kg) % 64;
+                } else {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const bool live = x[r] > -INFINITY;
-                            tk.key[ncol * 16 + r16][slot + r] = live ? pack_key(x[r], gid0 + r) : 0ull;
-                            tk.s[ncol * 16 + r16][slot + r] = live ? s[r] : -INFINITY;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            if (x[r] > -INFINITY) {
-                                best = key_max(best, pack_key(s[r], gid0 + r));
-                                if constexpr (VAR == kVarGrouped) lse = lse_add(lse, x[r]);
-                            }
+                    for (int r = 0; r < 4; ++r) {
+                        if (x[r] > -INFINITY) {
+                            best = key_max(best, pack_key(s[r], gid0 + r));
+                            if constexpr (VAR == kVarGrouped) lse = lse_add(lse, x[r]);
                         }
                     }
                 }
             }
-            if constexpr (VAR == kVarTopk) {
-                // every slot of the new half was written above (empty blocks as key 0)
+        }
+        // The next group writes the other reduction buffer; this one is
+        // rewritten two groups later, after every wave has passed the next
+        // group's barrier and so has finished reading it.
+        buf ^= 1;
+
+        if constexpr (VAR == kVarTopk) {
+            __syncthreads();     // every slot of the new half is written (empty ones as key 0)
+            topk_sort<NB>(tk);   // ends with a barrier
+        }
+
+        // ---- segment end: combine the column winners and write a partial record ----
+        if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
+            if (cur.g + cur.nvm == cur.seg_end) {
+                best = key_max(best, shfl_xor_u64(best, 16));
+                best = key_max(best, shfl_xor_u64(best, 32));
+                if constexpr (VAR == kVarGrouped) {
+#pragma unroll
+                    for (int m = 16; m <= 32; m <<= 1) {
+                        Lse o{__shfl_xor(lse.mx, m, 64), __shfl_xor(lse.sm, m, 64)};
+                        lse = lse_merge(lse, o);
+                    }
+                }
+                if (lane < 16) {
+                    sm.fkey[wave][lane] = best;
+                    sm.fmx[wave][lane] = lse.mx;
+                    sm.fsm[wave][lane] = lse.sm;
+                }
                 __syncthreads();
-                topk_sort<NB>(tk);   // ends with a barrier
-            } else {
-                __syncthreads();     // sm.red is rewritten by the next group
+                if (threadIdx.x < 16 * NB) {
+                    const int n = threadIdx.x >> 4;
+                    const int c = threadIdx.x & 15;
+                    const int b = bbase + n * 16 + c;
+                    uint64_t k = pack_key(-INFINITY, -1);
+                    Lse l = lse_empty();
+                    for (int ww = n; ww < kWaves; ww += NB) {
+                        k = key_max(k, sm.fkey[ww][c]);
+                        l = lse_merge(l, Lse{sm.fmx[ww][c], sm.fsm[ww][c]});
+                    }
+                    if (b < a.B) {
+                        const int p = (VAR == kVarGrouped) ? w + cur.t : w;
+                        const size_t o = (size_t)p * a.B + b;
+                        const int32_t id = key_index(k);
+                        a.pm[o] = id >= 0 ? key_score(k) : -INFINITY;
+                        a.pidx[o] = id;
+                        if constexpr (VAR == kVarGrouped) {
+                            const float T = a.temp ? a.temp[b] : 1.f;
+                            const bool g_row = (a.flags & kFlagNoNoise) || !(T > 0.f);
+                            a.pL[o] = g_row ? l.mx : lse_value(l);
+                        }
+                    }
+                }
+                __syncthreads();
+                best = pack_key(-INFINITY, -1);
+                lse = lse_empty();
             }
         }
 
-        if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
-            // combine the four lanes sharing a column, then the waves sharing it
-            best = key_max(best, shfl_xor_u64(best, 16));
-            best = key_max(best, shfl_xor_u64(best, 32));
-            if constexpr (VAR == kVarGrouped) {
+        if (!more) break;
+        cur = nxt;
 #pragma unroll
-                for (int m = 16; m <= 32; m <<= 1) {
-                    Lse o{__shfl_xor(lse.mx, m, 64), __shfl_xor(lse.sm, m, 64)};
-                    lse = lse_merge(lse, o);
-                }
-            }
-            if (lane < 16) {
-                sm.fkey[wave][lane] = best;
-                sm.fmx[wave][lane] = lse.mx;
-                sm.fsm[wave][lane] = lse.sm;
-            }
-            __syncthreads();
-            if (threadIdx.x < 16 * NB) {
-                const int n = threadIdx.x >> 4;
-                const int c = threadIdx.x & 15;
-                const int b = bbase + n * 16 + c;
-                uint64_t k = pack_key(-INFINITY, -1);
-                Lse l = lse_empty();
-                for (int ww = n; ww < kWaves; ww += NB) {
-                    k = key_max(k, sm.fkey[ww][c]);
-                    l = lse_merge(l, Lse{sm.fmx[ww][c], sm.fsm[ww][c]});
-                }
-                if (b < a.B) {
-                    const int p = (VAR == kVarGrouped) ? w + t : w;
-                    const size_t o = (size_t)p * a.B + b;
-                    const int32_t id = key_index(k);
-                    a.pm[o] = id >= 0 ? key_score(k) : -INFINITY;
-                    a.pidx[o] = id;
-                    if constexpr (VAR == kVarGrouped) {
-                        bool g_row = true;
-                        const float T = a.temp ? a.temp[b] : 1.f;
-                        g_row = (a.flags & kFlagNoNoise) || !(T > 0.f);
-                        a.pL[o] = g_row ? l.mx : lse_value(l);
-                    }
-                }
-            }
-            __syncthreads();
-        }
-        mb = seg_end;
+        for (int j = 0; j < MPI; ++j) wrow[j] = wnext[j];
     }
 
     if constexpr (VAR == kVarTopk) {
@@ -323,21 +325,34 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     }
 }
 
-template <int NB, int MPI, int VAR>
+template <int NB, int MPI, int KS, int VAR>
 static hipError_t launch_one(const Stage1Args& a, int grid_y, hipStream_t stream) {
-    hipLaunchKernelGGL((stage1_kernel<NB, MPI, VAR>), dim3(a.G, grid_y), dim3(kThreads), 0,
+    hipLaunchKernelGGL((stage1_kernel<NB, MPI, KS, VAR>), dim3(a.G, grid_y), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
+// Instantiated (NB, MPI, KS) shapes.  MPI*KS sets the W bytes in flight per
+// wave and stage; NB*KS the H loads; the register budget bounds both.
 template <int VAR>
 static hipError_t launch_var(const Stage1Args& a, int grid_y, const Stage1Config& c,
                              hipStream_t stream) {
-    if (c.nb == 1 && c.mpi == 4) return launch_one<1, 4, VAR>(a, grid_y, stream);
-    if (c.nb == 2 && c.mpi == 4) return launch_one<2, 4, VAR>(a, grid_y, stream);
+#define FS_SHAPE(N_, M_, K_) \
+    if (c.nb == N_ && c.mpi == M_ && c.ks == K_) return launch_one<N_, M_, K_, VAR>(a, grid_y, stream);
+    FS_SHAPE(1, 4, 2)
+    FS_SHAPE(2, 4, 1)
     if constexpr (VAR != kVarTopk) {
-        if (c.nb == 4 && c.mpi == 2) return launch_one<4, 2, VAR>(a, grid_y, stream);
+        FS_SHAPE(1, 4, 4)
+        FS_SHAPE(1, 8, 1)
+        FS_SHAPE(1, 8, 2)
+        FS_SHAPE(1, 2, 4)
+        FS_SHAPE(2, 4, 2)
+        FS_SHAPE(2, 2, 2)
+        FS_SHAPE(2, 8, 1)
+        FS_SHAPE(4, 2, 1)
+        FS_SHAPE(4, 4, 1)
     }
+#undef FS_SHAPE
     return hipErrorInvalidValue;
 }
 

@@ -92,7 +92,8 @@ def run_topk(x, p, k):
 def run_logits(x, p):
     t = torch()
     out = t.full((x.B, x.V), 7.0, dtype=t.float32, device="cuda")
-    fs.check(fs.fs_logits(p, x.H, x.W, out), "fs_logits")
+    ws = workspace(p, fs.FS_VARIANT_LOGITS)
+    fs.check(fs.fs_logits(p, x.H, x.W, out, ws), "fs_logits")
     t.cuda.synchronize()
     return host(out).astype(np.float64), out
 

@@ -74,7 +74,7 @@ def test_null_and_negative_arguments_are_rejected():
     assert fs.fs_sample_grouped(p, 16, 16, None, None, None, None, None) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_merge_online(-1, 4, None, None, None, 0, 0, 0, None) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_merge_online(2, 4, None, None, None, 0, 0, 0, 0x1000) == fs.FS_ERR_INVALID_ARG
-    assert fs.fs_logits(p, 16, 16, None) == fs.FS_ERR_INVALID_ARG
+    assert fs.fs_logits(p, 16, 16, None, 16, 1 << 20) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_multinomial(p, None, None, None, 0x1000) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_debug_noise(0, 0, 0, 0, 1, -1, 4, 0x1000) == fs.FS_ERR_INVALID_ARG
 
@@ -95,11 +95,12 @@ def test_empty_batch_is_a_no_op():
     p = fs.params(0, 64, 128)
     assert fs.fs_sample(p, None, None, None, None, None) == fs.FS_OK
     assert fs.fs_sample_topk(p, None, None, None, None, 5, None) == fs.FS_OK
-    assert fs.fs_logits(p, None, None, None) == fs.FS_OK
+    assert fs.fs_logits(p, None, None, None, None) == fs.FS_OK
     assert fs.fs_merge_online(0, 3, None, None, None, 0, 0, 0, None) == fs.FS_OK
 
 
 def test_workspace_query_rejects_bad_requests():
     assert fs.fs_workspace_bytes(fs.params(2, 60, 128), fs.FS_VARIANT_FLAT) == 0
     assert fs.fs_workspace_bytes(fs.params(2, 64, 128), 7) == 0
+    assert fs.fs_workspace_bytes(fs.params(2, 64, 128), -1) == 0
     assert fs.fs_workspace_bytes(fs.params(2, 64, 128), fs.FS_VARIANT_TOPK, 0) == 0

@@ -149,6 +149,13 @@ CASES = [
     (17, 96, 2500, 256, 285, 0, "range", True),     # two N-blocks, partial
     (40, 128, 1500, 48, 3, 16, "mixed", False),     # four N-blocks, odd tile size
     (3, 512, 4096, 16, 0, 0, "one", False),         # smallest tile
+    # d with nks % 8 == 0 runs the resident-H kernel (one or two batch blocks)
+    (7, 1024, 3000, 128, 7, 0, "mixed", True),
+    (25, 1024, 2600, 64, 0, 32, "range", False),
+    (20, 512, 1500, 256, 5, 0, "mixed", False),
+    (2, 2048, 1111, 32, 1, 16, "range", True),
+    # fewer than four vocab blocks: the workgroup-cooperative kernel
+    (5, 64, 40, 16, 3, 0, "one", False),
 ]
 
 
