@@ -149,8 +149,9 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
 
 def cpu_baseline(torch, H_all, W, B, seconds):
     """The CPU oracle (numpy float64: logits, Philox-Gumbel noise, argmax) on
-    the first v ids of the vocabulary for the headline batch, scaled to a full
-    call.  Returns the JSON object."""
+    the headline batch.  Whole calls are repeated (steps 0, 1, ...) until about
+    `seconds` of CPU time is spent; if one call is longer than that, a prefix
+    of the vocabulary is timed and scaled to the full call."""
     import numpy as np
     from oracle import fs_oracle as O
     try:
@@ -160,24 +161,90 @@ def cpu_baseline(torch, H_all, W, B, seconds):
         cores = 1
     Hb = H_all[:B].view(torch.int16).cpu().numpy().view(np.uint16)
 
-    def run(nv):
-        Wb = W[:nv].view(torch.int16).cpu().numpy().view(np.uint16)
-        t0 = time.perf_counter()
+    def call(Wb, step):
         l = O.logits_bf16(Hb, Wb)
         x = O.tempered(l, None, None, None, 0, 0)
-        s = O.scores(x, None, SEED, 0, 0, 0)
-        O.sample_flat(s)
-        return time.perf_counter() - t0
+        s = O.scores(x, None, SEED, step, 0, 0)
+        return O.sample_flat(s)[0]
 
-    nv = 2048
-    t = run(nv)
-    nv = int(min(V, max(2048, nv * seconds / max(t, 1e-3))) // 16 * 16)
-    t = run(nv)
-    per_call = t * V / nv
+    Wsmall = W[:4096].view(torch.int16).cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    call(Wsmall, 0)
+    est = (time.perf_counter() - t0) * V / 4096          # seconds per full call, estimated
+    if est <= seconds:
+        Wb = W.view(torch.int16).cpu().numpy().view(np.uint16)
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < seconds:
+            call(Wb, n)
+            n += 1
+        t = time.perf_counter() - t0
+        per_call = t / n
+        sample = (f"{n} full oracle calls (float64 logits + Philox-Gumbel + argmax), B={B}, "
+                  f"d={D}, V={V}, steps 0..{n - 1}: {t:.1f} s")
+    else:
+        nv = int(min(V, max(4096, 4096 * seconds / est * V / 4096)) // 16 * 16)
+        Wb = W[:nv].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        call(Wb, 0)
+        t = time.perf_counter() - t0
+        per_call = t * V / nv
+        sample = (f"one oracle call over the first {nv} of {V} ids (B={B}, d={D}): {t:.1f} s, "
+                  f"scaled by {V}/{nv}")
     return {"value": 1.0 / per_call, "unit": "calls/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle flat sample (float64 logits + Philox-Gumbel + argmax) for B={B} "
-                      f"rows over the first {nv} of {V} ids, d={D}: {t:.1f} s, scaled by {V}/{nv}",
-            "seconds_per_call": per_call}
+            "sample": sample, "seconds_per_call": per_call}
+
+
+def hbm_probe(torch, fs, W):
+    """Practical HBM ceiling: a plain streaming read of the W buffer and a copy
+    of 1 GiB, each timed with HIP events (GB/s of bytes moved)."""
+    nbytes = W.numel() * 2
+    sink = torch.empty(256 * 256, dtype=torch.int32, device="cuda")
+    timer = Timer(torch)
+    for i in range(3):
+        fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256), "read probe")
+    t_read, _ = timer.run(lambda i: fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256)), 20)
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    for i in range(3):
+        fs.check(fs.fs_debug_copy(b, a, n, 1024), "copy")
+    t_copy, _ = timer.run(lambda i: fs.check(fs.fs_debug_copy(b, a, n, 1024)), 10)
+    del a, b
+    return {"read_GBps": nbytes / t_read / 1e9, "copy_GBps": 2 * n / t_copy / 1e9,
+            "read_grid": 256, "copy_grid": 1024, "copy_bytes": n}
+
+
+def source_digest():
+    """sha256 over the stage-1 kernel sources, to tell whether a stored
+    counter summary still describes the kernel being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lm_head_gumbel_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(B):
+    """HBM bytes per stage-1 launch from the committed counter summary for
+    batch B, or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"stage1_d4096_v151936_b{B}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -191,6 +258,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -223,6 +291,11 @@ def main():
         log(json.dumps(r))
         rows.append(r)
 
+    probe = None
+    if not args.no_probe:
+        probe = hbm_probe(torch, fs, W)
+        log(json.dumps(probe))
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -248,9 +321,14 @@ def main():
                    "tokens_per_s": head["tokens_per_s"]},
         "roofline": {"bound": "hbm", "achieved": alg_bytes(args.batch) / t_k1 / 1e9,
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": alg_bytes(args.batch) / t_k1 / PEAK_HBM, "traffic": None,
-                     "kernel": "fs::stage1_kernel (flat)", "kernel_us": head["stage1_us"],
-                     "bytes_per_launch": alg_bytes(args.batch)},
+                     "frac": alg_bytes(args.batch) / t_k1 / PEAK_HBM,
+                     "traffic": stored_traffic(args.batch),
+                     "kernel": "fs::resident_kernel (flat stage 1)",
+                     "kernel_us": head["stage1_us"],
+                     "bytes_per_launch": alg_bytes(args.batch),
+                     "frac_of_read_probe": (alg_bytes(args.batch) / t_k1 / 1e9 / probe["read_GBps"]
+                                            if probe else None)},
+        "hbm_probe": probe,
         "cpu_baseline": cpu,
         "unfused_calls_per_s": head.get("unfused_calls_per_s"),
         "variants": {k: head[k] for k in ("grouped_calls_per_s", "topk40_calls_per_s")
