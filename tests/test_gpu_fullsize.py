@@ -1,0 +1,185 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same entry points, same kernels).  The oracle computes the
+rows it is given one by one (all rows up to B = 64, a sample of rows above).
+
+Workloads (synthetic stand-ins for the pages' Qwen3-class decode LM heads):
+  small model   d=2048, V=151936, B in {1, 8, 32}, T=0.7, tiles of 256;
+                1000 decode steps (step = Philox counter word 2) for the
+                histogram test
+  mid-size      d=4096, V=151936, B in {1, 4, 16, 64}, T=1, last 285 ids
+                masked, grouped records and hierarchical resample
+  compute-lean  d=4096, V=128256, B in {128, 256}, T_b ~ U[0.3, 1.5]
+  top-k/online  d=5120, V=152064, B=32, top-40, online merge over 8 chunks of
+                19008 ids
+"""
+import numpy as np
+import pytest
+
+import lm_head_gumbel_amd as fs
+from lm_head_gumbel_amd.inputs import WORKLOADS, PHILOX_SEED, hidden_bf16, weights_bf16
+from oracle import fs_oracle as O
+from gpu_util import (Inputs, TOL_GAP, check_index_rows, check_values, log, run_flat,
+                      run_grouped, run_merge, run_topk, torch)
+from stats_util import chi_square_rows_p, softmax
+
+pytestmark = pytest.mark.gpu
+
+_W_CACHE = {}
+
+
+def weights(V, d):
+    key = (V, d)
+    if key not in _W_CACHE:
+        _W_CACHE.clear()
+        log(f"generating W [{V}, {d}] bf16")
+        _W_CACHE[key] = weights_bf16(V, d)
+    return _W_CACHE[key]
+
+
+def oracle_rows(Hb, Wb, rows, temp, n_valid, seed, step, tile_v, flags=0):
+    """Oracle results for a subset of rows (row b keeps its own noise index b)."""
+    l = O.logits_bf16(Hb[rows], Wb)
+    t = None if temp is None else np.asarray(temp)[rows]
+    x = O.tempered(l, t, n_valid)
+    B, V = x.shape
+    greedy = O.greedy_rows(t, B, flags)
+    s = x.copy()
+    ids = np.arange(V, dtype=np.int64)
+    from oracle import philox as px
+    for j, b in enumerate(rows):
+        if not greedy[j]:
+            s[j] += O.gumbel_from_word(px.noise_words(seed, b, ids, step, px.STREAM_TOKEN))
+    s[np.isneginf(x)] = -np.inf
+    return l, x, s
+
+
+def check_flat(gi, gs, x, s, rows):
+    fidx, fmax, fgap = O.sample_flat(s)
+    n = check_index_rows(gi[rows], fidx, fgap, s, what="flat")
+    check_values(gs[rows], fmax, what="flat score")
+    return n
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_small_model_flat_and_grouped(B):
+    wl = WORKLOADS[f"small_b{B}"]
+    log(f"small model B={B} d={wl.d} V={wl.V}")
+    Hb = hidden_bf16(B, wl.d)
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()
+    x_in = Inputs(Hb, Wb, temp)
+    rows = np.arange(B)
+    for step in (0, 999):
+        p = x_in.params(tile_v=wl.tile_v, seed=PHILOX_SEED, step=step)
+        gi, gs = run_flat(x_in, p)
+        l, x, s = oracle_rows(Hb, Wb, rows, temp, None, PHILOX_SEED, step, wl.tile_v)
+        n = check_flat(gi, gs, x, s, rows)
+        m, ti, L, go = run_grouped(x_in, p)
+        om, oidx, oL, ogap = O.tile_records(x, s, wl.tile_v)
+        check_values(m, om, what="tile max")
+        check_values(L, oL, what="tile log-mass")
+        pinned = ogap > TOL_GAP
+        assert np.array_equal(ti[pinned], oidx[pinned])
+        log(f"  step {step}: {n}/{B} flat rows pinned, {pinned.mean():.4f} of tiles pinned")
+
+
+def test_small_model_histogram_1000_steps():
+    """1000 decode steps of 8 rows: the per-row draws follow softmax(l/0.7)."""
+    wl = WORKLOADS["small_b8"]
+    Hb = hidden_bf16(8, wl.d)
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()
+    x_in = Inputs(Hb, Wb, temp)
+    t = torch()
+    idx = t.empty((1000, 8), dtype=t.int32, device="cuda")
+    p = x_in.params(tile_v=wl.tile_v, seed=PHILOX_SEED)
+    ws = t.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_FLAT), dtype=t.uint8, device="cuda")
+    for step in range(1000):
+        p.step = step
+        fs.check(fs.fs_sample(p, x_in.H, x_in.W, x_in.temp, None, idx[step], None, ws))
+    draws = idx.cpu().numpy()
+    l = O.logits_bf16(Hb, Wb)
+    probs = [softmax(l[b] / float(temp[b])) for b in range(8)]
+    pv = chi_square_rows_p([draws[:, b] for b in range(8)], probs)
+    log(f"pooled chi-square over 8 rows x 1000 steps: p = {pv:.3f}")
+    assert pv > 0.01
+
+
+@pytest.mark.parametrize("B", [1, 4, 16, 64])
+def test_mid_size_masked_grouped(B):
+    wl = WORKLOADS[f"mid_b{B}"]
+    log(f"mid-size B={B} d={wl.d} V={wl.V} n_valid={wl.n_valid}")
+    Hb = hidden_bf16(B, wl.d)
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()
+    x_in = Inputs(Hb, Wb, temp)
+    rows = np.arange(B)
+    step = 3
+    p = x_in.params(n_valid=wl.n_valid, tile_v=wl.tile_v, seed=PHILOX_SEED, step=step)
+    gi, gs = run_flat(x_in, p)
+    l, x, s = oracle_rows(Hb, Wb, rows, temp, wl.n_valid, PHILOX_SEED, step, wl.tile_v)
+    check_flat(gi, gs, x, s, rows)
+    assert np.all(gi < wl.n_valid)
+    m, ti, L, go = run_grouped(x_in, p)
+    om, oidx, oL, ogap = O.tile_records(x, s, wl.tile_v)
+    check_values(m, om, what="tile max")
+    check_values(L, oL, what="tile log-mass")
+    pinned = ogap > TOL_GAP
+    assert np.array_equal(ti[pinned], oidx[pinned])
+    # tiles 1185 and 1186 hold only masked ids; tile 1184 has 29 masked ids
+    assert np.all(ti[:, 1185:] == -1) and np.all(np.isneginf(L[:, 1185:]))
+    gidx, ggap, gt = O.sample_grouped(oidx, oL, temp, PHILOX_SEED, step)
+    pin = (ggap > TOL_GAP) & np.array([gt[b] < 0 or ogap[b, gt[b]] > TOL_GAP for b in rows])
+    assert np.array_equal(go[pin], gidx[pin])
+    log(f"  grouped: {pin.sum()}/{B} rows pinned")
+
+
+@pytest.mark.parametrize("B", [128, 256])
+def test_compute_lean_sampled_rows(B):
+    wl = WORKLOADS[f"large_b{B}"]
+    log(f"compute-leaning B={B} d={wl.d} V={wl.V}")
+    Hb = hidden_bf16(B, wl.d)
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()
+    x_in = Inputs(Hb, Wb, temp)
+    rows = np.unique(np.concatenate([np.arange(0, B, 9), [B - 1]]))
+    for step in (0, 199):
+        p = x_in.params(tile_v=wl.tile_v, seed=PHILOX_SEED, step=step)
+        gi, gs = run_flat(x_in, p)
+        l, x, s = oracle_rows(Hb, Wb, rows, temp, None, PHILOX_SEED, step, wl.tile_v)
+        n = check_flat(gi, gs, x, s, rows)
+        log(f"  step {step}: {n}/{rows.size} sampled rows pinned")
+
+
+def test_topk_and_online_merge():
+    wl = WORKLOADS["topk_b32"]
+    log(f"top-k/online B={wl.B} d={wl.d} V={wl.V} k={wl.k} chunks={wl.chunks}")
+    Hb = hidden_bf16(wl.B, wl.d)
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()
+    x_in = Inputs(Hb, Wb, temp)
+    rows = np.arange(wl.B)
+    step = 11
+    p = x_in.params(tile_v=wl.tile_v, seed=PHILOX_SEED, step=step)
+    l, x, s = oracle_rows(Hb, Wb, rows, temp, None, PHILOX_SEED, step, wl.tile_v)
+    tk = run_topk(x_in, p, wl.k)
+    oi, ogap, omarg = O.topk_sample(x, s, wl.k)
+    pin = (ogap > TOL_GAP) & (omarg > 1e-3)
+    assert np.array_equal(tk[pin], oi[pin])
+    log(f"  top-{wl.k}: {pin.sum()}/{wl.B} rows pinned")
+    # online merge over 8 sequential chunks of V/8 ids: chunk records from the
+    # grouped entry point with one tile per chunk, then the binary merge
+    chunk = wl.V // wl.chunks
+    pc = x_in.params(tile_v=chunk, seed=PHILOX_SEED, step=step)
+    m, ti, L, _ = run_grouped(x_in, pc, with_sample=False)
+    assert ti.shape[1] == wl.chunks
+    om, oidx, oL, cgap = O.tile_records(x, s, chunk)
+    check_values(L, oL, what="chunk log-mass")
+    gz, gA = run_merge(ti, L, temp, PHILOX_SEED, step)
+    oz, oA, omarg = O.online_merge(oidx, oL, temp, PHILOX_SEED, step)
+    check_values(gA, oA, what="merged log-mass")
+    pin = (omarg > 1e-2) & (cgap > TOL_GAP).all(axis=1)
+    assert np.array_equal(gz[pin], oz[pin])
+    # the merged log-mass is the log-sum-exp over the whole vocabulary
+    check_values(gA, [O.log_sum_exp(x[b]) for b in rows], what="total log-mass")
+    log(f"  online merge: {pin.sum()}/{wl.B} rows pinned")
