@@ -82,6 +82,7 @@ struct Plan {
     Stage1Config cfg;
     ResidentConfig rcfg;
     int grid_y;
+    int xcd_pair;
     uint32_t k0, k1;
 };
 
@@ -132,6 +133,15 @@ ResidentConfig pick_resident(int B, int nks) {
     return resident_default(B <= 16 ? 1 : 2, nks);
 }
 
+// FS_XCD_PAIR=0 disables the XCD pairing of batch groups (tuning experiments).
+bool xcd_pairing() {
+    static const bool on = [] {
+        const char* e = std::getenv("FS_XCD_PAIR");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
 // FS_STAGE1_KIND=coop|stream forces a kernel family for tuning experiments.
 int forced_kind() {
     static const int k = [] {
@@ -178,6 +188,16 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     pl.cfg = pick_config(pl.stream, p->B);
     const int nb = pl.kind == kResident ? pl.rcfg.nb : pl.cfg.nb;
     pl.grid_y = (p->B + 16 * nb - 1) / (16 * nb);
+    pl.xcd_pair = 0;
+    if (pl.kind == kResident && pl.grid_y > 1 && xcd_pairing()) {
+        // every batch group of a row range resident at once, on one XCD
+        const int g = (cus * wg_per_cu() / pl.grid_y) / 8 * 8;
+        if (g >= 8 && g <= pl.nmb) {
+            pl.G = g;
+            pl.P = g + (variant == kVarGrouped ? pl.T - 1 : 0);
+            pl.xcd_pair = 1;
+        }
+    }
     pl.k0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
     pl.k1 = (uint32_t)(p->seed >> 32);
 }
@@ -253,6 +273,8 @@ Stage1Args stage1_args(const Plan& pl, const fs_params* p, const void* H, const 
     a.nmb = pl.nmb;
     a.G = pl.G;
     a.tile_mb = pl.tile_mb;
+    a.ny = pl.grid_y;
+    a.xcd_pair = pl.xcd_pair;
     a.k0 = pl.k0;
     a.k1 = pl.k1;
     a.step = p->step;

@@ -58,6 +58,8 @@ struct Stage1Args {
     int tile_mb;            // blocks per record tile (flat: one segment)
     uint32_t k0, k1, step, flags;
     int topk;               // k of the top-k variant
+    int ny;                 // resident kernel: batch groups sharing one row range
+    int xcd_pair;           // resident kernel: 1-D grid, groups of a range on one XCD
     // partial records [P][B] (P = G for flat, G + T - 1 for grouped)
     float* pm;
     int32_t* pidx;

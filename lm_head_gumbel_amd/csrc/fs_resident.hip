@@ -69,14 +69,27 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     constexpr int NIT = HK / KS;
     __shared__ ResidentSmem<NB, MPI, NW> sm;
 
-    const int w = blockIdx.x;
+    // Row range w and batch group y of this workgroup.  With xcd_pair the grid
+    // is 1-D and the ny groups of a range get ids L, L + 8, L + 16, ...:
+    // workgroups are dealt to the eight XCDs round-robin, so the groups that
+    // read the same W rows run at the same time on one XCD and share its L2.
+    int w, y;
+    if (a.xcd_pair) {
+        const int L = blockIdx.x;
+        const int per = 8 * a.ny;
+        y = (L % per) / 8;
+        w = (L / per) * 8 + (L % 8);
+    } else {
+        w = blockIdx.x;
+        y = blockIdx.y;
+    }
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15;
     const int kg = lane >> 4;
     const int mb0 = part_begin(w, a.nmb, a.G);
     const int mb1 = part_begin(w + 1, a.nmb, a.G);
-    const int bbase = blockIdx.y * 16 * NB;
+    const int bbase = y * 16 * NB;
     const int ks0 = wave * HK;
 
     // this wave's slice of H, resident for the whole kernel (rows past B reuse
@@ -210,8 +223,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
 
 template <int NB, int MPI, int KS, int NW, int HK, int VAR>
 static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream) {
-    hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, VAR>), dim3(a.G, grid_y),
-                       dim3(64 * NW), 0, stream, a);
+    const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
+    hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, VAR>), grid, dim3(64 * NW), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
