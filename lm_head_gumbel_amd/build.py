@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfs.so")
-SOURCES = ["fs_api.hip", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_stage2.hip", "fs_probe.hip"]
+SOURCES = ["fs_api.hip", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip", "fs_stage2.hip", "fs_probe.hip"]
 ARCH = "gfx950"
 
 

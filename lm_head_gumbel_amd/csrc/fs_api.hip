@@ -71,7 +71,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // common shapes), stream (independent worker waves, H reloaded per stage) and
 // coop (workgroup-cooperative, H reloaded per stage; top-k and the shapes the
 // others do not cover).
-enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2 };
+enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2, kWide = 3 };
 
 // Validated shape of one call and its launch plan.
 struct Plan {
@@ -81,6 +81,7 @@ struct Plan {
     int P;         // record slots per row
     Stage1Config cfg;
     ResidentConfig rcfg;
+    int nt;        // kWide: batch columns per workgroup
     int grid_y;
     int xcd_pair;
     uint32_t k0, k1;
@@ -133,6 +134,15 @@ ResidentConfig pick_resident(int B, int nks) {
     return resident_default(B <= 16 ? 1 : 2, nks);
 }
 
+// FS_WIDE=0 disables the LDS-tiled large-batch kernel (tuning experiments).
+bool wide_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("FS_WIDE");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
 // FS_XCD_PAIR=0 disables the XCD pairing of batch groups (tuning experiments).
 bool xcd_pairing() {
     static const bool on = [] {
@@ -165,7 +175,10 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     pl.nmb = (p->V + kMBlock - 1) / kMBlock;
     pl.tile_mb = (variant == kVarGrouped) ? pl.tile_v / kMBlock : INT32_MAX / 2;
     const int nks = (p->d + 31) / 32;
+
+    // 1. kernel family
     pl.kind = kCoop;
+    pl.nt = 0;
     if (variant != kVarTopk) {
         pl.rcfg = pick_resident(p->B, nks);
         if (pl.rcfg.nw > 0 && resident_supported(pl.rcfg))
@@ -174,30 +187,45 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
             pl.kind = kStream;
         const int forced = forced_kind();
         if (forced == kCoop || (forced == kStream && pl.nmb >= 4)) pl.kind = forced;
+        // large batches: the LDS-tiled kernel shares each W tile among all columns
+        if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
+            p->d % 64 == 0 && forced < 0 && wide_enabled()) {
+            pl.kind = kWide;
+            pl.nt = p->B <= 64 ? 64 : 128;
+        }
     }
     pl.stream = pl.kind == kStream;
+    pl.cfg = pick_config(pl.stream, p->B);
+
+    // 2. batch groups
+    const int cols = pl.kind == kWide       ? pl.nt
+                     : pl.kind == kResident ? 16 * pl.rcfg.nb
+                                            : 16 * pl.cfg.nb;
+    pl.grid_y = (p->B + cols - 1) / cols;
+
+    // 3. workgroups along the vocabulary and record slots
+    int workers;
     if (pl.kind == kStream) {
         // four worker waves per workgroup, at most one worker per block
         pl.G = std::max(1, std::min(pl.nmb / 4, cus * wg_per_cu()));
-        pl.P = 4 * pl.G;
+        workers = 4 * pl.G;
     } else {
-        pl.G = std::max(1, std::min(pl.nmb, cus * wg_per_cu()));
-        pl.P = pl.G;
+        const int per_cu = pl.kind == kWide ? 1 : wg_per_cu();   // the wide kernel fills LDS
+        pl.G = std::max(1, std::min(pl.nmb, cus * per_cu));
+        workers = pl.G;
     }
-    if (variant == kVarGrouped) pl.P += pl.T - 1;
-    pl.cfg = pick_config(pl.stream, p->B);
-    const int nb = pl.kind == kResident ? pl.rcfg.nb : pl.cfg.nb;
-    pl.grid_y = (p->B + 16 * nb - 1) / (16 * nb);
     pl.xcd_pair = 0;
-    if (pl.kind == kResident && pl.grid_y > 1 && xcd_pairing()) {
-        // every batch group of a row range resident at once, on one XCD
-        const int g = (cus * wg_per_cu() / pl.grid_y) / 8 * 8;
+    if ((pl.kind == kResident || pl.kind == kWide) && pl.grid_y > 1 && xcd_pairing()) {
+        // all batch groups of a row range resident at once, on one XCD
+        const int per_cu = pl.kind == kWide ? 1 : wg_per_cu();
+        const int g = (cus * per_cu / pl.grid_y) / 8 * 8;
         if (g >= 8 && g <= pl.nmb) {
             pl.G = g;
-            pl.P = g + (variant == kVarGrouped ? pl.T - 1 : 0);
+            workers = g;
             pl.xcd_pair = 1;
         }
     }
+    pl.P = workers + (variant == kVarGrouped ? pl.T - 1 : 0);
     pl.k0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
     pl.k1 = (uint32_t)(p->seed >> 32);
 }
@@ -352,7 +380,8 @@ static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, c
     a.pm = w.pm;
     a.pidx = w.pidx;
     const hipError_t e =
-        pl.kind == kResident ? launch_resident(kVarFlat, a, pl.grid_y, pl.rcfg, s)
+        pl.kind == kWide       ? launch_wide(kVarFlat, a, pl.nt, pl.grid_y, s)
+        : pl.kind == kResident ? launch_resident(kVarFlat, a, pl.grid_y, pl.rcfg, s)
         : pl.stream          ? launch_stream(kVarFlat, a, pl.grid_y, pl.cfg, w.part, need_out, s)
                              : launch_stage1(kVarFlat, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
@@ -477,6 +506,9 @@ fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* log
     make_plan(p, kVarLogits, dev.cus, pl);
     Stage1Args a = stage1_args(pl, p, H, W, nullptr, nullptr);
     a.logits = logits;
+    if (pl.kind == kWide)
+        return from_hip(launch_wide(kVarLogits, a, pl.nt, pl.grid_y,
+                                    static_cast<hipStream_t>(stream)));
     if (pl.kind == kResident)
         return from_hip(launch_resident(kVarLogits, a, pl.grid_y, pl.rcfg,
                                         static_cast<hipStream_t>(stream)));

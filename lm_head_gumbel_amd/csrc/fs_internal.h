@@ -93,6 +93,10 @@ ResidentConfig resident_default(int nb, int nks);
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
                            hipStream_t stream);
 
+// LDS-tiled stage 1 for large batches (flat and logits variants): nt batch
+// columns per workgroup (64 or 128); requires d % 64 == 0.
+hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream);
+
 // Streaming stage 1 (flat, grouped or logits) over a.G workgroups of four
 // worker waves; `part` holds grid_y * 4 * a.G * 2 * nb KiB of partial sums.
 // with_fixup also launches the kernel finishing the split blocks.

@@ -1,0 +1,257 @@
+// Stage 1 for large batches (gfx950): an LDS-tiled bf16 GEMM with the
+// sampling epilogue fused in ("FlashSampling: Fast and Memory-Efficient Exact
+// Sampling", Abstract; FlashSampling explainer on aitrends.kr, Stage 1).
+//
+// A workgroup (8 waves) owns a balanced range of 16-row vocabulary blocks and
+// walks it in tiles of MT = 256 rows.  For each tile it contracts over the
+// hidden dimension in chunks of KC = 64: the W tile (256 rows x 128 bytes) and
+// the H tile (NT batch rows x 128 bytes) are loaded cooperatively as whole
+// 128-byte lines (eight lanes per row), written to a double-buffered LDS area
+// with a 144-byte row stride (conflict-free MFMA fragment reads), and each wave
+// computes a 128 x NT/4 sub-tile with v_mfma_f32_16x16x32_bf16 (NT = 64 or
+// 128; wider tiles would not fit the accumulators in 256 registers per lane).  W is read
+// from HBM once; H (at most 256 x d bf16) stays in L2.  After the last chunk
+// of a tile the waves fold their logits into per-column winners (temperature,
+// masks, Philox-Gumbel noise); the column winners of the two row-halves meet
+// in LDS at the end and become the workgroup's record.
+//
+// The loads of chunk s+1 are issued before the MFMAs of chunk s and written
+// to LDS after them, so one chunk of loads is always in flight.
+#include "fs_device.h"
+#include "fs_epilogue.h"
+#include "fs_internal.h"
+#include "fs_mfma.h"
+
+namespace fs {
+
+constexpr int kWideThreads = 512;
+constexpr int kMT = 256;         // rows per tile
+constexpr int kKC = 64;          // k per chunk
+constexpr int kRowBytes = 144;   // LDS row stride: 128 data bytes + 16 pad
+
+template <int NT>
+struct WideSmem {
+    char buf[2][(kMT + NT) * kRowBytes];
+    uint64_t fkey[2][NT];
+};
+
+template <int NT, int VAR>
+__global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
+    static_assert(NT == 64 || NT == 128, "column tile");
+    static_assert(VAR == kVarFlat || VAR == kVarLogits, "variant");
+    constexpr int WM = 2, WN = 4;
+    constexpr int RW = kMT / WM;          // 128 rows per wave
+    constexpr int MF = RW / 16;           // 8 A fragments
+    constexpr int NF = NT / WN / 16;      // 4, 2, 1 B fragments
+    constexpr int WP = kMT * 8 / kWideThreads;   // W pieces of 16 B per thread per chunk
+    constexpr int HP = NT * 8 / kWideThreads;    // H pieces
+    __shared__ WideSmem<NT> sm;
+
+    // row range w and column group y (see resident_kernel for the XCD pairing)
+    int w, y;
+    if (a.xcd_pair) {
+        const int L = blockIdx.x;
+        const int per = 8 * a.ny;
+        y = (L % per) / 8;
+        w = (L / per) * 8 + (L % 8);
+    } else {
+        w = blockIdx.x;
+        y = blockIdx.y;
+    }
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int r16 = lane & 15;
+    const int kg = lane >> 4;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int mb0 = part_begin(w, a.nmb, a.G);
+    const int mb1 = part_begin(w + 1, a.nmb, a.G);
+    const int row_end = min(mb1 * kMBlock, a.V);          // one past this range's last row
+    const int bbase = y * NT;
+    const int nchunks = a.d / kKC;
+    const int ntiles = (mb1 - mb0 + 15) / 16;
+    const int total = ntiles * nchunks;
+
+    // cooperative loader: piece q = tid + 512 i covers 16 bytes of row q >> 3
+    // at byte (q & 7) * 16 of the chunk; eight lanes read one whole line.
+    // Offsets are 32-bit element offsets from the range's first W row and
+    // from H (a range spans a few hundred rows, H at most 256 rows).
+    const uint16_t* wbase = a.W + (size_t)mb0 * kMBlock * a.d;
+    const int first_row = mb0 * kMBlock;
+    int wofs[WP];
+    int hofs[HP];
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+        const int q = tid + kWideThreads * i;
+        int b = bbase + (q >> 3);
+        b = b < a.B ? b : a.B - 1;   // padding columns reuse row B - 1, discarded later
+        hofs[i] = b * a.d + (q & 7) * 8;
+    }
+    auto set_tile_rows = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < WP; ++i) {
+            const int q = tid + kWideThreads * i;
+            int row = (mb0 + tile * 16) * kMBlock + (q >> 3);
+            row = row < row_end ? row : row_end - 1;   // never read another range's rows
+            wofs[i] = (row - first_row) * a.d + (q & 7) * 8;
+        }
+    };
+    // LDS byte offset of piece i of this thread (W rows first, then H rows)
+    auto lds_off = [&](int i, int row_base) {
+        const int q = tid + kWideThreads * i;
+        return (row_base + (q >> 3)) * kRowBytes + (q & 7) * 16;
+    };
+
+    u32x4 wst[WP], hst[HP];
+    auto load_chunk = [&](int c) {
+        const int k = c * kKC;
+#pragma unroll
+        for (int i = 0; i < WP; ++i) wst[i] = *(const global_u32x4*)(wbase + wofs[i] + k);
+#pragma unroll
+        for (int i = 0; i < HP; ++i) hst[i] = *(const global_u32x4*)(a.H + hofs[i] + k);
+    };
+    auto store_chunk = [&](int b) {
+        char* base = sm.buf[b];
+#pragma unroll
+        for (int i = 0; i < WP; ++i) *reinterpret_cast<u32x4*>(base + lds_off(i, 0)) = wst[i];
+#pragma unroll
+        for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4*>(base + lds_off(i, kMT)) = hst[i];
+    };
+
+    // per-lane column winners of this wave (one per B fragment); only the
+    // reciprocal temperature is kept per column, the rest of the column
+    // context is rebuilt in the epilogue without memory reads
+    float inv_t[NF];
+    uint64_t best[NF];
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+        const ColCtx c = col_ctx(a, bbase + wn * (NT / WN) + n * 16 + r16);
+        inv_t[n] = c.greedy ? 0.f : c.inv_t;   // 0 marks a greedy column
+        best[n] = pack_key(-INFINITY, -1);
+    }
+    Lse unused = lse_empty();
+
+    f32x4 acc[MF][NF];
+#pragma unroll
+    for (int j = 0; j < MF; ++j)
+#pragma unroll
+        for (int n = 0; n < NF; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    set_tile_rows(0);
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+
+    for (int s = 0; s < total; ++s) {
+        const int tile = s / nchunks;
+        const int c = s - tile * nchunks;
+        const bool more = s + 1 < total;
+        if (more) {
+            if (c + 1 == nchunks) set_tile_rows(tile + 1);
+            load_chunk(c + 1 == nchunks ? 0 : c + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // blocks of this wave that hold rows of the range (the last tile may be short)
+        const int blk0 = mb0 + tile * 16 + wm * MF;
+        const int nvalid = min(MF, mb1 - blk0);
+        if (nvalid > 0) {
+            const char* base = sm.buf[s & 1];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 bf[NF];
+#pragma unroll
+                for (int n = 0; n < NF; ++n) {
+                    const int col = wn * (NT / WN) + n * 16 + r16;
+                    bf[n] = *reinterpret_cast<const bf16x8*>(base + (kMT + col) * kRowBytes +
+                                                             kk * 64 + kg * 16);
+                }
+#pragma unroll
+                for (int j = 0; j < MF; ++j) {
+                    const int row = wm * RW + j * 16 + r16;
+                    const bf16x8 af =
+                        *reinterpret_cast<const bf16x8*>(base + row * kRowBytes + kk * 64 + kg * 16);
+#pragma unroll
+                    for (int n = 0; n < NF; ++n)
+                        acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[n], acc[j][n],
+                                                                            0, 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        if (c + 1 == nchunks) {
+            // the tile is complete: fold its logits into the column winners
+#pragma unroll
+            for (int j = 0; j < MF; ++j) {
+                if (j >= nvalid) continue;   // uniform
+                const int row0 = (blk0 + j) * kMBlock + 4 * kg;
+#pragma unroll
+                for (int n = 0; n < NF; ++n) {
+                    ColCtx c;
+                    c.col = bbase + wn * (NT / WN) + n * 16 + r16;
+                    c.ok = c.col < a.B;
+                    c.greedy = !(inv_t[n] > 0.f);
+                    c.inv_t = c.greedy ? 1.f : inv_t[n];
+                    c.allow_row = (a.allow && c.ok)
+                                      ? a.allow + (size_t)c.col * ((a.V + 31) >> 5) : nullptr;
+                    if constexpr (VAR == kVarLogits) {
+                        if (c.ok) {
+                            float* dst = a.logits + (size_t)c.col * a.V;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (row0 + r < a.V) dst[row0 + r] = acc[j][n][r];
+                        }
+                    } else {
+                        float x[4], sc[4];
+                        lane_scores(a, c, acc[j][n], row0, true, x, sc);
+                        fold<kVarFlat>(best[n], unused, x, sc, a.v_offset + row0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < MF; ++j)
+#pragma unroll
+                for (int n = 0; n < NF; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        if (more) store_chunk((s + 1) & 1);
+        __syncthreads();
+    }
+
+    if constexpr (VAR == kVarFlat) {
+        // the two row-halves' column winners meet in LDS
+#pragma unroll
+        for (int n = 0; n < NF; ++n) {
+            column_reduce<kVarFlat>(best[n], unused);
+            if (lane < 16) sm.fkey[wm][wn * (NT / WN) + n * 16 + lane] = best[n];
+        }
+        __syncthreads();
+        if (tid < NT) {
+            const ColCtx c = col_ctx(a, bbase + tid);
+            const uint64_t k = key_max(sm.fkey[0][tid], sm.fkey[1][tid]);
+            put_record<kVarFlat, false>(a, w, c, k, lse_empty());
+        }
+    }
+}
+
+template <int NT, int VAR>
+static hipError_t launch_wide_nt(const Stage1Args& a, int grid_y, hipStream_t stream) {
+    const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
+    hipLaunchKernelGGL((wide_kernel<NT, VAR>), grid, dim3(kWideThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream) {
+    if (variant == kVarFlat) {
+        if (nt == 64) return launch_wide_nt<64, kVarFlat>(a, grid_y, stream);
+        if (nt == 128) return launch_wide_nt<128, kVarFlat>(a, grid_y, stream);
+    } else if (variant == kVarLogits) {
+        if (nt == 64) return launch_wide_nt<64, kVarLogits>(a, grid_y, stream);
+        if (nt == 128) return launch_wide_nt<128, kVarLogits>(a, grid_y, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fs

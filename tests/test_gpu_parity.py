@@ -156,6 +156,9 @@ CASES = [
     (2, 2048, 1111, 32, 1, 16, "range", True),
     # fewer than four vocab blocks: the workgroup-cooperative kernel
     (5, 64, 40, 16, 3, 0, "one", False),
+    # B > 32 with d % 64 == 0: the LDS-tiled kernel (one and two column groups)
+    (100, 192, 1700, 64, 0, 16, "range", False),
+    (150, 256, 2000, 128, 5, 0, "mixed", True),
 ]
 
 
