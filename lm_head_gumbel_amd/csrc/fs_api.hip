@@ -118,9 +118,12 @@ Stage1Config pick_config(bool stream, int B) {
     return B <= 16 ? Stage1Config{1, 4, 2} : Stage1Config{2, 4, 1};
 }
 
-// Resident-H shape for a batch and hidden size (nw == 0: none instantiated).
-// FS_RES_CFG="nb,mpi,ks,nw" overrides it for tuning experiments.
-ResidentConfig pick_resident(int B, int nks) {
+// Resident-H shape for a batch, hidden size and variant (nw == 0: none
+// instantiated).  Above 16 rows two batch blocks per workgroup are preferred;
+// where no such shape holds the hidden size, one block per workgroup is used
+// with more batch groups.  FS_RES_CFG="nb,mpi,ks,nw" overrides the choice for
+// tuning experiments.
+ResidentConfig pick_resident(int B, int nks, int variant) {
     static const char* env = std::getenv("FS_RES_CFG");
     if (env) {
         ResidentConfig c{0, 0, 0, 0, 0};
@@ -131,7 +134,9 @@ ResidentConfig pick_resident(int B, int nks) {
         }
         return ResidentConfig{0, 0, 0, 0, 0};
     }
-    return resident_default(B <= 16 ? 1 : 2, nks);
+    ResidentConfig c = resident_default(B <= 16 ? 1 : 2, nks, variant);
+    if (c.nw == 0 && B > 16) c = resident_default(1, nks, variant);
+    return c;
 }
 
 // FS_WIDE=0 disables the LDS-tiled large-batch kernel (tuning experiments).
@@ -179,13 +184,16 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     // 1. kernel family
     pl.kind = kCoop;
     pl.nt = 0;
-    if (variant != kVarTopk) {
-        pl.rcfg = pick_resident(p->B, nks);
-        if (pl.rcfg.nw > 0 && resident_supported(pl.rcfg))
+    const int forced = forced_kind();
+    pl.rcfg = pick_resident(p->B, nks, variant);
+    const bool resident_ok = pl.rcfg.nw > 0 && resident_supported(pl.rcfg, variant);
+    if (variant == kVarTopk) {
+        if (resident_ok && forced < 0) pl.kind = kResident;
+    } else {
+        if (resident_ok)
             pl.kind = kResident;
         else if (pl.nmb >= 4)
             pl.kind = kStream;
-        const int forced = forced_kind();
         if (forced == kCoop || (forced == kStream && pl.nmb >= 4)) pl.kind = forced;
         // large batches: the LDS-tiled kernel shares each W tile among all columns
         if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
@@ -214,11 +222,23 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         pl.G = std::max(1, std::min(pl.nmb, cus * per_cu));
         workers = pl.G;
     }
+    // resident top-k keeps the x of its whole range in LDS: enough workgroups
+    // that no range exceeds that store
+    int min_g = 1;
+    if (variant == kVarTopk && pl.kind == kResident) {
+        const int cap_mb = resident_topk_rows(pl.rcfg.nb) / kMBlock;
+        min_g = (pl.nmb + cap_mb - 1) / cap_mb;
+        if (pl.G < min_g) {
+            pl.G = min_g;
+            workers = min_g;
+        }
+    }
     pl.xcd_pair = 0;
     if ((pl.kind == kResident || pl.kind == kWide) && pl.grid_y > 1 && xcd_pairing()) {
         // all batch groups of a row range resident at once, on one XCD
         const int per_cu = pl.kind == kWide ? 1 : wg_per_cu();
-        const int g = (cus * per_cu / pl.grid_y) / 8 * 8;
+        int g = (cus * per_cu / pl.grid_y) / 8 * 8;
+        if (g < min_g) g = (min_g + 7) / 8 * 8;
         if (g >= 8 && g <= pl.nmb) {
             pl.G = g;
             workers = g;
@@ -474,7 +494,8 @@ fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const
     a.cx = w.cx;
     a.cs = w.cs;
     a.cidx = w.cidx;
-    hipError_t e = launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
+    hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
+                                        : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
     return from_hip(launch_stage2_topk(w.cx, w.cs, w.cidx, pl.G, pl.B, k, out_idx, s));
 }

@@ -34,11 +34,11 @@ __device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
     return c;
 }
 
-// Tempered, masked logits x and noisy scores s of four consecutive rows
-// row0..row0+3 (local W rows) of one column.
-__device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c, f32x4 v,
-                                            int row0, bool blk_ok, float (&x)[4],
-                                            float (&s)[4]) {
+// Tempered, masked logits x of four consecutive rows row0..row0+3 (local W
+// rows) of one column: -inf past V, at or past n_valid, where the allow bit
+// is clear, and for NaN.
+__device__ __forceinline__ void lane_x(const Stage1Args& a, const ColCtx& c, f32x4 v, int row0,
+                                       bool blk_ok, float (&x)[4]) {
     const int gid0 = a.v_offset + row0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -47,8 +47,17 @@ __device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c
         if (ok && c.allow_row) ok = (c.allow_row[i >> 5] >> (i & 31)) & 1u;
         const float xv = v[r] * c.inv_t;
         x[r] = (ok && xv == xv) ? xv : -INFINITY;
-        s[r] = x[r];
     }
+}
+
+// x as above and the noisy scores s = x + Gumbel (s = x for greedy columns).
+__device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c, f32x4 v,
+                                            int row0, bool blk_ok, float (&x)[4],
+                                            float (&s)[4]) {
+    const int gid0 = a.v_offset + row0;
+    lane_x(a, c, v, row0, blk_ok, x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = x[r];
     if (!c.greedy && blk_ok && c.ok) {
         const uint4 rw = philox4x32_10(
             make_uint4((uint32_t)gid0 >> 2, (uint32_t)c.col, a.step, kStreamToken), a.k0, a.k1);

@@ -86,10 +86,19 @@ hipError_t launch_stage1(int variant, const Stage1Args& a, int grid_y, const Sta
 struct ResidentConfig {
     int nb, mpi, ks, nw, hk;
 };
-bool resident_supported(const ResidentConfig& c);
-// Preferred instantiated shape for nb batch blocks and nks k-steps (nw == 0:
-// none).
-ResidentConfig resident_default(int nb, int nks);
+bool resident_supported(const ResidentConfig& c, int variant);
+// Preferred instantiated shape for nb batch blocks, nks k-steps and a
+// variant (nw == 0: none).
+ResidentConfig resident_default(int nb, int nks, int variant);
+// Top-k: the most vocabulary rows one resident workgroup may own.
+int resident_topk_rows(int nb);
+
+// LDS budget of the top-k row store: 96 KiB of x per workgroup.
+template <int NB>
+struct TopkRows {
+    static constexpr int kRows = 96 * 1024 / (16 * NB * 4);   // multiple of 64
+    static constexpr int kStride = kRows + 4;                  // padded row of one column
+};
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
                            hipStream_t stream);
 

@@ -8,7 +8,10 @@
 // (temperature, masks, Philox-Gumbel noise, per-tile winners and log-mass)
 // follows ("FlashSampling: Fast and Memory-Efficient Exact Sampling",
 // Abstract; FlashSampling explainer on aitrends.kr, Stage 1 and
-// tensor-parallel paragraphs).
+// tensor-parallel paragraphs).  The top-k variant keeps the tempered logits
+// of its whole row range in LDS (the range is at most TopkRows<NB>::kRows
+// rows, the host sizes the grid for it) and selects each column's k best at
+// the end (implementation paragraph of the explainer).
 //
 // The per-group loop is unrolled at compile time (HK k-steps per wave, HK/KS
 // stages), so register indices into the resident H are static and every load
@@ -19,6 +22,9 @@
 #include "fs_epilogue.h"
 #include "fs_internal.h"
 #include "fs_mfma.h"
+#include "fs_topk.h"
+
+#include <type_traits>
 
 namespace fs {
 
@@ -61,13 +67,29 @@ struct ResidentSmem {
     float fsm[NW][16];
 };
 
+// Top-k: x of the workgroup's rows, one padded row of LDS per column, plus
+// per-wave staging for the selected candidates.
+template <int NB, int NW>
+struct TopkRowsSmem {
+    float x[16 * NB][TopkRows<NB>::kStride];
+    float sx[NW][64];
+    int sid[NW][64];
+};
+struct NoTopkRows {};
+
+template <int NB, int MPI, int NW>
+constexpr bool topk_fits() {
+    return sizeof(ResidentSmem<NB, MPI, NW>) + sizeof(TopkRowsSmem<NB, NW>) <= 160 * 1024;
+}
+
 template <int NB, int MPI, int KS, int NW, int HK, int VAR>
 __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     static_assert(NW % NB == 0, "NB must divide the wave count");
     static_assert(HK % (2 * KS) == 0, "stages are processed in pairs");
-    static_assert(VAR == kVarFlat || VAR == kVarGrouped || VAR == kVarLogits, "variant");
     constexpr int NIT = HK / KS;
     __shared__ ResidentSmem<NB, MPI, NW> sm;
+    using TkSmem = typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW>, NoTopkRows>::type;
+    __shared__ TkSmem tk;
 
     // Row range w and batch group y of this workgroup.  With xcd_pair the grid
     // is 1-D and the ny groups of a range get ids L, L + 8, L + 16, ...:
@@ -177,6 +199,11 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                     for (int r = 0; r < 4; ++r)
                         if (row0 + r < a.V) dst[row0 + r] = v[r];
                 }
+            } else if constexpr (VAR == kVarTopk) {
+                float x[4];
+                lane_x(a, cc, v, row0, true, x);
+                *reinterpret_cast<f32x4*>(&tk.x[ncol * 16 + r16][row0 - mb0 * kMBlock]) =
+                    f32x4{x[0], x[1], x[2], x[3]};
             } else {
                 float x[4], s[4];
                 lane_scores(a, cc, v, row0, true, x, s);
@@ -187,7 +214,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // groups on, after every wave has passed the next group's barrier
         buf ^= 1;
 
-        if constexpr (VAR != kVarLogits) {
+        if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
             if (cur.g + cur.nvm == cur.seg_end) {   // a record segment ends here
                 column_reduce<VAR>(best, lse);
                 if (lane < 16) {
@@ -219,14 +246,31 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
 #pragma unroll
         for (int j = 0; j < MPI; ++j) wrow[j] = wnext[j];
     }
+
+    if constexpr (VAR == kVarTopk) {
+        // every row of the range is in LDS: each wave selects for its columns
+        __syncthreads();
+        const int nr = (mb1 - mb0) * kMBlock;
+        for (int cl = wave; cl < 16 * NB; cl += NW) {
+            const ColCtx c = col_ctx(a, bbase + cl);
+            if (!c.ok) continue;   // uniform
+            topk_select_column<TopkRows<NB>::kRows / 64>(
+                a, c, tk.x[cl], nr, a.v_offset + mb0 * kMBlock,
+                ((size_t)w * a.B + c.col) * a.topk, tk.sx[wave], tk.sid[wave]);
+        }
+    }
 }
 
 template <int NB, int MPI, int KS, int NW, int HK, int VAR>
 static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream) {
-    const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
-    hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, VAR>), grid, dim3(64 * NW), 0,
-                       stream, a);
-    return hipGetLastError();
+    if constexpr (VAR == kVarTopk && !topk_fits<NB, MPI, NW>()) {
+        return hipErrorInvalidValue;   // the row store does not fit next to this shape's LDS
+    } else {
+        const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
+        hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, VAR>), grid, dim3(64 * NW), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
 }
 
 // Instantiated shapes (nb, mpi, ks, nw, hk), in order of preference for a
@@ -257,17 +301,21 @@ static hipError_t launch_res_var(const Stage1Args& a, int grid_y, const Resident
     return hipErrorInvalidValue;
 }
 
-bool resident_supported(const ResidentConfig& c) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_) \
-    if (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_) return true;
+bool resident_supported(const ResidentConfig& c, int variant) {
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_)                                          \
+    if (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_) \
+        return variant != kVarTopk || topk_fits<NB_, MPI_, NW_>();
     FS_RESIDENT_SHAPES(FS_RES)
 #undef FS_RES
     return false;
 }
 
-ResidentConfig resident_default(int nb, int nks) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_) \
-    if (nb == NB_ && nks == NW_ * HK_) return ResidentConfig{NB_, MPI_, KS_, NW_, HK_};
+int resident_topk_rows(int nb) { return nb == 1 ? TopkRows<1>::kRows : TopkRows<2>::kRows; }
+
+ResidentConfig resident_default(int nb, int nks, int variant) {
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_)                                          \
+    if (nb == NB_ && nks == NW_ * HK_ && (variant != kVarTopk || topk_fits<NB_, MPI_, NW_>())) \
+        return ResidentConfig{NB_, MPI_, KS_, NW_, HK_};
     FS_RESIDENT_SHAPES(FS_RES)
 #undef FS_RES
     return ResidentConfig{0, 0, 0, 0, 0};
@@ -279,6 +327,7 @@ hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const R
         case kVarFlat: return launch_res_var<kVarFlat>(a, grid_y, c, stream);
         case kVarGrouped: return launch_res_var<kVarGrouped>(a, grid_y, c, stream);
         case kVarLogits: return launch_res_var<kVarLogits>(a, grid_y, c, stream);
+        case kVarTopk: return launch_res_var<kVarTopk>(a, grid_y, c, stream);
     }
     return hipErrorInvalidValue;
 }

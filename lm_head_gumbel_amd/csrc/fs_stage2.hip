@@ -10,6 +10,7 @@
 //  * a noise dump used by the tests.
 #include "fs_device.h"
 #include "fs_internal.h"
+#include "fs_topk.h"
 
 namespace fs {
 
@@ -101,11 +102,127 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// top-k: candidates [G][B][k] (x, s, id), each workgroup list sorted by x.
-// Radix select of the k-th largest packed (x, id) key over the row's G*k
-// candidates (8 passes of 8 bits), then argmax s over the keys >= it.
+// top-k: candidates [G][B][k] (x, s, id) from stage 1, one list per workgroup
+// (unused entries have id -1).  The row's k largest (x, -id) over all lists
+// are selected exactly, then the largest s among them wins.
+//
+// stage2_topk_kernel: one workgroup of 512 threads per row holds the order
+// images of the G*k candidate x in registers (PER per thread) and finds the
+// k-th largest value t bit by bit with block-wide counts; among values equal
+// to t the lowest ids are taken (a second bitwise search over ids, only when
+// there are more such ties than places).  Larger candidate sets use the
+// radix-select kernel below it.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRedThreads) void stage2_topk_kernel(const float* cx,
+constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+// Block-wide sum of per-wave counts (each wave passes its uniform count).
+// The two halves of red alternate between calls, so one barrier suffices.
+__device__ __forceinline__ int block_count(int wave_cnt, int (&red)[2][kTopkWaves], int& parity) {
+    if ((threadIdx.x & 63) == 0) red[parity][threadIdx.x >> 6] = wave_cnt;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) t += red[parity][i];
+    parity ^= 1;
+    return t;
+}
+
+__device__ uint64_t block_max_key_topk(uint64_t k) {
+    __shared__ uint64_t part[kTopkWaves];
+    for (int m = 32; m >= 1; m >>= 1) k = key_max(k, shfl_xor_u64(k, m));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = k;
+    __syncthreads();
+    uint64_t r = part[0];
+    for (int i = 1; i < kTopkWaves; ++i) r = key_max(r, part[i]);
+    return r;
+}
+
+template <int PER>
+__global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(const float* cx,
+                                                                   const float* cs,
+                                                                   const int32_t* cidx, int G,
+                                                                   int B, int k,
+                                                                   int32_t* out_idx) {
+    const int b = blockIdx.x;
+    const int n = G * k;
+    __shared__ int red[2][kTopkWaves];
+    int parity = 0;
+    // candidate e = threadIdx.x + kTopkThreads * i: entry e % k of list e / k
+    auto offset = [&](int e) {
+        const int w = e / k;
+        return ((size_t)w * B + b) * k + (e - w * k);
+    };
+    uint32_t u[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = threadIdx.x + kTopkThreads * i;
+        u[i] = 0u;
+        if (e < n) {
+            const size_t o = offset(e);
+            if (cidx[o] >= 0) u[i] = topk_order(cx[o]);
+        }
+    }
+    auto count_ge = [&](uint32_t t) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) c += wave_count(u[i] >= t);
+        return block_count(c, red, parity);
+    };
+
+    // take u > t and, of u == t, the `need` lowest ids (ids <= id_max); with
+    // at most k valid candidates every valid one (t = 1 lies below them all)
+    uint32_t t = 1;
+    int need = 0;
+    int id_max = INT32_MAX;
+    if (count_ge(1) > k) {
+        t = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = t | (1u << bit);
+            if (count_ge(cand) >= k) t = cand;
+        }
+        const int gt = count_ge(t + 1);   // t <= image of +inf: no wrap
+        need = k - gt;
+        const int ties = count_ge(t) - gt;
+        if (ties > need) {
+            // smallest m with #(u == t and id <= m) >= need
+            auto count_tie_le = [&](int m) {
+                int c = 0;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = threadIdx.x + kTopkThreads * i;
+                    bool p = false;
+                    if (u[i] == t) p = cidx[offset(e)] <= m;
+                    c += wave_count(p);
+                }
+                return block_count(c, red, parity);
+            };
+            int lo = 0;
+            for (int bit = 30; bit >= 0; --bit)
+                if (count_tie_le(lo + (1 << bit) - 1) < need) lo += 1 << bit;
+            id_max = lo;
+        }
+    }
+
+    uint64_t best = pack_key(-INFINITY, -1);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = threadIdx.x + kTopkThreads * i;
+        if (u[i] > t || (need > 0 && u[i] == t)) {
+            const size_t o = offset(e);
+            const int32_t id = cidx[o];
+            if (u[i] > t || id <= id_max) best = key_max(best, pack_key(cs[o], id));
+        }
+    }
+    best = block_max_key_topk(best);
+    if (threadIdx.x == 0) out_idx[b] = key_index(best);
+}
+
+// Radix select of the k-th largest packed (x, id) key over the row's G*k
+// candidates (8 passes of 8 bits, candidates re-read from memory each pass),
+// then argmax s over the keys >= it: any number of candidates.
+__global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(const float* cx,
                                                                   const float* cs,
                                                                   const int32_t* cidx, int G,
                                                                   int B, int k,
@@ -427,8 +544,21 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
 
 hipError_t launch_stage2_topk(const float* cx, const float* cs, const int32_t* cidx, int G,
                               int B, int k, int32_t* out_idx, hipStream_t stream) {
-    hipLaunchKernelGGL(stage2_topk_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cs, cidx,
-                       G, B, k, out_idx);
+    const int64_t n = (int64_t)G * k;
+#define FS_TOPK2(PER_)                                                                       \
+    if (n <= (int64_t)kTopkThreads * PER_) {                                                 \
+        hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \
+                           cx, cs, cidx, G, B, k, out_idx);                                  \
+        return hipGetLastError();                                                            \
+    }
+    FS_TOPK2(4)
+    FS_TOPK2(8)
+    FS_TOPK2(16)
+    FS_TOPK2(32)
+    FS_TOPK2(64)
+#undef FS_TOPK2
+    hipLaunchKernelGGL(stage2_topk_radix_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cs,
+                       cidx, G, B, k, out_idx);
     return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 import lm_head_gumbel_amd as fs
-from lm_head_gumbel_amd.inputs import (f32_to_bf16_bits, hidden_bf16, normal_f32,
-                                       tiny_reference, weights_bf16)
+from lm_head_gumbel_amd.inputs import (bf16_bits_to_f32, f32_to_bf16_bits, hidden_bf16,
+                                       normal_f32, tiny_reference, weights_bf16)
 from oracle import fs_oracle as O
 from oracle import philox as px
 from gpu_util import (Inputs, TOL_GAP, TOL_VALUE, check_index_rows, check_values, log,
@@ -260,6 +260,38 @@ def test_nan_logits_never_win():
     assert not np.any(gi == 17)
     m, ti, L, _ = run_grouped(x, p)
     check_values(L, r["tile_L"], what="tile log-mass with NaN")
+
+
+@pytest.mark.parametrize("B,d", [(3, 1024), (24, 1024), (5, 136)])
+def test_topk_exact_ties_take_lowest_ids(B, d):
+    """W rows 300..499 are copies of one row aligned with every hidden state,
+    so each batch row's largest logits are 200 exactly equal values.  The
+    top-k set is then ids 300 .. 300+k-1 (ties go to the lower id), spread
+    over several workgroups, and the sample is the largest noisy score among
+    them."""
+    V, lo, hi = 3000, 300, 500
+    Hb, Wb, temp, _ = make_case(B, d, V, "range", False)
+    Wb = Wb.copy()
+    hsum = bf16_bits_to_f32(Hb).astype(np.float64).sum(axis=0)
+    Wb[lo:hi] = f32_to_bf16_bits((20.0 / d * hsum).astype(np.float32))[None, :]
+    x_in = Inputs(Hb, Wb, temp)
+    l = O.logits_bf16(Hb, Wb)
+    assert np.all(l[:, lo:hi] == l[:, lo:lo + 1]) and np.all(l[:, lo] > np.delete(l, np.s_[lo:hi], 1).max(1))
+    for step in (0, 3):
+        p = x_in.params(seed=SEED, step=step, tile_v=128)
+        r = O.run_call(l, temp, None, None, SEED, step, 0, 128)
+        for k in (1, 7, 40):
+            log(f"ties B={B} d={d} k={k} step={step}")
+            got = run_topk(x_in, p, k)
+            assert np.all((got >= lo) & (got < lo + k)), got
+            s = r["s"][:, lo:lo + k]
+            want = lo + np.argmax(s, axis=1)
+            top2 = np.sort(s, axis=1)
+            gap = top2[:, -1] - top2[:, -2] if k > 1 else np.full(B, np.inf)
+            pin = gap > TOL_GAP
+            assert np.array_equal(got[pin], want[pin])
+            oi, _, _ = O.topk_sample(r["x"], r["s"], k)
+            assert np.array_equal(oi[pin], want[pin])
 
 
 def test_repeated_calls_bit_identical():
