@@ -256,7 +256,6 @@ struct Workspace {
     int32_t* pidx = nullptr;
     float* pL = nullptr;
     float* cx = nullptr;
-    float* cs = nullptr;
     int32_t* cidx = nullptr;
     float* mm = nullptr;
     float* ms = nullptr;
@@ -288,9 +287,8 @@ size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
     } else if (variant == FS_VARIANT_TOPK) {
         const size_t n = (size_t)pl.G * B * (size_t)k;
         char* a = take(n * 4);
-        char* b = take(n * 4);
         char* c = take(n * 4);
-        if (w) { w->cx = (float*)a; w->cs = (float*)b; w->cidx = (int32_t*)c; }
+        if (w) { w->cx = (float*)a; w->cidx = (int32_t*)c; }
     } else if (variant == FS_VARIANT_LOGITS) {
         char* a = pl.stream ? take(part_bytes(pl)) : nullptr;
         if (w) w->part = a;
@@ -492,12 +490,12 @@ fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const
     Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
     a.topk = k;
     a.cx = w.cx;
-    a.cs = w.cs;
     a.cidx = w.cidx;
     hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
                                         : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
-    return from_hip(launch_stage2_topk(w.cx, w.cs, w.cidx, pl.G, pl.B, k, out_idx, s));
+    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, pl.B, k, temp, p->flags, pl.k0, pl.k1,
+                                       p->step, out_idx, s));
 }
 
 fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L,

@@ -67,13 +67,11 @@ struct ResidentSmem {
     float fsm[NW][16];
 };
 
-// Top-k: x of the workgroup's rows, one padded row of LDS per column, plus
-// per-wave staging for the selected candidates.
+// Top-k: x of the workgroup's rows, one padded row of LDS per column (also
+// the scratch area of the column's selection).
 template <int NB, int NW>
 struct TopkRowsSmem {
-    float x[16 * NB][TopkRows<NB>::kStride];
-    float sx[NW][64];
-    int sid[NW][64];
+    alignas(16) float x[16 * NB][TopkRows<NB>::kStride];
 };
 struct NoTopkRows {};
 
@@ -134,7 +132,6 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // epilogue column of this thread: N-block wave % NB, column lane & 15
     const int ncol = wave % NB;
     const ColCtx cc = col_ctx(a, bbase + ncol * 16 + r16);
-
     WStage<MPI, KS> sa, sb;
     const uint16_t* wrow[MPI];
     const uint16_t* wnext[MPI];
@@ -249,15 +246,23 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
 
     if constexpr (VAR == kVarTopk) {
         // every row of the range is in LDS: each wave selects for its columns
+        // wave, wave + NW, ... all at once
+        constexpr int C = (16 * NB + NW - 1) / NW;
         __syncthreads();
-        const int nr = (mb1 - mb0) * kMBlock;
-        for (int cl = wave; cl < 16 * NB; cl += NW) {
-            const ColCtx c = col_ctx(a, bbase + cl);
-            if (!c.ok) continue;   // uniform
-            topk_select_column<TopkRows<NB>::kRows / 64>(
-                a, c, tk.x[cl], nr, a.v_offset + mb0 * kMBlock,
-                ((size_t)w * a.B + c.col) * a.topk, tk.sx[wave], tk.sid[wave]);
+        float* xc[C];
+        size_t o[C];
+        int nc = 0;
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+            const int cl = wave + NW * q;
+            const bool ok = cl < 16 * NB && bbase + cl < a.B;
+            nc += ok ? 1 : 0;   // valid columns come first
+            xc[q] = tk.x[ok ? cl : wave];
+            o[q] = ((size_t)w * a.B + bbase + (ok ? cl : 0)) * a.topk;
         }
+        if (nc > 0)
+            topk_select_columns<C, TopkRows<NB>::kRows / 64>(a, nc, xc, (mb1 - mb0) * kMBlock,
+                                                             a.v_offset + mb0 * kMBlock, o);
     }
 }
 

@@ -37,12 +37,11 @@ struct Stage1Smem {
     float fsm[kWaves][16];
 };
 
-// Top-k candidate lists: per column a sorted list of 64 (key, s) entries
+// Top-k candidate lists: per column a sorted list of 64 keys (x, id)
 // followed by 64 slots for the newest block group.
 template <int NB>
 struct TopkSmem {
     uint64_t key[16 * NB][128];
-    float s[16 * NB][128];
 };
 struct NoTopkSmem {};
 
@@ -64,9 +63,6 @@ __device__ void topk_sort(TopkSmem<NB>& t) {
                 if ((ki < kj) == desc) {
                     t.key[c][i] = kj;
                     t.key[c][j] = ki;
-                    const float si = t.s[c][i];
-                    t.s[c][i] = t.s[c][j];
-                    t.s[c][j] = si;
                 }
             }
             __syncthreads();
@@ -120,10 +116,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     const uint32_t* allow_row = (a.allow && col_ok) ? a.allow + (size_t)col * allow_words : nullptr;
 
     if constexpr (VAR == kVarTopk) {
-        for (int e = threadIdx.x; e < 16 * NB * 128; e += kThreads) {
-            tk.key[e / 128][e % 128] = 0ull;
-            tk.s[e / 128][e % 128] = -INFINITY;
-        }
+        for (int e = threadIdx.x; e < 16 * NB * 128; e += kThreads) tk.key[e / 128][e % 128] = 0ull;
         __syncthreads();
     }
 
@@ -216,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
                     x[r] = (ok && xv == xv) ? xv : -INFINITY;
                 }
                 float s[4] = {x[0], x[1], x[2], x[3]};
-                if (!greedy && blk_ok && col_ok) {
+                if (VAR != kVarTopk && !greedy && blk_ok && col_ok) {
                     const uint4 rw = philox4x32_10(
                         make_uint4((uint32_t)gid0 >> 2, (uint32_t)col, a.step, kStreamToken),
                         a.k0, a.k1);
@@ -232,7 +225,6 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
                     for (int r = 0; r < 4; ++r) {
                         const bool live = x[r] > -INFINITY;
                         tk.key[ncol * 16 + r16][slot + r] = live ? pack_key(x[r], gid0 + r) : 0ull;
-                        tk.s[ncol * 16 + r16][slot + r] = live ? s[r] : -INFINITY;
                     }
                 } else {
 #pragma unroll
@@ -319,7 +311,6 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
             const size_t o = ((size_t)w * a.B + b) * a.topk + r;
             const bool live = k != 0ull;
             a.cx[o] = live ? key_score(k) : -INFINITY;
-            a.cs[o] = live ? tk.s[c][r] : -INFINITY;
             a.cidx[o] = live ? key_index(k) : -1;
         }
     }

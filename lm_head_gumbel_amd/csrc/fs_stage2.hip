@@ -102,19 +102,24 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// top-k: candidates [G][B][k] (x, s, id) from stage 1, one list per workgroup
+// top-k: candidates [G][B][k] (x, id) from stage 1, one list per workgroup
 // (unused entries have id -1).  The row's k largest (x, -id) over all lists
-// are selected exactly, then the largest s among them wins.
+// are selected exactly; the noise s = x + Gumbel is drawn for those k only
+// and the largest s wins.
 //
-// stage2_topk_kernel: one workgroup of 512 threads per row holds the order
-// images of the G*k candidate x in registers (PER per thread) and finds the
-// k-th largest value t bit by bit with block-wide counts; among values equal
-// to t the lowest ids are taken (a second bitwise search over ids, only when
-// there are more such ties than places).  Larger candidate sets use the
-// radix-select kernel below it.
+// stage2_topk_kernel: one workgroup of 512 threads per row holds the G*k
+// candidates in registers (PER per thread).  A lower bound
+// prunes the candidates: in each wave the k-th largest of the 64 lane maxima
+// is at most the row's k-th largest x, and so is the largest of these wave
+// bounds.  The few candidates that reach it are gathered in LDS and one wave
+// selects among them (a bound once more, from the lanes' two largest, then
+// an exact bitwise search with ties to the lower id).  When too many reach it, the whole block runs
+// the exact search on all candidates.  More than 512 * 64 candidates use the
+// radix-select kernel below.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkGather = 512;   // gathered candidates, at most 8 per lane of one wave
 
 // Block-wide sum of per-wave counts (each wave passes its uniform count).
 // The two halves of red alternate between calls, so one barrier suffices.
@@ -139,38 +144,167 @@ __device__ uint64_t block_max_key_topk(uint64_t k) {
     return r;
 }
 
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    for (int m = 32; m >= 1; m >>= 1) k = key_max(k, shfl_xor_u64(k, m));
+    return k;
+}
+
+// Key (s, id) of a selected candidate of row b: s = x + Gumbel, or x on a
+// greedy row.
+__device__ __forceinline__ uint64_t scored_key(uint32_t u, int32_t id, int b, bool greedy,
+                                               uint32_t k0, uint32_t k1, uint32_t step) {
+    const float x = ordered_to_float(u);
+    const float s = greedy ? x : x + token_gumbel(k0, k1, step, b, id);
+    return pack_key(s, id);
+}
+
 template <int PER>
-__global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(const float* cx,
-                                                                   const float* cs,
-                                                                   const int32_t* cidx, int G,
-                                                                   int B, int k,
-                                                                   int32_t* out_idx) {
+__global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
+    const float* cx, const int32_t* cidx, int G, int B, int k, const float* temp, uint32_t flags,
+    uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
     const int b = blockIdx.x;
-    const int n = G * k;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const bool greedy = row_is_greedy(temp, b, flags);
     __shared__ int red[2][kTopkWaves];
+    __shared__ uint32_t wbound[kTopkWaves];
+    __shared__ uint32_t g_u[kTopkGather];
+    __shared__ uint32_t g_tb[kTopkGather];
+    __shared__ int g_n;
     int parity = 0;
-    // candidate e = threadIdx.x + kTopkThreads * i: entry e % k of list e / k
-    auto offset = [&](int e) {
-        const int w = e / k;
-        return ((size_t)w * B + b) * k + (e - w * k);
-    };
+    // candidate e = threadIdx.x + 512 * i is entry e % k of list e / k; the
+    // (list, entry) pair advances by (512 / k, 512 % k) per i.  Every
+    // candidate is loaded up front, unconditionally (slots past the end
+    // re-read candidate 0 and are then ignored), so the loads of a thread are
+    // all in flight together.
+    const int n = G * k;
+    const int dq = kTopkThreads / k, dr = kTopkThreads % k;
+    int lw = threadIdx.x / k, lr = threadIdx.x % k;
     uint32_t u[PER];
+    int32_t iv[PER];
+    uint32_t lmax = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = threadIdx.x + kTopkThreads * i;
-        u[i] = 0u;
-        if (e < n) {
-            const size_t o = offset(e);
-            if (cidx[o] >= 0) u[i] = topk_order(cx[o]);
+        const bool ok = threadIdx.x + kTopkThreads * i < n;
+        const size_t o = ok ? ((size_t)lw * B + b) * k + lr : (size_t)b * k;
+        const int32_t id = cidx[o];
+        const float xv = cx[o];
+        iv[i] = ok ? id : -1;
+        u[i] = iv[i] >= 0 ? topk_order(xv) : 0u;
+        lmax = u[i] > lmax ? u[i] : lmax;
+        lw += dq;
+        lr += dr;
+        if (lr >= k) {
+            lr -= k;
+            ++lw;
         }
     }
+
+    // lower bound and gathering of the candidates that reach it
+    uint32_t wb[1];
+    const uint32_t lm[1][1] = {{lmax}};
+    wave_kth<1, 1, 16>(lm, k, wb);
+    if (lane == 0) wbound[wave] = wb[0];
+    if (threadIdx.x == 0) g_n = 0;
+    __syncthreads();
+    uint32_t lo = 1;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) lo = wbound[i] > lo ? wbound[i] : lo;
+    // each wave reserves room for all its survivors with one atomic, then
+    // writes them at ballot-prefix positions
+    {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) c += u[i] >= lo ? 1 : 0;
+        const int nw = wave_sum<PER>(c);
+        int base = 0;
+        if (lane == 0 && nw > 0) base = atomicAdd(&g_n, nw);
+        base = __shfl(base, 0, 64);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const bool keep = u[i] >= lo;
+            const uint64_t kb = __ballot(keep);
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(kb >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0u));
+            if (keep && pos < kTopkGather) {
+                g_u[pos] = u[i];
+                g_tb[pos] = ~(uint32_t)iv[i];
+            }
+            base += __popcll(kb);
+        }
+    }
+    __syncthreads();
+    const int ng = g_n;   // uniform
+
+    if (ng <= kTopkGather) {
+        if (wave != 0) return;
+        // one wave: eight gathered candidates per lane, the bound once more
+        uint32_t v[1][8], tb[1][8];
+        uint32_t top[1][2] = {{0u, 0u}};   // the lane's two largest
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int q = lane + 64 * j;
+            v[0][j] = q < ng ? g_u[q] : 0u;
+            tb[0][j] = g_tb[q];
+            const uint32_t lo1 = v[0][j] < top[0][0] ? v[0][j] : top[0][0];
+            top[0][0] = v[0][j] > top[0][0] ? v[0][j] : top[0][0];
+            top[0][1] = lo1 > top[0][1] ? lo1 : top[0][1];
+        }
+        uint32_t th[1];
+        wave_kth<1, 2, 16>(top, k, th);
+        const uint32_t lo2 = th[0] > 1u ? th[0] : 1u;
+        int c2 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c2 += v[0][j] >= lo2 ? 1 : 0;
+        const int n2 = wave_sum<8>(c2);
+        uint64_t best = pack_key(-INFINITY, -1);
+        if (n2 <= 64) {
+            // compact to one per lane (every lane has read its entries above)
+            int base = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool keep = v[0][j] >= lo2;
+                const uint64_t kb = __ballot(keep);
+                if (keep) {
+                    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                               (uint32_t)(kb >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0u));
+                    g_u[pos] = v[0][j];
+                    g_tb[pos] = tb[0][j];
+                }
+                base += __popcll(kb);
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            uint32_t w1[1][1], t1[1][1];
+            bool sel[1][1];
+            w1[0][0] = lane < n2 ? g_u[lane] : 0u;
+            t1[0][0] = g_tb[lane];
+            wave_select<1, 1>(w1, t1, k, sel);
+            if (sel[0][0])
+                best = scored_key(w1[0][0], (int32_t)~t1[0][0], b, greedy, k0, k1, step);
+        } else {
+            bool sel[1][8];
+            wave_select<1, 8>(v, tb, k, sel);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sel[0][j])
+                    best = key_max(best,
+                                   scored_key(v[0][j], (int32_t)~tb[0][j], b, greedy, k0, k1, step));
+        }
+        best = wave_max_key(best);
+        if (lane == 0) out_idx[b] = key_index(best);
+        return;
+    }
+
+    // many candidates reach the bound: exact search over all of them
     auto count_ge = [&](uint32_t t) {
         int c = 0;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) c += wave_count(u[i] >= t);
-        return block_count(c, red, parity);
+        for (int i = 0; i < PER; ++i) c += u[i] >= t ? 1 : 0;
+        return block_count(wave_sum<PER>(c), red, parity);
     };
-
     // take u > t and, of u == t, the `need` lowest ids (ids <= id_max); with
     // at most k valid candidates every valid one (t = 1 lies below them all)
     uint32_t t = 1;
@@ -190,31 +324,21 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(const float* 
             auto count_tie_le = [&](int m) {
                 int c = 0;
 #pragma unroll
-                for (int i = 0; i < PER; ++i) {
-                    const int e = threadIdx.x + kTopkThreads * i;
-                    bool p = false;
-                    if (u[i] == t) p = cidx[offset(e)] <= m;
-                    c += wave_count(p);
-                }
-                return block_count(c, red, parity);
+                for (int i = 0; i < PER; ++i) c += (u[i] == t && iv[i] <= m) ? 1 : 0;
+                return block_count(wave_sum<PER>(c), red, parity);
             };
-            int lo = 0;
+            int lo_id = 0;
             for (int bit = 30; bit >= 0; --bit)
-                if (count_tie_le(lo + (1 << bit) - 1) < need) lo += 1 << bit;
-            id_max = lo;
+                if (count_tie_le(lo_id + (1 << bit) - 1) < need) lo_id += 1 << bit;
+            id_max = lo_id;
         }
     }
 
     uint64_t best = pack_key(-INFINITY, -1);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = threadIdx.x + kTopkThreads * i;
-        if (u[i] > t || (need > 0 && u[i] == t)) {
-            const size_t o = offset(e);
-            const int32_t id = cidx[o];
-            if (u[i] > t || id <= id_max) best = key_max(best, pack_key(cs[o], id));
-        }
-    }
+    for (int i = 0; i < PER; ++i)
+        if (u[i] > t || (need > 0 && u[i] == t && iv[i] <= id_max))
+            best = key_max(best, scored_key(u[i], iv[i], b, greedy, k0, k1, step));
     best = block_max_key_topk(best);
     if (threadIdx.x == 0) out_idx[b] = key_index(best);
 }
@@ -222,11 +346,9 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(const float* 
 // Radix select of the k-th largest packed (x, id) key over the row's G*k
 // candidates (8 passes of 8 bits, candidates re-read from memory each pass),
 // then argmax s over the keys >= it: any number of candidates.
-__global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(const float* cx,
-                                                                  const float* cs,
-                                                                  const int32_t* cidx, int G,
-                                                                  int B, int k,
-                                                                  int32_t* out_idx) {
+__global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
+    const float* cx, const int32_t* cidx, int G, int B, int k, const float* temp, uint32_t flags,
+    uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
     const int b = blockIdx.x;
     __shared__ uint32_t hist[256];
     __shared__ uint64_t s_prefix;
@@ -289,11 +411,9 @@ __global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(const fl
     uint64_t best = pack_key(-INFINITY, -1);
     for (int e = threadIdx.x; e < n; e += kRedThreads) {
         uint64_t key;
-        if (cand_key(e, key) && key >= thresh) {
-            const int w = e / k, r = e % k;
-            const size_t o = ((size_t)w * B + b) * k + r;
-            best = key_max(best, pack_key(cs[o], cidx[o]));
-        }
+        if (cand_key(e, key) && key >= thresh)
+            best = key_max(best, scored_key(float_to_ordered(key_score(key)), key_index(key), b,
+                                            row_is_greedy(temp, b, flags), k0, k1, step));
     }
     best = block_max_key(best);
     if (threadIdx.x == 0) out_idx[b] = key_index(best);
@@ -542,13 +662,13 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
     return hipGetLastError();
 }
 
-hipError_t launch_stage2_topk(const float* cx, const float* cs, const int32_t* cidx, int G,
-                              int B, int k, int32_t* out_idx, hipStream_t stream) {
-    const int64_t n = (int64_t)G * k;
+hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
+                              const float* temp, uint32_t flags, uint32_t k0, uint32_t k1,
+                              uint32_t step, int32_t* out_idx, hipStream_t stream) {
 #define FS_TOPK2(PER_)                                                                       \
-    if (n <= (int64_t)kTopkThreads * PER_) {                                                 \
+    if ((int64_t)G * k <= (int64_t)kTopkThreads * PER_) {                                   \
         hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \
-                           cx, cs, cidx, G, B, k, out_idx);                                  \
+                           cx, cidx, G, B, k, temp, flags, k0, k1, step, out_idx);           \
         return hipGetLastError();                                                            \
     }
     FS_TOPK2(4)
@@ -557,8 +677,8 @@ hipError_t launch_stage2_topk(const float* cx, const float* cs, const int32_t* c
     FS_TOPK2(32)
     FS_TOPK2(64)
 #undef FS_TOPK2
-    hipLaunchKernelGGL(stage2_topk_radix_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cs,
-                       cidx, G, B, k, out_idx);
+    hipLaunchKernelGGL(stage2_topk_radix_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cidx,
+                       G, B, k, temp, flags, k0, k1, step, out_idx);
     return hipGetLastError();
 }
 

@@ -2,18 +2,22 @@
 // explainer on aitrends.kr, implementation paragraph: top-k candidates per
 // tile, then a global top-k merge).  The candidate set is the k valid ids
 // with the largest tempered logit x, ties to the lower id; the sample is the
-// largest noisy score s = x + Gumbel among them.
+// largest noisy score s = x + Gumbel among them, so noise is only needed for
+// the row's final k candidates.
 //
 // Selection works on the order-preserving 32-bit image of x (masked ids map
 // to 0, below every valid value): the k-th largest value t is found bit by
 // bit from the top by counting the values >= a candidate threshold with wave
-// ballots, then the values > t and the first `need` values == t in id order
-// are taken.  Every step is a count, so the result does not depend on timing.
+// ballots; the values > t are taken, and of the values == t the lowest ids
+// (a second bitwise search, only when there are more ties than places).
+// Every step is a count, so the result does not depend on timing.
 #pragma once
 
 #include "fs_device.h"
 #include "fs_epilogue.h"
 #include "fs_internal.h"
+
+#include <type_traits>
 
 namespace fs {
 
@@ -24,87 +28,296 @@ __device__ __forceinline__ uint32_t topk_order(float x) {
 // Set lanes of a wave-wide predicate (the same value in every lane).
 __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 
-// Gumbel noise of global id gid in column c (token stream).
-__device__ __forceinline__ float token_gumbel(const Stage1Args& a, int col, int gid) {
+constexpr int bits_for(int m) { return m < 2 ? 1 : 1 + bits_for(m >> 1); }
+
+// Wave-wide sum of per-lane counts 0 <= c <= M, one ballot per bit of c:
+// the per-lane sums run on the vector unit, so only a few vector-to-scalar
+// hand-offs remain per count.
+template <int M>
+__device__ __forceinline__ int wave_sum(int c) {
+    int n = 0;
+#pragma unroll
+    for (int b = 0; b < bits_for(M); ++b) n += __popcll(__ballot((c >> b) & 1)) << b;
+    return n;
+}
+
+// Gumbel noise of global id gid in batch row b (token stream).
+__device__ __forceinline__ float token_gumbel(uint32_t k0, uint32_t k1, uint32_t step, int b,
+                                              int gid) {
     const uint4 w4 =
-        philox4x32_10(make_uint4((uint32_t)gid >> 2, (uint32_t)col, a.step, kStreamToken), a.k0,
-                      a.k1);
+        philox4x32_10(make_uint4((uint32_t)gid >> 2, (uint32_t)b, step, kStreamToken), k0, k1);
     const int q = gid & 3;
     const uint32_t word = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
     return gumbel_from_word(word);
 }
 
-// One wave: the top-k candidates of rows [0, nr) of one column whose x sit
-// in LDS at xcol[row] (row r is global id gid0 + r).  Writes a.topk
-// candidates (x, s, id) at offset o of a.cx / a.cs / a.cidx, unused slots as
-// (-inf, -inf, -1).  sx / sid: 64 entries of per-wave LDS staging.  NR * 64
-// must cover nr.
-template <int NR>
-__device__ void topk_select_column(const Stage1Args& a, const ColCtx& c, const float* xcol,
-                                   int nr, int gid0, size_t o, float* sx, int* sid) {
-    const int lane = threadIdx.x & 63;
-    const int k = a.topk;
-    uint32_t u[NR];
+// The k-th largest of the 64 * M values of each of C sets (M per lane), or
+// 0 when a set holds fewer than k nonzero values; bit by bit from the top,
+// every count a wave ballot.  With LOW > 0 the search stops above bit LOW:
+// the result is then the k-th largest value with its low LOW bits cleared,
+// still a value that at least k entries reach (a lower bound).  The C
+// searches run interleaved: each step is a short chain of vector compare,
+// ballot count and scalar select, so interleaving hides its latency.
+template <int C, int M, int LOW = 0>
+__device__ __forceinline__ void wave_kth(const uint32_t (&v)[C][M], int k, uint32_t (&t)[C]) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const int r = lane + 64 * i;
-        u[i] = r < nr ? topk_order(xcol[r]) : 0u;
+    for (int c = 0; c < C; ++c) t[c] = 0;
+    for (int bit = 31; bit >= LOW; --bit) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint32_t cand = t[c] | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < M; ++i) n += v[c][i] >= cand ? 1 : 0;
+            if (wave_sum<M>(n) >= k) t[c] = cand;
+        }
     }
-    auto count_ge = [&](uint32_t t) {
+}
+
+// Exact top-k among M entries per lane, for C independent sets at once:
+// marks the k largest pairs (u, tb) of each set, compared by u and then by
+// tb, among its entries with u > 0 (u == 0: no entry; the pairs of real
+// entries are distinct), or all its real entries when there are at most k.
+// With tb = ~id the lower id wins a tie in u.
+template <int C, int M>
+__device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uint32_t (&tb)[C][M],
+                                            int k, bool (&sel)[C][M]) {
+    auto count = [&](int c, auto pred) {
         int n = 0;
 #pragma unroll
-        for (int i = 0; i < NR; ++i) n += wave_count(u[i] >= t);
-        return n;
+        for (int i = 0; i < M; ++i) n += pred(c, i) ? 1 : 0;
+        return wave_sum<M>(n);
     };
-
-    // select u > t, plus the first `need` of u == t in row order; with at
-    // most k valid values that is every valid one (t = 1 lies below them all)
-    uint32_t t = 1;
-    int need = 0;
-    if (count_ge(1) > k) {
-        t = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = t | (1u << bit);
-            if (count_ge(cand) >= k) t = cand;
-        }
-        need = k - count_ge(t + 1);   // t <= image of +inf, so t + 1 does not wrap
-    }
-
-    // compact the selected (x, id) into the wave's staging area, in row order
-    const uint64_t below = (1ull << lane) - 1ull;
-    int nsel = 0, ties = 0;
+    // per set: take u > t, and u == t with tb >= tt (t, tt wave-uniform)
+    uint32_t t[C], tt[C];
+    bool big[C];
+    int need[C];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const bool tie = u[i] == t && need > 0;
-        const uint64_t tb = __ballot(tie);
-        const bool sel = u[i] > t || (tie && ties + __popcll(tb & below) < need);
-        ties += __popcll(tb);
-        const uint64_t sb = __ballot(sel);
-        if (sel) {
+    for (int c = 0; c < C; ++c) {
+        big[c] = count(c, [&](int cc, int i) { return u[cc][i] >= 1u; }) > k;
+        t[c] = 0;
+        tt[c] = 0;
+    }
+    for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint32_t cand = t[c] | (1u << bit);
+            if (count(c, [&](int cc, int i) { return u[cc][i] >= cand; }) >= k) t[c] = cand;
+        }
+    }
+    bool any_tie = false;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (!big[c]) t[c] = 0;   // at most k: every real entry
+        // t >= 1 for a big set, and t + 1 does not wrap (t is at most the image of +inf)
+        need[c] = big[c] ? k - count(c, [&](int cc, int i) { return u[cc][i] > t[cc]; }) : 0;
+        big[c] = big[c] && count(c, [&](int cc, int i) { return u[cc][i] == t[cc]; }) > need[c];
+        any_tie = any_tie || big[c];
+    }
+    if (any_tie) {   // more equal values at t than places: the largest tb among them
+        for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const uint32_t cand = tt[c] | (1u << bit);
+                if (big[c] && count(c, [&](int cc, int i) {
+                        return u[cc][i] == t[cc] && tb[cc][i] >= cand;
+                    }) >= need[c])
+                    tt[c] = cand;
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+            sel[c][i] = u[c][i] > t[c] || (t[c] > 0 && u[c][i] == t[c] && tb[c][i] >= tt[c]);
+}
+
+// Writes the (row, x) of the marked entries of set c to staging (ballot-
+// prefix order); returns their number.  rowx(c, i, row, x) gives an entry.
+template <int C, int M, typename RowX>
+__device__ __forceinline__ int stage_selected(const bool (&sel)[C][M], int c, RowX rowx, float* sx,
+                                              int* sid) {
+    const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
+    int nsel = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const uint64_t sb = __ballot(sel[c][i]);
+        if (sel[c][i]) {
             const int pos = nsel + __popcll(sb & below);
-            const int r = lane + 64 * i;
-            sx[pos] = xcol[r];
-            sid[pos] = gid0 + r;
+            int row;
+            float x;
+            rowx(c, i, row, x);
+            sx[pos] = x;
+            sid[pos] = row;
         }
         nsel += __popcll(sb);
+    }
+    return nsel;
+}
+
+// One wave, C columns at once: the top-k candidates of rows [0, nr) of C
+// columns (c < nc are real) whose x sit in LDS at xc[c][row] (row r is
+// global id gid0 + r; each xc[c] is 16-byte aligned, holds NR * 64 >= 768
+// entries and is overwritten).  Writes a.topk candidates (x, id) of column c
+// at offset o[c] of a.cx / a.cidx, unused slots as (-inf, -1).  The noise is
+// drawn later, for the row's final k only.
+//
+// A lower bound cuts the work: the k-th largest of the lanes' two largest
+// values is at most the column's k-th largest value (k of the column's
+// values are at least that large).  Usually little more than k values reach
+// it; those are compacted to one per lane and the exact selection runs on
+// them, all C columns interleaved (other paths take up to four per lane, or
+// all entries, one column at a time).
+template <int C, int NR>
+__device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
+                                                   float* const (&xc)[C], int nr, int gid0,
+                                                   const size_t (&o)[C]) {
+    static_assert(NR % 4 == 0 && NR * 64 >= 768, "row store of at least 768 entries");
+    constexpr int kDummy = 704;   // write target of lanes that keep nothing
+    const int lane = threadIdx.x & 63;
+    const int k = a.topk;
+    // entry i = 4 * q + j of this lane is row 256 * q + 4 * lane + j
+    auto row_of = [&](int i) { return 256 * (i >> 2) + 4 * lane + (i & 3); };
+    uint32_t u[C][NR];
+    uint32_t top[C][2];   // the lane's two largest values
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        top[c][0] = top[c][1] = 0;
+#pragma unroll
+        for (int q = 0; q < NR / 4; ++q) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(xc[c] + 256 * q + 4 * lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 4 * q + j;
+                const uint32_t v = (c < nc && row_of(i) < nr) ? topk_order(v4[j]) : 0u;
+                u[c][i] = v;
+                const uint32_t lo2 = v < top[c][0] ? v : top[c][0];
+                top[c][0] = v > top[c][0] ? v : top[c][0];
+                top[c][1] = lo2 > top[c][1] ? lo2 : top[c][1];
+            }
+        }
+    }
+    // bound: the k-th largest of the 2 * 64 lane tops (0 when there are fewer)
+    uint32_t lo[C];
+    wave_kth<C, 2, 16>(top, k, lo);   // to 16 bits: a bound, slightly below the exact one
+    int nmax = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        lo[c] = lo[c] > 1u ? lo[c] : 1u;
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) n += u[c][i] >= lo[c] ? 1 : 0;
+        n = wave_sum<NR>(n);
+        nmax = n > nmax ? n : nmax;
+    }
+
+    // staging of the selected: x at xc[c][512, 576), rows at xc[c][576, 640)
+    int nsel[C];
+    if (nmax <= 256) {
+        // compact the values >= lo: x to xc[c][0, 256), rows to xc[c][256, 512)
+        // (every lane has read its entries above)
+        int cnt[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            int* crow = reinterpret_cast<int*>(xc[c]);
+            int base = 0;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const bool keep = u[c][i] >= lo[c];
+                const uint64_t kb = __ballot(keep);
+                const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                           (uint32_t)(kb >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0u));
+                xc[c][keep ? pos : kDummy] = ordered_to_float(u[c][i]);
+                crow[keep ? 256 + pos : kDummy + 1] = row_of(i);
+                base += __popcll(kb);
+            }
+            cnt[c] = base;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if (nmax <= 64) {
+            // the usual case: one survivor per lane, the C columns interleaved
+            uint32_t v[C][1], tb[C][1];
+            float vx[C][1];
+            int vr[C][1];
+            bool sel[C][1];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                vx[c][0] = xc[c][lane];
+                vr[c][0] = reinterpret_cast<const int*>(xc[c])[256 + lane];
+                v[c][0] = lane < cnt[c] ? topk_order(vx[c][0]) : 0u;
+                tb[c][0] = ~(uint32_t)vr[c][0];
+            }
+            wave_select<C, 1>(v, tb, k, sel);
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                nsel[c] = stage_selected<C, 1>(
+                    sel, c, [&](int cc, int, int& row, float& x) { row = vr[cc][0]; x = vx[cc][0]; },
+                    xc[c] + 512, reinterpret_cast<int*>(xc[c] + 576));
+        } else {
+            // one column at a time, up to two or four survivors per lane
+            auto run1 = [&](int c, auto m_tag) {
+                constexpr int M = decltype(m_tag)::value;
+                uint32_t v[1][M], tb[1][M];
+                float vx[M];
+                int vr[M];
+                bool sel[1][M];
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    const int q = lane + 64 * j;
+                    vx[j] = xc[c][q];
+                    vr[j] = reinterpret_cast<const int*>(xc[c])[256 + q];
+                    v[0][j] = q < cnt[c] ? topk_order(vx[j]) : 0u;
+                    tb[0][j] = ~(uint32_t)vr[j];
+                }
+                wave_select<1, M>(v, tb, k, sel);
+                return stage_selected<1, M>(
+                    sel, 0, [&](int, int j, int& row, float& x) { row = vr[j]; x = vx[j]; },
+                    xc[c] + 512, reinterpret_cast<int*>(xc[c] + 576));
+            };
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                nsel[c] = cnt[c] <= 128 ? run1(c, std::integral_constant<int, 2>{})
+                                        : run1(c, std::integral_constant<int, 4>{});
+        }
+    } else {
+        // more than 256 values reach the bound (many equal values): the
+        // exact selection on every entry, one column at a time
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            uint32_t uc[1][NR], tb[1][NR];
+            bool sel[1][NR];
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                uc[0][i] = u[c][i];
+                tb[0][i] = ~(uint32_t)row_of(i);
+            }
+            wave_select<1, NR>(uc, tb, k, sel);
+            // the staging area overlaps rows 512..639: every lane has read them
+            nsel[c] = stage_selected<1, NR>(
+                sel, 0, [&](int, int i, int& row, float& x) {
+                    row = row_of(i);
+                    x = ordered_to_float(uc[0][i]);
+                },
+                xc[c] + 512, reinterpret_cast<int*>(xc[c] + 576));
+        }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-    // noise for the selected only, one candidate per lane
+    // the selected, one candidate per lane
     if (lane < k) {
-        float x = -INFINITY, s = -INFINITY;
-        int id = -1;
-        if (lane < nsel) {
-            x = sx[lane];
-            id = sid[lane];
-            s = c.greedy ? x : x + token_gumbel(a, c.col, id);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (c >= nc) break;
+            const bool live = lane < nsel[c];
+            a.cx[o[c] + lane] = live ? xc[c][512 + lane] : -INFINITY;
+            a.cidx[o[c] + lane] =
+                live ? gid0 + reinterpret_cast<const int*>(xc[c] + 576)[lane] : -1;
         }
-        a.cx[o + lane] = x;
-        a.cs[o + lane] = s;
-        a.cidx[o + lane] = id;
     }
-    __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace fs

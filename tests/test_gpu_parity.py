@@ -294,6 +294,34 @@ def test_topk_exact_ties_take_lowest_ids(B, d):
             assert np.array_equal(oi[pin], want[pin])
 
 
+@pytest.mark.parametrize("V,k", [(200000, 64), (40000, 40), (1024, 8)])
+def test_topk_all_logits_equal(V, k):
+    """Every W row is the same row, so all V logits of a batch row are equal
+    and the top-k set is ids 0 .. k-1.  The sizes drive the selection into its
+    less common branches: whole workgroup ranges of ties (768 and 160 rows
+    per workgroup) and stage-2 candidate sets that the lower bound cannot
+    prune."""
+    B, d = 3, 512
+    Hb = hidden_bf16(B, d, seed=21)
+    row = weights_bf16(1, d, std=0.05, seed=22)
+    Wb = np.ascontiguousarray(np.broadcast_to(row, (V, d)))
+    temp = np.array([1.0, 0.6, 0.0], np.float32)   # the last row greedy
+    x_in = Inputs(Hb, Wb, temp)
+    l = O.logits_bf16(Hb, row)
+    p = x_in.params(seed=SEED, step=2)
+    log(f"all-equal logits V={V} k={k}")
+    got = run_topk(x_in, p, k)
+    assert np.all((got >= 0) & (got < k)), got
+    x = O.tempered(np.repeat(l, k, axis=1), temp)
+    sc = O.scores(x, temp, SEED, 2, 0, 0)
+    want = np.argmax(sc, axis=1)
+    top2 = np.sort(sc, axis=1)
+    pin = (top2[:, -1] - top2[:, -2]) > TOL_GAP
+    pin[2] = True   # greedy row: equal scores, the lowest id
+    assert want[2] == 0
+    assert np.array_equal(got[pin], want[pin])
+
+
 def test_repeated_calls_bit_identical():
     Hb, Wb, temp, allow = make_case(33, 256, 5000, "mixed", True)
     x = Inputs(Hb, Wb, temp, allow)
