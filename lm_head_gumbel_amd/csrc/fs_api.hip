@@ -126,13 +126,13 @@ Stage1Config pick_config(bool stream, int B) {
 ResidentConfig pick_resident(int B, int nks, int variant) {
     static const char* env = std::getenv("FS_RES_CFG");
     if (env) {
-        ResidentConfig c{0, 0, 0, 0, 0};
-        if (std::sscanf(env, "%d,%d,%d,%d", &c.nb, &c.mpi, &c.ks, &c.nw) == 4 && c.nw > 0 &&
-            nks % c.nw == 0) {
-            c.hk = nks / c.nw;
+        ResidentConfig c{0, 0, 0, 0, 0, 0};
+        const int n = std::sscanf(env, "%d,%d,%d,%d,%d", &c.nb, &c.mpi, &c.ks, &c.nw, &c.hl);
+        if ((n == 4 || n == 5) && c.nw > 0 && nks % c.nw == 0 && nks / c.nw > c.hl) {
+            c.hk = nks / c.nw - c.hl;
             return c;
         }
-        return ResidentConfig{0, 0, 0, 0, 0};
+        return ResidentConfig{0, 0, 0, 0, 0, 0};
     }
     ResidentConfig c = resident_default(B <= 16 ? 1 : 2, nks, variant);
     if (c.nw == 0 && B > 16) c = resident_default(1, nks, variant);

@@ -80,10 +80,11 @@ struct Stage1Config {
 hipError_t launch_stage1(int variant, const Stage1Args& a, int grid_y, const Stage1Config& cfg,
                          hipStream_t stream);
 
-// Resident-H stage 1: nw waves split the hidden dimension, hk k-steps each
-// (nks == nw * hk), mpi blocks per group, ks k-steps per pipeline stage.
+// Resident-H stage 1: nw waves split the hidden dimension, hk + hl k-steps
+// each (nks == nw * (hk + hl); hk of them held in registers, hl in LDS), mpi
+// blocks per group, ks k-steps per pipeline stage.
 struct ResidentConfig {
-    int nb, mpi, ks, nw, hk;
+    int nb, mpi, ks, nw, hk, hl;
 };
 bool resident_supported(const ResidentConfig& c, int variant);
 // Preferred instantiated shape for nb batch blocks, nks k-steps and a

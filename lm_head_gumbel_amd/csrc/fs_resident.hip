@@ -46,17 +46,41 @@ __device__ __forceinline__ void load_w(WStage<MPI, KS>& s, const uint16_t* (&wro
     }
 }
 
+// MFMAs of stage `it` with the H fragments in registers (k-steps it * KS ..
+// + KS - 1 < HK; the index is clamped so that the call compiles for every
+// unrolled stage).
 template <int NB, int MPI, int KS, int HK>
 __device__ __forceinline__ void mfma_w(f32x4 (&acc)[MPI][NB], const WStage<MPI, KS>& s,
                                        const bf16x8 (&h)[NB][HK], int it) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+    for (int kk = 0; kk < KS; ++kk) {
+        const int ks = it * KS + kk < HK ? it * KS + kk : HK - 1;
 #pragma unroll
         for (int j = 0; j < MPI; ++j)
 #pragma unroll
             for (int n = 0; n < NB; ++n)
-                acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.w[j][kk], h[n][it * KS + kk],
-                                                                    acc[j][n], 0, 0, 0);
+                acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.w[j][kk], h[n][ks], acc[j][n],
+                                                                    0, 0, 0);
+    }
+}
+
+// MFMAs of stage `it` with the H fragments in LDS: k-step it * KS + kk - HK of
+// hl ([HL][NB] fragments, 64 lanes each, this lane's entry).
+template <int NB, int MPI, int KS, int HK>
+__device__ __forceinline__ void mfma_w_lds(f32x4 (&acc)[MPI][NB], const WStage<MPI, KS>& s,
+                                           const bf16x8* hl, int it) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        bf16x8 hb[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) hb[n] = hl[((it * KS + kk - HK) * NB + n) * 64];
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.w[j][kk], hb[n], acc[j][n],
+                                                                    0, 0, 0);
+    }
 }
 
 template <int NB, int MPI, int NW>
@@ -75,17 +99,32 @@ struct TopkRowsSmem {
 };
 struct NoTopkRows {};
 
-template <int NB, int MPI, int NW>
+// The last HL k-steps of each wave's H slice, when the registers cannot hold
+// the whole slice: per wave [HL][NB] fragments of 64 lanes (each lane reads
+// back only what it wrote).
+template <int NB, int NW, int HL>
+struct HlSmem {
+    bf16x8 h[NW][HL][NB][64];
+};
+struct NoHl {};
+
+template <int NB, int MPI, int NW, int HL>
 constexpr bool topk_fits() {
-    return sizeof(ResidentSmem<NB, MPI, NW>) + sizeof(TopkRowsSmem<NB, NW>) <= 160 * 1024;
+    return sizeof(ResidentSmem<NB, MPI, NW>) + sizeof(TopkRowsSmem<NB, NW>) +
+               (HL > 0 ? sizeof(HlSmem<NB, NW, (HL > 0 ? HL : 1)>) : 0) <=
+           160 * 1024;
 }
 
-template <int NB, int MPI, int KS, int NW, int HK, int VAR>
+template <int NB, int MPI, int KS, int NW, int HK, int HL, int VAR>
 __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     static_assert(NW % NB == 0, "NB must divide the wave count");
-    static_assert(HK % (2 * KS) == 0, "stages are processed in pairs");
-    constexpr int NIT = HK / KS;
+    static_assert(HK % KS == 0 && HL % KS == 0 && (HK + HL) % (2 * KS) == 0,
+                  "stages are processed in pairs");
+    constexpr int HT = HK + HL;   // k-steps per wave
+    constexpr int NIT = HT / KS;
     __shared__ ResidentSmem<NB, MPI, NW> sm;
+    using HlPart = typename std::conditional<(HL > 0), HlSmem<NB, NW, (HL > 0 ? HL : 1)>, NoHl>::type;
+    __shared__ HlPart hls;
     using TkSmem = typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW>, NoTopkRows>::type;
     __shared__ TkSmem tk;
 
@@ -110,11 +149,14 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     const int mb0 = part_begin(w, a.nmb, a.G);
     const int mb1 = part_begin(w + 1, a.nmb, a.G);
     const int bbase = y * 16 * NB;
-    const int ks0 = wave * HK;
+    const int ks0 = wave * HT;
 
     // this wave's slice of H, resident for the whole kernel (rows past B reuse
-    // row B - 1, their columns are discarded; k past d reads zeros)
+    // row B - 1, their columns are discarded; k past d reads zeros): the first
+    // HK k-steps in registers, the last HL in LDS
     bf16x8 hres[NB][HK];
+    const bf16x8* hl = nullptr;
+    if constexpr (HL > 0) hl = &hls.h[wave][0][0][lane];
     {
         const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero16);
 #pragma unroll
@@ -125,6 +167,13 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             for (int s = 0; s < HK; ++s) {
                 const int k = (ks0 + s) * 32 + kg * 8;
                 hres[n][s] = load_bf16x8(k < a.d ? hrow + k : zero);
+            }
+            if constexpr (HL > 0) {
+#pragma unroll
+                for (int s = 0; s < HL; ++s) {
+                    const int k = (ks0 + HK + s) * 32 + kg * 8;
+                    hls.h[wave][s][n][lane] = load_bf16x8(k < a.d ? hrow + k : zero);
+                }
             }
         }
     }
@@ -160,14 +209,20 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         for (int it = 0; it < NIT; it += 2) {
             load_w<MPI, KS>(sb, wrow, it + 1, ks0, kg, a.d);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_w<NB, MPI, KS, HK>(acc, sa, hres, it);
+            if (HL == 0 || it * KS < HK)
+                mfma_w<NB, MPI, KS, HK>(acc, sa, hres, it);
+            else
+                mfma_w_lds<NB, MPI, KS, HK>(acc, sa, hl, it);
             __builtin_amdgcn_sched_barrier(0);
             if (it + 2 < NIT)
                 load_w<MPI, KS>(sa, wrow, it + 2, ks0, kg, a.d);
             else
                 load_w<MPI, KS>(sa, wnext, 0, ks0, kg, a.d);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_w<NB, MPI, KS, HK>(acc, sb, hres, it + 1);
+            if (HL == 0 || (it + 1) * KS < HK)
+                mfma_w<NB, MPI, KS, HK>(acc, sb, hres, it + 1);
+            else
+                mfma_w_lds<NB, MPI, KS, HK>(acc, sb, hl, it + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -266,50 +321,56 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     }
 }
 
-template <int NB, int MPI, int KS, int NW, int HK, int VAR>
+template <int NB, int MPI, int KS, int NW, int HK, int HL, int VAR>
 static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream) {
-    if constexpr (VAR == kVarTopk && !topk_fits<NB, MPI, NW>()) {
+    if constexpr (VAR == kVarTopk && !topk_fits<NB, MPI, NW, HL>()) {
         return hipErrorInvalidValue;   // the row store does not fit next to this shape's LDS
     } else {
         const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
-        hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, VAR>), grid, dim3(64 * NW), 0,
+        hipLaunchKernelGGL((resident_kernel<NB, MPI, KS, NW, HK, HL, VAR>), grid, dim3(64 * NW), 0,
                            stream, a);
         return hipGetLastError();
     }
 }
 
-// Instantiated shapes (nb, mpi, ks, nw, hk), in order of preference for a
-// given (nb, hk).  Each fits 256 registers per lane without spilling.
+// Instantiated shapes (nb, mpi, ks, nw, hk, hl), in order of preference for
+// a given nb and k-step count nw * (hk + hl).  Each fits 256 registers per
+// lane without spilling; hl > 0 keeps the last hl k-steps of each wave's H
+// slice in LDS (d = 5120 with two batch blocks).
 #define FS_RESIDENT_SHAPES(X) \
-    X(1, 2, 4, 8, 16)         \
-    X(1, 4, 2, 8, 16)         \
-    X(1, 2, 4, 4, 32)         \
-    X(1, 2, 4, 8, 8)          \
-    X(1, 2, 2, 8, 20)         \
-    X(1, 2, 2, 8, 4)          \
-    X(1, 2, 1, 8, 2)          \
-    X(2, 1, 4, 8, 16)         \
-    X(2, 1, 2, 8, 16)         \
-    X(2, 2, 2, 8, 16)         \
-    X(2, 2, 4, 8, 8)          \
-    X(2, 2, 2, 8, 4)          \
-    X(2, 2, 1, 8, 2)
+    X(1, 2, 4, 8, 16, 0)      \
+    X(1, 4, 2, 8, 16, 0)      \
+    X(1, 2, 4, 4, 32, 0)      \
+    X(1, 2, 4, 8, 8, 0)       \
+    X(1, 2, 2, 8, 20, 0)      \
+    X(1, 2, 2, 8, 4, 0)       \
+    X(1, 2, 1, 8, 2, 0)       \
+    X(2, 1, 4, 8, 16, 0)      \
+    X(2, 1, 2, 8, 16, 0)      \
+    X(2, 2, 2, 8, 16, 0)      \
+    X(2, 1, 2, 8, 16, 4)      \
+    X(2, 2, 4, 8, 8, 0)       \
+    X(2, 2, 2, 8, 4, 0)       \
+    X(2, 2, 1, 8, 2, 0)
+
+#define FS_RES_MATCH(NB_, MPI_, KS_, NW_, HK_, HL_) \
+    (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_ && c.hl == HL_)
 
 template <int VAR>
 static hipError_t launch_res_var(const Stage1Args& a, int grid_y, const ResidentConfig& c,
                                  hipStream_t stream) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_)                                          \
-    if (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_) \
-        return launch_res<NB_, MPI_, KS_, NW_, HK_, VAR>(a, grid_y, stream);
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)          \
+    if (FS_RES_MATCH(NB_, MPI_, KS_, NW_, HK_, HL_)) \
+        return launch_res<NB_, MPI_, KS_, NW_, HK_, HL_, VAR>(a, grid_y, stream);
     FS_RESIDENT_SHAPES(FS_RES)
 #undef FS_RES
     return hipErrorInvalidValue;
 }
 
 bool resident_supported(const ResidentConfig& c, int variant) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_)                                          \
-    if (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_) \
-        return variant != kVarTopk || topk_fits<NB_, MPI_, NW_>();
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)          \
+    if (FS_RES_MATCH(NB_, MPI_, KS_, NW_, HK_, HL_)) \
+        return variant != kVarTopk || topk_fits<NB_, MPI_, NW_, HL_>();
     FS_RESIDENT_SHAPES(FS_RES)
 #undef FS_RES
     return false;
@@ -318,12 +379,13 @@ bool resident_supported(const ResidentConfig& c, int variant) {
 int resident_topk_rows(int nb) { return nb == 1 ? TopkRows<1>::kRows : TopkRows<2>::kRows; }
 
 ResidentConfig resident_default(int nb, int nks, int variant) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_)                                          \
-    if (nb == NB_ && nks == NW_ * HK_ && (variant != kVarTopk || topk_fits<NB_, MPI_, NW_>())) \
-        return ResidentConfig{NB_, MPI_, KS_, NW_, HK_};
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)                                          \
+    if (nb == NB_ && nks == NW_ * (HK_ + HL_) &&                                     \
+        (variant != kVarTopk || topk_fits<NB_, MPI_, NW_, HL_>()))                   \
+        return ResidentConfig{NB_, MPI_, KS_, NW_, HK_, HL_};
     FS_RESIDENT_SHAPES(FS_RES)
 #undef FS_RES
-    return ResidentConfig{0, 0, 0, 0, 0};
+    return ResidentConfig{0, 0, 0, 0, 0, 0};
 }
 
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,

@@ -154,6 +154,8 @@ CASES = [
     (25, 1024, 2600, 64, 0, 32, "range", False),
     (20, 512, 1500, 256, 5, 0, "mixed", False),
     (2, 2048, 1111, 32, 1, 16, "range", True),
+    # d = 5120 with two batch blocks: part of each wave's H slice lives in LDS
+    (24, 5120, 2000, 128, 3, 16, "mixed", True),
     # fewer than four vocab blocks: the workgroup-cooperative kernel
     (5, 64, 40, 16, 3, 0, "one", False),
     # B > 32 with d % 64 == 0: the LDS-tiled kernel (one and two column groups)
