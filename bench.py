@@ -147,6 +147,134 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
     return res
 
 
+def _gpu_weights(torch, v, d, std=0.02, seed=0):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return (torch.randn((v, d), generator=g, device="cuda", dtype=torch.float32) * std
+            ).to(torch.bfloat16)
+
+
+def _gpu_hidden(torch, B, d, seed=1):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn((B, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def bench_workloads(torch, fs, steps, W_head):
+    """The other configured workloads at their own shapes (secondary lines):
+    small-model flat, mid-size masked grouped, compute-leaning flat with
+    per-row temperatures, top-k and online merge at d=5120, and the stage-1
+    kernel on one vocabulary shard (V/G rows, v_offset = the shard start) as
+    a rank of a G-way vocabulary split would run it."""
+    from lm_head_gumbel_amd.inputs import WORKLOADS
+    timer = Timer(torch)
+    out = []
+    n = max(10, steps // 4)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        return timer.run(fn, n)[0]
+
+    def line(name, wl, what, t, extra=None):
+        r = {"workload": name, "B": wl.B, "d": wl.d, "V": wl.V, "what": what,
+             "calls_per_s": 1.0 / t, "us_per_call": t * 1e6,
+             "hbm_GBps": alg_bytes(wl.B, wl.d, wl.V) / t / 1e9,
+             "mfma_frac": 2.0 * wl.B * wl.d * wl.V / t / PEAK_BF16}
+        if extra:
+            r.update(extra)
+        log(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}))
+        out.append(r)
+
+    cache = {}
+
+    def weights(v, d):
+        if (v, d) not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[(v, d)] = _gpu_weights(torch, v, d)
+        return cache[(v, d)]
+
+    for name in ("small_b32", "mid_b64", "large_b128", "large_b256", "topk_b32"):
+        wl = WORKLOADS[name]
+        W = weights(wl.V, wl.d)
+        H = _gpu_hidden(torch, wl.B, wl.d)
+        temp = torch.from_numpy(wl.temps()).cuda()
+        p = fs.params(wl.B, wl.d, wl.V, n_valid=wl.n_valid, tile_v=wl.tile_v, seed=SEED)
+        idx = torch.empty(wl.B, dtype=torch.int32, device="cuda")
+        ws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_FLAT), dtype=torch.uint8,
+                         device="cuda")
+
+        def flat(i):
+            p.step = i
+            fs.check(fs.fs_sample(p, H, W, temp, None, idx, None, ws), name)
+
+        line(name, wl, "flat fs_sample", timed(flat))
+        if name == "mid_b64":
+            T = fs.fs_num_tiles(p)
+            tm = torch.empty((wl.B, T), dtype=torch.float32, device="cuda")
+            ti = torch.empty((wl.B, T), dtype=torch.int32, device="cuda")
+            tl = torch.empty((wl.B, T), dtype=torch.float32, device="cuda")
+            gws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_GROUPED), dtype=torch.uint8,
+                              device="cuda")
+
+            def grouped(i):
+                p.step = i
+                fs.check(fs.fs_sample_grouped(p, H, W, temp, None, tm, ti, tl, idx, gws), name)
+
+            line(name, wl, "grouped fs_sample_grouped (masked tail, hierarchical resample)",
+                 timed(grouped))
+        if name == "topk_b32":
+            kws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, wl.k),
+                              dtype=torch.uint8, device="cuda")
+
+            def topk(i):
+                p.step = i
+                fs.check(fs.fs_sample_topk(p, H, W, temp, None, wl.k, idx, kws), name)
+
+            line(name, wl, f"top-{wl.k} fs_sample_topk", timed(topk))
+            chunk = wl.V // wl.chunks
+            pc = fs.params(wl.B, wl.d, wl.V, tile_v=chunk, seed=SEED)
+            C = fs.fs_num_tiles(pc)
+            tm = torch.empty((wl.B, C), dtype=torch.float32, device="cuda")
+            ti = torch.empty((wl.B, C), dtype=torch.int32, device="cuda")
+            tl = torch.empty((wl.B, C), dtype=torch.float32, device="cuda")
+            oL = torch.empty(wl.B, dtype=torch.float32, device="cuda")
+            gws = torch.empty(fs.fs_workspace_bytes(pc, fs.FS_VARIANT_GROUPED), dtype=torch.uint8,
+                              device="cuda")
+
+            def online(i):
+                pc.step = i
+                fs.check(fs.fs_sample_grouped(pc, H, W, temp, None, tm, ti, tl, None, gws), name)
+                fs.check(fs.fs_merge_online(wl.B, C, ti, tl, temp, SEED, i, 0, idx, oL), name)
+
+            line(name, wl, f"online merge over {C} chunks of {chunk} ids "
+                 "(fs_sample_grouped + fs_merge_online)", timed(online))
+        del H, temp, ws
+
+    # one rank's shard of a G-way vocabulary split (the stage-1 kernel alone)
+    cache.clear()
+    W = W_head
+    H = _gpu_hidden(torch, 32, D)
+    for G in (2, 4, 8):
+        vs = V // G
+        start = (G - 1) * vs     # the last shard: its ids are offset by the shard start
+        p = fs.params(32, D, vs, v_offset=start, n_valid=start + vs, seed=SEED)
+        ws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_FLAT), dtype=torch.uint8,
+                         device="cuda")
+        Ws = W[start:start + vs]
+
+        def shard(i):
+            p.step = i
+            fs.check(fs.fs_sample_stage1(p, H, Ws, None, None, ws), "shard")
+
+        t = timed(shard)
+        wl = type("S", (), {"B": 32, "d": D, "V": vs})()
+        line(f"shard_{G}", wl, f"stage 1 on one of {G} vocabulary shards ({vs} rows)", t)
+    cache.clear()
+    return out
+
+
 def cpu_baseline(torch, H_all, W, B, seconds):
     """The CPU oracle (numpy float64: logits, Philox-Gumbel noise, argmax) on
     the headline batch.  Whole calls are repeated (steps 0, 1, ...) until about
@@ -259,6 +387,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other configured workloads and the shard shapes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -290,6 +420,11 @@ def main():
         r = bench_batch(torch, fs, H_all, W, B, max(20, args.steps // 2), max(5, args.warmup // 2))
         log(json.dumps(r))
         rows.append(r)
+
+    workloads = None
+    if not args.no_workloads:
+        log("other workloads and shard shapes")
+        workloads = bench_workloads(torch, fs, args.steps, W)
 
     probe = None
     if not args.no_probe:
@@ -335,6 +470,8 @@ def main():
                      if k in head},
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in rows],
+        "workloads": ([{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                       for r in workloads] if workloads is not None else None),
     }
     print(json.dumps(out), flush=True)
 

@@ -226,7 +226,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     // that no range exceeds that store
     int min_g = 1;
     if (variant == kVarTopk && pl.kind == kResident) {
-        const int cap_mb = resident_topk_rows(pl.rcfg.nb) / kMBlock;
+        const int cap_mb = resident_topk_rows(pl.rcfg) / kMBlock;
         min_g = (pl.nmb + cap_mb - 1) / cap_mb;
         if (pl.G < min_g) {
             pl.G = min_g;

@@ -90,14 +90,16 @@ bool resident_supported(const ResidentConfig& c, int variant);
 // Preferred instantiated shape for nb batch blocks, nks k-steps and a
 // variant (nw == 0: none).
 ResidentConfig resident_default(int nb, int nks, int variant);
-// Top-k: the most vocabulary rows one resident workgroup may own.
-int resident_topk_rows(int nb);
+// Top-k: the most vocabulary rows one resident workgroup of shape c may own.
+int resident_topk_rows(const ResidentConfig& c);
 
-// LDS budget of the top-k row store: 96 KiB of x per workgroup.
-template <int NB>
+// Top-k row store of one resident workgroup: the most vocabulary rows it
+// may own (x of all its columns in LDS): 96 KiB of x, or 640 rows when part
+// of the H slice also lives in LDS (hl > 0).
+template <int NB, int HL>
 struct TopkRows {
-    static constexpr int kRows = 96 * 1024 / (16 * NB * 4);   // multiple of 64
-    static constexpr int kStride = kRows + 4;                  // padded row of one column
+    static constexpr int kRows = HL > 0 ? 640 : 96 * 1024 / (16 * NB * 4);   // multiple of 128
+    static constexpr int kStride = kRows + 4;   // padded row of one column
 };
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
                            hipStream_t stream);

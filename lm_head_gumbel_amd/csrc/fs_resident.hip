@@ -9,7 +9,7 @@
 // follows ("FlashSampling: Fast and Memory-Efficient Exact Sampling",
 // Abstract; FlashSampling explainer on aitrends.kr, Stage 1 and
 // tensor-parallel paragraphs).  The top-k variant keeps the tempered logits
-// of its whole row range in LDS (the range is at most TopkRows<NB>::kRows
+// of its whole row range in LDS (the range is at most TopkRows<NB, HL>::kRows
 // rows, the host sizes the grid for it) and selects each column's k best at
 // the end (implementation paragraph of the explainer).
 //
@@ -93,9 +93,9 @@ struct ResidentSmem {
 
 // Top-k: x of the workgroup's rows, one padded row of LDS per column (also
 // the scratch area of the column's selection).
-template <int NB, int NW>
+template <int NB, int NW, int HL>
 struct TopkRowsSmem {
-    alignas(16) float x[16 * NB][TopkRows<NB>::kStride];
+    alignas(16) float x[16 * NB][TopkRows<NB, HL>::kStride];
 };
 struct NoTopkRows {};
 
@@ -110,7 +110,7 @@ struct NoHl {};
 
 template <int NB, int MPI, int NW, int HL>
 constexpr bool topk_fits() {
-    return sizeof(ResidentSmem<NB, MPI, NW>) + sizeof(TopkRowsSmem<NB, NW>) +
+    return sizeof(ResidentSmem<NB, MPI, NW>) + sizeof(TopkRowsSmem<NB, NW, HL>) +
                (HL > 0 ? sizeof(HlSmem<NB, NW, (HL > 0 ? HL : 1)>) : 0) <=
            160 * 1024;
 }
@@ -125,7 +125,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     __shared__ ResidentSmem<NB, MPI, NW> sm;
     using HlPart = typename std::conditional<(HL > 0), HlSmem<NB, NW, (HL > 0 ? HL : 1)>, NoHl>::type;
     __shared__ HlPart hls;
-    using TkSmem = typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW>, NoTopkRows>::type;
+    using TkSmem =
+        typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW, HL>, NoTopkRows>::type;
     __shared__ TkSmem tk;
 
     // Row range w and batch group y of this workgroup.  With xcd_pair the grid
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             o[q] = ((size_t)w * a.B + bbase + (ok ? cl : 0)) * a.topk;
         }
         if (nc > 0)
-            topk_select_columns<C, TopkRows<NB>::kRows / 64>(a, nc, xc, (mb1 - mb0) * kMBlock,
+            topk_select_columns<C, TopkRows<NB, HL>::kRows / 64>(a, nc, xc, (mb1 - mb0) * kMBlock,
                                                              a.v_offset + mb0 * kMBlock, o);
     }
 }
@@ -336,7 +337,8 @@ static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream
 // Instantiated shapes (nb, mpi, ks, nw, hk, hl), in order of preference for
 // a given nb and k-step count nw * (hk + hl).  Each fits 256 registers per
 // lane without spilling; hl > 0 keeps the last hl k-steps of each wave's H
-// slice in LDS (d = 5120 with two batch blocks).
+// slice in LDS (d = 5120 with two batch blocks; the 18 + 2 split leaves
+// room in LDS for the top-k row store).
 #define FS_RESIDENT_SHAPES(X) \
     X(1, 2, 4, 8, 16, 0)      \
     X(1, 4, 2, 8, 16, 0)      \
@@ -349,6 +351,7 @@ static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream
     X(2, 1, 2, 8, 16, 0)      \
     X(2, 2, 2, 8, 16, 0)      \
     X(2, 1, 2, 8, 16, 4)      \
+    X(2, 1, 2, 8, 18, 2)      \
     X(2, 2, 4, 8, 8, 0)       \
     X(2, 2, 2, 8, 4, 0)       \
     X(2, 2, 1, 8, 2, 0)
@@ -376,7 +379,10 @@ bool resident_supported(const ResidentConfig& c, int variant) {
     return false;
 }
 
-int resident_topk_rows(int nb) { return nb == 1 ? TopkRows<1>::kRows : TopkRows<2>::kRows; }
+int resident_topk_rows(const ResidentConfig& c) {
+    if (c.nb == 1) return c.hl > 0 ? TopkRows<1, 1>::kRows : TopkRows<1, 0>::kRows;
+    return c.hl > 0 ? TopkRows<2, 1>::kRows : TopkRows<2, 0>::kRows;
+}
 
 ResidentConfig resident_default(int nb, int nks, int variant) {
 #define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)                                          \

@@ -158,8 +158,8 @@ __device__ __forceinline__ int stage_selected(const bool (&sel)[C][M], int c, Ro
 
 // One wave, C columns at once: the top-k candidates of rows [0, nr) of C
 // columns (c < nc are real) whose x sit in LDS at xc[c][row] (row r is
-// global id gid0 + r; each xc[c] is 16-byte aligned, holds NR * 64 >= 768
-// entries and is overwritten).  Writes a.topk candidates (x, id) of column c
+// global id gid0 + r; each xc[c] is 16-byte aligned, holds NR * 64 >= 640
+// entries plus at least two of padding, and is overwritten).  Writes a.topk candidates (x, id) of column c
 // at offset o[c] of a.cx / a.cidx, unused slots as (-inf, -1).  The noise is
 // drawn later, for the row's final k only.
 //
@@ -173,24 +173,36 @@ template <int C, int NR>
 __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
                                                    float* const (&xc)[C], int nr, int gid0,
                                                    const size_t (&o)[C]) {
-    static_assert(NR % 4 == 0 && NR * 64 >= 768, "row store of at least 768 entries");
-    constexpr int kDummy = 704;   // write target of lanes that keep nothing
+    static_assert(NR % 2 == 0 && NR * 64 >= 640, "row store of at least 640 entries");
+    constexpr int kDummy = 640;   // write target of lanes that keep nothing (padding)
+    constexpr int PK = NR % 4 == 0 ? 4 : 2;   // entries per LDS read
     const int lane = threadIdx.x & 63;
     const int k = a.topk;
-    // entry i = 4 * q + j of this lane is row 256 * q + 4 * lane + j
-    auto row_of = [&](int i) { return 256 * (i >> 2) + 4 * lane + (i & 3); };
+    // entry i = PK * q + j of this lane is row 64 PK q + PK lane + j
+    auto row_of = [&](int i) { return 64 * PK * (i / PK) + PK * lane + (i % PK); };
     uint32_t u[C][NR];
     uint32_t top[C][2];   // the lane's two largest values
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         top[c][0] = top[c][1] = 0;
 #pragma unroll
-        for (int q = 0; q < NR / 4; ++q) {
-            const f32x4 v4 = *reinterpret_cast<const f32x4*>(xc[c] + 256 * q + 4 * lane);
+        for (int q = 0; q < NR / PK; ++q) {
+            float vq[PK];
+            if constexpr (PK == 4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(xc[c] + 256 * q + 4 * lane);
+                vq[0] = v4[0];
+                vq[1] = v4[1];
+                vq[2] = v4[2];
+                vq[3] = v4[3];
+            } else {
+                const float2 v2 = *reinterpret_cast<const float2*>(xc[c] + 128 * q + 2 * lane);
+                vq[0] = v2.x;
+                vq[1] = v2.y;
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 4 * q + j;
-                const uint32_t v = (c < nc && row_of(i) < nr) ? topk_order(v4[j]) : 0u;
+            for (int j = 0; j < PK; ++j) {
+                const int i = PK * q + j;
+                const uint32_t v = (c < nc && row_of(i) < nr) ? topk_order(vq[j]) : 0u;
                 u[c][i] = v;
                 const uint32_t lo2 = v < top[c][0] ? v : top[c][0];
                 top[c][0] = v > top[c][0] ? v : top[c][0];

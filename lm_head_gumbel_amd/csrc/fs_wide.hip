@@ -28,7 +28,6 @@
 
 namespace fs {
 
-constexpr int kWideThreads = 512;
 constexpr int kMT = 256;         // rows per tile
 constexpr int kKC = 64;          // k per chunk
 constexpr int kRowBytes = 144;   // LDS row stride: 128 data bytes + 16 pad
@@ -39,16 +38,16 @@ struct WideSmem {
     uint64_t fkey[2][NT];
 };
 
-template <int NT, int VAR>
-__global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
-    static_assert(NT == 64 || NT == 128, "column tile");
+template <int NT, int NTHR, int VAR>
+__global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
+    static_assert((NT == 64 || NT == 128) && NTHR == 512, "column tile and workgroup size");
     static_assert(VAR == kVarFlat || VAR == kVarLogits, "variant");
-    constexpr int WM = 2, WN = 4;
+    constexpr int WM = 2, WN = NTHR / 64 / WM;   // wave grid: 2 x 4
     constexpr int RW = kMT / WM;          // 128 rows per wave
     constexpr int MF = RW / 16;           // 8 A fragments
-    constexpr int NF = NT / WN / 16;      // 4, 2, 1 B fragments
-    constexpr int WP = kMT * 8 / kWideThreads;   // W pieces of 16 B per thread per chunk
-    constexpr int HP = NT * 8 / kWideThreads;    // H pieces
+    constexpr int NF = NT / WN / 16;      // 1 or 2 B fragments
+    constexpr int WP = kMT * 8 / NTHR;    // W pieces of 16 B per thread per chunk
+    constexpr int HP = NT * 8 / NTHR;     // H pieces
     __shared__ WideSmem<NT> sm;
 
     // row range w and column group y (see resident_kernel for the XCD pairing)
@@ -87,7 +86,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
     int hofs[HP];
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
-        const int q = tid + kWideThreads * i;
+        const int q = tid + NTHR * i;
         int b = bbase + (q >> 3);
         b = b < a.B ? b : a.B - 1;   // padding columns reuse row B - 1, discarded later
         hofs[i] = b * a.d + (q & 7) * 8;
@@ -95,7 +94,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
     auto set_tile_rows = [&](int tile) {
 #pragma unroll
         for (int i = 0; i < WP; ++i) {
-            const int q = tid + kWideThreads * i;
+            const int q = tid + NTHR * i;
             int row = (mb0 + tile * 16) * kMBlock + (q >> 3);
             row = row < row_end ? row : row_end - 1;   // never read another range's rows
             wofs[i] = (row - first_row) * a.d + (q & 7) * 8;
@@ -103,7 +102,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
     };
     // LDS byte offset of piece i of this thread (W rows first, then H rows)
     auto lds_off = [&](int i, int row_base) {
-        const int q = tid + kWideThreads * i;
+        const int q = tid + NTHR * i;
         return (row_base + (q >> 3)) * kRowBytes + (q & 7) * 16;
     };
 
@@ -263,8 +262,9 @@ __global__ __launch_bounds__(kWideThreads) void wide_kernel(Stage1Args a) {
 
 template <int NT, int VAR>
 static hipError_t launch_wide_nt(const Stage1Args& a, int grid_y, hipStream_t stream) {
+    constexpr int NTHR = 512;
     const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
-    hipLaunchKernelGGL((wide_kernel<NT, VAR>), grid, dim3(kWideThreads), 0, stream, a);
+    hipLaunchKernelGGL((wide_kernel<NT, NTHR, VAR>), grid, dim3(NTHR), 0, stream, a);
     return hipGetLastError();
 }
 
