@@ -321,6 +321,7 @@ Stage1Args stage1_args(const Plan& pl, const fs_params* p, const void* H, const 
     a.tile_mb = pl.tile_mb;
     a.ny = pl.grid_y;
     a.xcd_pair = pl.xcd_pair;
+    a.P = pl.P;
     a.k0 = pl.k0;
     a.k1 = pl.k1;
     a.step = p->step;
@@ -462,7 +463,7 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     const int workers = pl.stream ? 4 * pl.G : pl.G;
     const int units = pl.stream ? 4 * pl.nmb : pl.nmb;
     const int tile_units = pl.stream ? 4 * pl.tile_mb : pl.tile_mb;
-    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.B, pl.T, workers, units,
+    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.P, pl.B, pl.T, workers, units,
                                           tile_units, temp, p->flags, pl.k0, pl.k1, p->step,
                                           tile_max, tile_idx, tile_logmass, out_idx, s));
 }

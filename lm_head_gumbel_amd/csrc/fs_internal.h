@@ -60,7 +60,9 @@ struct Stage1Args {
     int topk;               // k of the top-k variant
     int ny;                 // resident kernel: batch groups sharing one row range
     int xcd_pair;           // resident kernel: 1-D grid, groups of a range on one XCD
-    // partial records [P][B] (P = G for flat, G + T - 1 for grouped)
+    // partial records [B][P] (P slots per row: the workers for flat, workers
+    // + T - 1 for grouped, where (worker w, tile t) is slot w + t)
+    int P;
     float* pm;
     int32_t* pidx;
     float* pL;
@@ -117,7 +119,7 @@ hipError_t launch_stream(int variant, const Stage1Args& a, int grid_y, const Sta
 hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
                               int32_t* out_idx, float* out_score, hipStream_t stream);
 
-hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int B,
+hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P, int B,
                                  int T, int G, int nmb, int tile_mb, const float* temp,
                                  uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
                                  float* tile_max, int32_t* tile_idx, float* tile_L,

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
                     }
                     if (b < a.B) {
                         const int p = (VAR == kVarGrouped) ? w + cur.t : w;
-                        const size_t o = (size_t)p * a.B + b;
+                        const size_t o = (size_t)b * a.P + p;
                         const int32_t id = key_index(k);
                         a.pm[o] = id >= 0 ? key_score(k) : -INFINITY;
                         a.pidx[o] = id;

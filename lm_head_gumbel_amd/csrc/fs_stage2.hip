@@ -36,8 +36,8 @@ __global__ __launch_bounds__(kRedThreads) void stage2_flat_kernel(const float* p
     const int b = blockIdx.x;
     uint64_t best = pack_key(-INFINITY, -1);
     for (int p = threadIdx.x; p < P; p += kRedThreads) {
-        const int32_t id = pidx[(size_t)p * B + b];
-        if (id >= 0) best = key_max(best, pack_key(pm[(size_t)p * B + b], id));
+        const int32_t id = pidx[(size_t)b * P + p];
+        if (id >= 0) best = key_max(best, pack_key(pm[(size_t)b * P + p], id));
     }
     best = block_max_key(best);
     if (threadIdx.x == 0) {
@@ -54,7 +54,7 @@ __device__ __forceinline__ bool row_is_greedy(const float* temp, int b, uint32_t
 }
 
 __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
-    const float* pm, const int32_t* pidx, const float* pL, int B, int T, int G, int nmb,
+    const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int G, int nmb,
     int tile_mb, const float* temp, uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
     float* tile_max, int32_t* tile_idx, float* tile_L, int32_t* out_idx) {
     const int b = blockIdx.x;
@@ -67,8 +67,8 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
         const int wl = part_owner(last, nmb, G);
         uint64_t k = pack_key(-INFINITY, -1);
         Lse l = lse_empty();
-        for (int w = wf; w <= wl; ++w) {   // partial record (w, t) lives at index w + t
-            const size_t o = (size_t)(w + t) * B + b;
+        for (int w = wf; w <= wl; ++w) {   // partial record (w, t) lives in slot w + t
+            const size_t o = (size_t)b * P + (w + t);
             const int32_t id = pidx[o];
             if (id >= 0) k = key_max(k, pack_key(pm[o], id));
             const float Lp = pL[o];
@@ -651,13 +651,13 @@ hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B
     return hipGetLastError();
 }
 
-hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int B,
-                                 int T, int G, int nmb, int tile_mb, const float* temp,
+hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
+                                 int B, int T, int G, int nmb, int tile_mb, const float* temp,
                                  uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
                                  float* tile_max, int32_t* tile_idx, float* tile_L,
                                  int32_t* out_idx, hipStream_t stream) {
     hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kRedThreads), 0, stream, pm, pidx,
-                       pL, B, T, G, nmb, tile_mb, temp, flags, k0, k1, step, tile_max, tile_idx,
+                       pL, P, B, T, G, nmb, tile_mb, temp, flags, k0, k1, step, tile_max, tile_idx,
                        tile_L, out_idx);
     return hipGetLastError();
 }
