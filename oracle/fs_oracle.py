@@ -34,6 +34,9 @@ What is computed (all in float64; every helper is a direct definition):
   online merge  Bernoulli binary merge of (z_c, L_c) chunk summaries,
                 uniforms from stream 2                             [FS-kr Group-Gumbel-Max]
   top-k         k largest x (lowest id on ties), then argmax s     [FS-kr implementation; GMX]
+  top-p after   sort the top-k set, keep the shortest prefix whose
+  top-k         exclusive softmax mass is below top_p times the
+                set's mass, then argmax s over the kept prefix     [FS-kr top-p; CAKE]
   multinomial   inverse CDF of softmax(x) at a stream-3 uniform    [FS-kr problem statement]
 
 Readings taken where the pages leave a step open (each is listed in the design doc):
@@ -46,6 +49,11 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
   * Ties go to the lowest id everywhere [CAKE Correctness contract].
   * A NaN logit counts as masked; a tile or row with nothing valid gives
     m = L = -inf and index -1.
+  * Top-p after top-k works on softmax(x) restricted to the top-k set (x is
+    already tempered), orders the set by x descending with ties to the lower
+    id, and keeps element j when the mass of the elements before it is below
+    top_p times the set's mass [CAKE launch forms]; the draw is the Gumbel
+    argmax over the kept elements, the same noise as every other variant.
 """
 import math
 
@@ -339,6 +347,51 @@ def topk_sample(x, s, k, id0=0):
         out[b] = id0 + int(S[j])
         gap[b] = top_two_gap(s[b, S])
     return out, gap, margin
+
+
+def topk_topp_sample(x, s, k, top_p, id0=0):
+    """Top-p after top-k ([FS-kr] top-p paragraph: top-k first, then top-p
+    on the few candidates; [CAKE] launch forms: keep the shortest prefix
+    whose exclusive mass is below top_p times the top-k mass).
+
+    Per row: S = the k valid ids with the largest x (lowest id on ties),
+    ordered by x descending and then id; q = softmax of x over S; element j
+    of that order is kept when sum_{i<j} q_i < top_p (the q sum to 1 over S);
+    the sample is argmax over the kept ids of s (lowest id on ties).
+
+    Returns (idx [B], s-gap within the kept set [B], top-k membership margin
+    x(k) - x(k+1) [B], cut margin [B]: the distance of the exclusive masses
+    on both sides of the cut from top_p)."""
+    x = np.asarray(x, np.float64)
+    s = np.asarray(s, np.float64)
+    B, V = x.shape
+    out = np.full(B, -1, np.int64)
+    gap = np.full(B, math.inf)
+    margin = np.full(B, math.inf)
+    cut = np.full(B, math.inf)
+    for b in range(B):
+        valid = np.nonzero(np.isfinite(x[b]))[0]
+        if valid.size == 0:
+            continue
+        order = valid[np.lexsort((valid, -x[b, valid]))]   # by x descending, then id
+        S = order[:k]
+        if order.size > k:
+            margin[b] = float(x[b, order[k - 1]] - x[b, order[k]])
+        w = np.exp(x[b, S] - x[b, S[0]])
+        q = w / w.sum()
+        excl = np.concatenate([[0.0], np.cumsum(q)[:-1]])
+        keep = excl < top_p
+        kept = S[keep]
+        # the kept ones are a prefix: the first dropped element (if any) and
+        # the last kept one bound the cut
+        nk = kept.size
+        d_in = abs(top_p - excl[nk - 1])
+        d_out = abs(excl[nk] - top_p) if nk < S.size else math.inf
+        cut[b] = min(d_in, d_out)
+        j, _ = first_argmax(s[b, kept])
+        out[b] = id0 + int(kept[j])
+        gap[b] = top_two_gap(s[b, kept])
+    return out, gap, margin, cut
 
 
 def multinomial(x, temp=None, seed=0, step=0, flags=0, id0=0):

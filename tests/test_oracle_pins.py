@@ -230,6 +230,51 @@ def check_topk(o):
     assert chi_square_p(draws, p) > 0.01
 
 
+def _topp_golden():
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "topp_worked_example.txt")
+    probs, cases = None, []
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if not f or f[0].startswith("#"):
+                continue
+            if f[0] == "probs":
+                probs = np.array([float(v) for v in f[1:]])
+            elif f[0] == "case":
+                cases.append((int(f[1]), float(f[2]), [int(v) for v in f[3:]]))
+    return probs, cases
+
+
+def check_topk_topp(o):
+    """Top-p after top-k: the hand-worked cuts of tests/golden (kept ids are
+    exactly the support of the draws, with the renormalised probabilities),
+    top_p = 1 is the top-k sample, and a tiny top_p keeps only argmax x."""
+    probs, cases = _topp_golden()
+    with np.errstate(divide="ignore"):
+        x = np.log(probs)[None, :]
+    for k, top_p, kept in cases:
+        draws = []
+        for step in range(1500):
+            s = o.scores(x, None, seed=4242, step=step)
+            draws.append(o.topk_topp_sample(x, s, k, top_p)[0][0])
+        draws = np.array(draws)
+        assert set(np.unique(draws)) == set(kept), (k, top_p, kept, np.unique(draws))
+        p = np.zeros(probs.size)
+        p[kept] = probs[kept] / probs[kept].sum()
+        if len(kept) > 1:
+            assert chi_square_p(draws, p) > 0.01
+    rng = np.random.default_rng(31)
+    xr = rng.normal(0.0, 2.0, size=(6, 40))
+    xr[0, 5] = -np.inf
+    s = o.scores(xr, None, seed=9, step=4)
+    for k in (1, 7, 40):
+        assert np.array_equal(o.topk_topp_sample(xr, s, k, 1.0)[0], o.topk_sample(xr, s, k)[0])
+        assert np.array_equal(o.topk_topp_sample(xr, s, k, 1e-12)[0],
+                              np.argmax(np.where(np.isfinite(xr), xr, -np.inf), axis=1))
+
+
 def check_multinomial(o):
     """Inverse-CDF baseline follows softmax(x); a one-hot distribution returns its id."""
     l, x = small_row(V=16, T=0.7, masked=(1, 2))
@@ -256,7 +301,7 @@ def check_scaled_noise_form(o):
 
 PINS = [check_logits_exact, check_softmax_exact, check_greedy, check_partition_invariance,
         check_logmass, check_max_stability, check_hierarchical, check_online_merge,
-        check_topk, check_multinomial, check_scaled_noise_form]
+        check_topk, check_topk_topp, check_multinomial, check_scaled_noise_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -341,6 +386,36 @@ def _mutant(name):
         # W read as if stored [d, V] instead of row-major [V, d]
         mod.logits = lambda H, W: np.asarray(H, np.float64) @ np.asarray(W, np.float64).reshape(
             np.asarray(W).shape[1], np.asarray(W).shape[0])
+    elif name == "topp_inclusive_mass":
+        def topk_topp_sample(x, s, k, top_p, id0=0):
+            # keeps j while the mass up to and including j is below top_p
+            x = np.asarray(x, np.float64)
+            out = np.full(x.shape[0], -1, np.int64)
+            for b in range(x.shape[0]):
+                valid = np.nonzero(np.isfinite(x[b]))[0]
+                S = valid[np.lexsort((valid, -x[b, valid]))][:k]
+                q = np.exp(x[b, S] - x[b, S[0]])
+                q /= q.sum()
+                kept = S[np.cumsum(q) < top_p]
+                kept = kept if kept.size else S[:1]
+                out[b] = id0 + int(kept[np.argmax(np.asarray(s)[b, kept])])
+            return out, None, None, None
+        mod.topk_topp_sample = topk_topp_sample
+    elif name == "topp_in_id_order":
+        def topk_topp_sample(x, s, k, top_p, id0=0):
+            # cuts the top-k set in id order instead of probability order
+            x = np.asarray(x, np.float64)
+            out = np.full(x.shape[0], -1, np.int64)
+            for b in range(x.shape[0]):
+                valid = np.nonzero(np.isfinite(x[b]))[0]
+                S = np.sort(valid[np.lexsort((valid, -x[b, valid]))][:k])
+                q = np.exp(x[b, S] - x[b, S].max())
+                q /= q.sum()
+                excl = np.concatenate([[0.0], np.cumsum(q)[:-1]])
+                kept = S[excl < top_p]
+                out[b] = id0 + int(kept[np.argmax(np.asarray(s)[b, kept])])
+            return out, None, None, None
+        mod.topk_topp_sample = topk_topp_sample
     elif name == "topk_by_noisy_score":
         mod.topk_sample = lambda x, s, k, id0=0: O.topk_sample(s, s, k, id0)
     else:
@@ -359,6 +434,8 @@ MUTANTS = {
     "noise_word_shared_by_block": check_hierarchical,
     "transposed_operand": check_logits_exact,
     "topk_by_noisy_score": check_topk,
+    "topp_inclusive_mass": check_topk_topp,
+    "topp_in_id_order": check_topk_topp,
 }
 
 
