@@ -144,6 +144,14 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
         for i in range(3):
             topk(i)
         res["topk40_calls_per_s"] = 1.0 / timer.run(topk, max(10, steps // 4))[0]
+
+        def topp(i):
+            p.step = i
+            fs.check(fs.fs_sample_topk_topp(p, H, W, None, None, k, 0.9, idx, kws), "topp")
+
+        for i in range(3):
+            topp(i)
+        res["topk40_topp0.9_calls_per_s"] = 1.0 / timer.run(topp, max(10, steps // 4))[0]
     return res
 
 
@@ -233,6 +241,12 @@ def bench_workloads(torch, fs, steps, W_head):
                 fs.check(fs.fs_sample_topk(p, H, W, temp, None, wl.k, idx, kws), name)
 
             line(name, wl, f"top-{wl.k} fs_sample_topk", timed(topk))
+
+            def topp(i):
+                p.step = i
+                fs.check(fs.fs_sample_topk_topp(p, H, W, temp, None, wl.k, 0.9, idx, kws), name)
+
+            line(name, wl, f"top-{wl.k} then top-p 0.9 fs_sample_topk_topp", timed(topp))
             chunk = wl.V // wl.chunks
             pc = fs.params(wl.B, wl.d, wl.V, tile_v=chunk, seed=SEED)
             C = fs.fs_num_tiles(pc)
@@ -466,8 +480,8 @@ def main():
         "hbm_probe": probe,
         "cpu_baseline": cpu,
         "unfused_calls_per_s": head.get("unfused_calls_per_s"),
-        "variants": {k: head[k] for k in ("grouped_calls_per_s", "topk40_calls_per_s")
-                     if k in head},
+        "variants": {k: head[k] for k in ("grouped_calls_per_s", "topk40_calls_per_s",
+                                          "topk40_topp0.9_calls_per_s") if k in head},
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in rows],
         "workloads": ([{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}

@@ -161,6 +161,19 @@ fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const
                          const uint32_t* allow, int32_t k, int32_t* out_idx,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* fs_sample_topk_topp -- top-p after top-k (FlashSampling explainer, top-p
+ * paragraph: compress the candidates with top-k first, then apply top-p to
+ * the few left; the cut follows the rule of the "flashinfer.cake_sampling"
+ * page, launch forms).  S_b as for fs_sample_topk, ordered by x descending
+ * (ties to the lower id); with q = softmax of x over S_b, element j of that
+ * order is kept when the mass of the elements before it is below top_p
+ * (computed in float64 from the FP32 x); out_idx[b] = argmax over the kept
+ * elements of s.  0 < top_p <= 1 (else FS_ERR_INVALID_ARG); top_p = 1 gives
+ * fs_sample_topk's result.  1 <= k <= 64.  Same workspace as fs_sample_topk. */
+fs_status fs_sample_topk_topp(const fs_params* p, const void* H, const void* W, const float* temp,
+                              const uint32_t* allow, int32_t k, float top_p, int32_t* out_idx,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* fs_merge_online -- online binary merge of C group summaries (FlashSampling
  * explainer, Group-Gumbel-Max paragraph).  z and L are device [B, C]
  * row-major (e.g. tile_idx and tile_logmass of fs_sample_grouped with one

@@ -57,6 +57,9 @@ _SIGS = {
                                          _P, _P, ctypes.c_size_t, _P]),
     "fs_sample_topk": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, ctypes.c_int32,
                                       _P, _P, ctypes.c_size_t, _P]),
+    "fs_sample_topk_topp": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P,
+                                           ctypes.c_int32, ctypes.c_float, _P, _P,
+                                           ctypes.c_size_t, _P]),
     "fs_merge_online": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, _P, _P,
                                        _P]),
@@ -160,6 +163,13 @@ def fs_sample_topk(p, H, W, temp, allow, k, out_idx, ws=None, ws_bytes=None, str
     w, n = _ws(ws, ws_bytes)
     return lib().fs_sample_topk(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(temp), _ptr(allow), k,
                                 _ptr(out_idx), w, n, _stream(stream))
+
+
+def fs_sample_topk_topp(p, H, W, temp, allow, k, top_p, out_idx, ws=None, ws_bytes=None,
+                        stream=None):
+    w, n = _ws(ws, ws_bytes)
+    return lib().fs_sample_topk_topp(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(temp), _ptr(allow),
+                                     k, float(top_p), _ptr(out_idx), w, n, _stream(stream))
 
 
 def fs_merge_online(B, C, z, L, temp, seed, step, flags, out_idx, out_L=None, stream=None):

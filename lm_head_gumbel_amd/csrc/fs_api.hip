@@ -336,6 +336,39 @@ fs_status check_operands(const fs_params* p, const void* H, const void* W) {
     return FS_OK;
 }
 
+// Top-k (top_p >= 1) or top-p after top-k (0 < top_p < 1): shared body.
+fs_status sample_topk(const fs_params* p, const void* H, const void* W, const float* temp,
+                      const uint32_t* allow, int32_t k, float top_p, int32_t* out_idx, void* ws,
+                      size_t ws_bytes, void* stream) {
+    fs_status st = check_params(p);
+    if (st != FS_OK) return st;
+    if (k < 1) return FS_ERR_INVALID_ARG;
+    if (!(top_p > 0.f && top_p <= 1.f)) return FS_ERR_INVALID_ARG;   // NaN included
+    if (k > kMaxTopK) return FS_ERR_UNSUPPORTED;
+    if (p->B == 0) return FS_OK;
+    if (!out_idx) return FS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->V > 0 && (st = check_operands(p, H, W)) != FS_OK) return st;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    if (p->V == 0) return from_hip(launch_fill_idx(out_idx, p->B, -1, nullptr, s));
+    Plan pl;
+    make_plan(p, kVarTopk, dev.cus, pl);
+    Workspace w;
+    const size_t need = layout(FS_VARIANT_TOPK, pl, k, nullptr, nullptr);
+    if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
+    layout(FS_VARIANT_TOPK, pl, k, static_cast<char*>(ws), &w);
+    Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
+    a.topk = k;
+    a.cx = w.cx;
+    a.cidx = w.cidx;
+    hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
+                                        : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
+    if (e != hipSuccess) return FS_ERR_HIP;
+    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, pl.B, k, top_p, temp, p->flags, pl.k0,
+                                       pl.k1, p->step, out_idx, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,35 +501,17 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
                                           tile_max, tile_idx, tile_logmass, out_idx, s));
 }
 
+
 fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const float* temp,
                          const uint32_t* allow, int32_t k, int32_t* out_idx, void* ws,
                          size_t ws_bytes, void* stream) {
-    fs_status st = check_params(p);
-    if (st != FS_OK) return st;
-    if (k < 1) return FS_ERR_INVALID_ARG;
-    if (k > kMaxTopK) return FS_ERR_UNSUPPORTED;
-    if (p->B == 0) return FS_OK;
-    if (!out_idx) return FS_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p->V > 0 && (st = check_operands(p, H, W)) != FS_OK) return st;
-    DeviceInfo dev;
-    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
-    if (p->V == 0) return from_hip(launch_fill_idx(out_idx, p->B, -1, nullptr, s));
-    Plan pl;
-    make_plan(p, kVarTopk, dev.cus, pl);
-    Workspace w;
-    const size_t need = layout(FS_VARIANT_TOPK, pl, k, nullptr, nullptr);
-    if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
-    layout(FS_VARIANT_TOPK, pl, k, static_cast<char*>(ws), &w);
-    Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
-    a.topk = k;
-    a.cx = w.cx;
-    a.cidx = w.cidx;
-    hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
-                                        : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
-    if (e != hipSuccess) return FS_ERR_HIP;
-    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, pl.B, k, temp, p->flags, pl.k0, pl.k1,
-                                       p->step, out_idx, s));
+    return sample_topk(p, H, W, temp, allow, k, 1.f, out_idx, ws, ws_bytes, stream);
+}
+
+fs_status fs_sample_topk_topp(const fs_params* p, const void* H, const void* W, const float* temp,
+                              const uint32_t* allow, int32_t k, float top_p, int32_t* out_idx,
+                              void* ws, size_t ws_bytes, void* stream) {
+    return sample_topk(p, H, W, temp, allow, k, top_p, out_idx, ws, ws_bytes, stream);
 }
 
 fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L,

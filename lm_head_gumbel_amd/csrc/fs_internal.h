@@ -125,9 +125,10 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                                  float* tile_max, int32_t* tile_idx, float* tile_L,
                                  int32_t* out_idx, hipStream_t stream);
 
+// top_p >= 1: plain top-k; 0 < top_p < 1: top-p after top-k.
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
-                              const float* temp, uint32_t flags, uint32_t k0, uint32_t k1,
-                              uint32_t step, int32_t* out_idx, hipStream_t stream);
+                              float top_p, const float* temp, uint32_t flags, uint32_t k0,
+                              uint32_t k1, uint32_t step, int32_t* out_idx, hipStream_t stream);
 
 hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
                                uint32_t k0, uint32_t k1, uint32_t step, uint32_t flags,

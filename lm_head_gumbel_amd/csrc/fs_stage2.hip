@@ -104,8 +104,8 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
 // ---------------------------------------------------------------------------
 // top-k: candidates [G][B][k] (x, id) from stage 1, one list per workgroup
 // (unused entries have id -1).  The row's k largest (x, -id) over all lists
-// are selected exactly; the noise s = x + Gumbel is drawn for those k only
-// and the largest s wins.
+// are selected exactly; optionally only the top-p prefix of them is kept;
+// the noise s = x + Gumbel is drawn for the kept only and the largest s wins.
 //
 // stage2_topk_kernel: one workgroup of 512 threads per row holds the G*k
 // candidates in registers (PER per thread).  A lower bound
@@ -158,10 +158,57 @@ __device__ __forceinline__ uint64_t scored_key(uint32_t u, int32_t id, int b, bo
     return pack_key(s, id);
 }
 
+// Wave-wide bitonic sort of one 64-bit key per lane, largest key in lane 0.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t o = shfl_xor_u64(key, stride);
+            // blocks of `size` lanes alternate direction; the last one is descending
+            const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
+            key = take_max ? (key > o ? key : o) : (key < o ? key : o);
+        }
+    return key;
+}
+
+// One wave: the sample among the row's selected top-k candidates, at most 64
+// and one per lane, as the key (order image of x << 32) | ~id (0: none).
+// With top_p < 1 the candidates are sorted by key (x descending, ties to
+// the lower id) and only those whose exclusive softmax mass (float64) is
+// below top_p times the set's mass are kept ("flashinfer.cake_sampling",
+// launch forms).  The noise is drawn for the kept candidates only.  Returns
+// the winning id in every lane (-1 when there is none).
+__device__ int32_t finish_topk(uint64_t key, int b, bool greedy, float top_p, uint32_t k0,
+                               uint32_t k1, uint32_t step) {
+    const int lane = threadIdx.x & 63;
+    bool keep = key != 0ull;
+    if (top_p < 1.f) {
+        key = wave_sort_desc(key);
+        keep = key != 0ull;
+        const double x = ordered_to_float((uint32_t)(key >> 32));
+        const double xmax = __shfl(x, 0, 64);   // lane 0 holds the largest
+        const double q = keep ? exp(x - xmax) : 0.0;
+        double incl = q;   // inclusive prefix sum over the sorted lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const double total = __shfl(incl, 63, 64);
+        keep = keep && (incl - q) < (double)top_p * total;
+    }
+    uint64_t best = pack_key(-INFINITY, -1);
+    if (keep)
+        best = scored_key((uint32_t)(key >> 32), (int32_t)~(uint32_t)key, b, greedy, k0, k1, step);
+    return key_index(wave_max_key(best));
+}
+
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
-    const float* cx, const int32_t* cidx, int G, int B, int k, const float* temp, uint32_t flags,
-    uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
+    const float* cx, const int32_t* cidx, int G, int B, int k, float top_p, const float* temp,
+    uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -258,7 +305,7 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) c2 += v[0][j] >= lo2 ? 1 : 0;
         const int n2 = wave_sum<8>(c2);
-        uint64_t best = pack_key(-INFINITY, -1);
+        uint64_t key = 0ull;   // this lane's selected candidate, if any
         if (n2 <= 64) {
             // compact to one per lane (every lane has read its entries above)
             int base = 0;
@@ -282,19 +329,31 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
             w1[0][0] = lane < n2 ? g_u[lane] : 0u;
             t1[0][0] = g_tb[lane];
             wave_select<1, 1>(w1, t1, k, sel);
-            if (sel[0][0])
-                best = scored_key(w1[0][0], (int32_t)~t1[0][0], b, greedy, k0, k1, step);
+            if (sel[0][0]) key = ((uint64_t)w1[0][0] << 32) | t1[0][0];
         } else {
+            // at most k <= 64 selected: gather them one per lane
             bool sel[1][8];
             wave_select<1, 8>(v, tb, k, sel);
+            __builtin_amdgcn_wave_barrier();
+            int base = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (sel[0][j])
-                    best = key_max(best,
-                                   scored_key(v[0][j], (int32_t)~tb[0][j], b, greedy, k0, k1, step));
+            for (int j = 0; j < 8; ++j) {
+                const uint64_t sb = __ballot(sel[0][j]);
+                if (sel[0][j]) {
+                    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                               (uint32_t)(sb >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)sb, 0u));
+                    g_u[pos] = v[0][j];
+                    g_tb[pos] = tb[0][j];
+                }
+                base += __popcll(sb);
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            if (lane < base) key = ((uint64_t)g_u[lane] << 32) | g_tb[lane];
         }
-        best = wave_max_key(best);
-        if (lane == 0) out_idx[b] = key_index(best);
+        const int32_t id = finish_topk(key, b, greedy, top_p, k0, k1, step);
+        if (lane == 0) out_idx[b] = id;
         return;
     }
 
@@ -334,21 +393,34 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
         }
     }
 
-    uint64_t best = pack_key(-INFINITY, -1);
+    // gather the (at most k) selected in LDS, then one wave finishes
+    __syncthreads();   // every wave is done reading the gather area
+    if (threadIdx.x == 0) g_n = 0;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-        if (u[i] > t || (need > 0 && u[i] == t && iv[i] <= id_max))
-            best = key_max(best, scored_key(u[i], iv[i], b, greedy, k0, k1, step));
-    best = block_max_key_topk(best);
-    if (threadIdx.x == 0) out_idx[b] = key_index(best);
+        if (u[i] > t || (need > 0 && u[i] == t && iv[i] <= id_max)) {
+            const int pos = atomicAdd(&g_n, 1);
+            if (pos < 64) {
+                g_u[pos] = u[i];
+                g_tb[pos] = ~(uint32_t)iv[i];
+            }
+        }
+    __syncthreads();
+    if (wave == 0) {
+        const int nsel = g_n < 64 ? g_n : 64;
+        const uint64_t key = lane < nsel ? ((uint64_t)g_u[lane] << 32) | g_tb[lane] : 0ull;
+        const int32_t id = finish_topk(key, b, greedy, top_p, k0, k1, step);
+        if (lane == 0) out_idx[b] = id;
+    }
 }
 
 // Radix select of the k-th largest packed (x, id) key over the row's G*k
 // candidates (8 passes of 8 bits, candidates re-read from memory each pass),
 // then argmax s over the keys >= it: any number of candidates.
 __global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
-    const float* cx, const int32_t* cidx, int G, int B, int k, const float* temp, uint32_t flags,
-    uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
+    const float* cx, const int32_t* cidx, int G, int B, int k, float top_p, const float* temp,
+    uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
     const int b = blockIdx.x;
     __shared__ uint32_t hist[256];
     __shared__ uint64_t s_prefix;
@@ -408,15 +480,26 @@ __global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
         }
         thresh = prefix;   // keys are distinct, so exactly k keys are >= prefix
     }
-    uint64_t best = pack_key(-INFINITY, -1);
+    // gather the (at most k) selected keys, then one wave finishes
+    __shared__ uint64_t sel[64];
+    __shared__ int nsel;
+    if (threadIdx.x == 0) nsel = 0;
+    __syncthreads();
     for (int e = threadIdx.x; e < n; e += kRedThreads) {
         uint64_t key;
-        if (cand_key(e, key) && key >= thresh)
-            best = key_max(best, scored_key(float_to_ordered(key_score(key)), key_index(key), b,
-                                            row_is_greedy(temp, b, flags), k0, k1, step));
+        if (cand_key(e, key) && key >= thresh) {
+            const int pos = atomicAdd(&nsel, 1);
+            if (pos < 64) sel[pos] = key;
+        }
     }
-    best = block_max_key(best);
-    if (threadIdx.x == 0) out_idx[b] = key_index(best);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const uint64_t key = lane < min(nsel, 64) ? sel[lane] : 0ull;
+        const int32_t id =
+            finish_topk(key, b, row_is_greedy(temp, b, flags), top_p, k0, k1, step);
+        if (lane == 0) out_idx[b] = id;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -663,12 +746,12 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
 }
 
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
-                              const float* temp, uint32_t flags, uint32_t k0, uint32_t k1,
-                              uint32_t step, int32_t* out_idx, hipStream_t stream) {
+                              float top_p, const float* temp, uint32_t flags, uint32_t k0,
+                              uint32_t k1, uint32_t step, int32_t* out_idx, hipStream_t stream) {
 #define FS_TOPK2(PER_)                                                                       \
     if ((int64_t)G * k <= (int64_t)kTopkThreads * PER_) {                                   \
         hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \
-                           cx, cidx, G, B, k, temp, flags, k0, k1, step, out_idx);           \
+                           cx, cidx, G, B, k, top_p, temp, flags, k0, k1, step, out_idx);    \
         return hipGetLastError();                                                            \
     }
     FS_TOPK2(4)
@@ -678,7 +761,7 @@ hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B
     FS_TOPK2(64)
 #undef FS_TOPK2
     hipLaunchKernelGGL(stage2_topk_radix_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cidx,
-                       G, B, k, temp, flags, k0, k1, step, out_idx);
+                       G, B, k, top_p, temp, flags, k0, k1, step, out_idx);
     return hipGetLastError();
 }
 

@@ -89,6 +89,22 @@ def run_topk(x, p, k):
     return host(idx).astype(np.int64)
 
 
+def run_topp(x, p, k, top_p):
+    t = torch()
+    idx = t.full((x.B,), -7, dtype=t.int32, device="cuda")
+    ws = workspace(p, fs.FS_VARIANT_TOPK, k)
+    fs.check(fs.fs_sample_topk_topp(p, x.H, x.W, x.temp, x.allow, k, top_p, idx, ws),
+             "fs_sample_topk_topp")
+    t.cuda.synchronize()
+    return host(idx).astype(np.int64)
+
+
+# top-p cut pinned when every exclusive mass next to the cut is this far from
+# top_p: the GPU's masses come from FP32 x (relative error ~1e-6 each), the
+# oracle's from float64 logits
+TOL_CUT = 1e-4
+
+
 def run_logits(x, p):
     t = torch()
     out = t.full((x.B, x.V), 7.0, dtype=t.float32, device="cuda")

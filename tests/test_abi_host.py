@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fs_sample", "fs_sample_grouped", "fs_sample_topk", "fs_merge_online",
+    for n in ("fs_sample", "fs_sample_grouped", "fs_sample_topk", "fs_sample_topk_topp",
+              "fs_merge_online",
               "fs_logits", "fs_multinomial", "fs_workspace_bytes", "fs_status_string",
               "fs_debug_noise", "fs_num_tiles", "fs_version"):
         assert n in names
@@ -71,6 +72,8 @@ def test_null_and_negative_arguments_are_rejected():
     assert fs.fs_sample(fs.params(2, 64, 128, flags=8), 16, 16, None, None, 16) == \
         fs.FS_ERR_INVALID_ARG
     assert fs.fs_sample_topk(p, 16, 16, None, None, 0, 16) == fs.FS_ERR_INVALID_ARG
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert fs.fs_sample_topk_topp(p, 16, 16, None, None, 5, bad, 16) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_sample_grouped(p, 16, 16, None, None, None, None, None) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_merge_online(-1, 4, None, None, None, 0, 0, 0, None) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_merge_online(2, 4, None, None, None, 0, 0, 0, 0x1000) == fs.FS_ERR_INVALID_ARG
@@ -95,6 +98,7 @@ def test_empty_batch_is_a_no_op():
     p = fs.params(0, 64, 128)
     assert fs.fs_sample(p, None, None, None, None, None) == fs.FS_OK
     assert fs.fs_sample_topk(p, None, None, None, None, 5, None) == fs.FS_OK
+    assert fs.fs_sample_topk_topp(p, None, None, None, None, 5, 0.9, None) == fs.FS_OK
     assert fs.fs_logits(p, None, None, None, None) == fs.FS_OK
     assert fs.fs_merge_online(0, 3, None, None, None, 0, 0, 0, None) == fs.FS_OK
 

@@ -183,3 +183,42 @@ def test_topk_and_online_merge():
     # the merged log-mass is the log-sum-exp over the whole vocabulary
     check_values(gA, [O.log_sum_exp(x[b]) for b in rows], what="total log-mass")
     log(f"  online merge: {pin.sum()}/{wl.B} rows pinned")
+
+
+def test_topk_topp_histogram():
+    """Top-40 then top-p 0.9 at the d=5120, V=152064 shape: over 600 decode
+    steps the draws of 8 rows follow softmax(x) renormalised over the kept
+    prefix of the top-40 set (pooled chi-square)."""
+    wl = WORKLOADS["topk_b32"]
+    B, k, top_p, steps = 8, wl.k, 0.9, 600
+    Hb = hidden_bf16(wl.B, wl.d)[:B].copy()
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()[:B]
+    x_in = Inputs(Hb, Wb, temp)
+    t = torch()
+    idx = t.empty((steps, B), dtype=t.int32, device="cuda")
+    p = x_in.params(tile_v=wl.tile_v, seed=PHILOX_SEED)
+    ws = t.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, k), dtype=t.uint8, device="cuda")
+    for step in range(steps):
+        p.step = step
+        fs.check(fs.fs_sample_topk_topp(p, x_in.H, x_in.W, x_in.temp, None, k, top_p, idx[step],
+                                        ws))
+    draws = idx.cpu().numpy()
+    x = O.tempered(O.logits_bf16(Hb, Wb), temp)
+    _, _, margin, cut = O.topk_topp_sample(x, x, k, top_p)
+    rows = [b for b in range(B) if margin[b] > 1e-3 and cut[b] > 1e-4]   # sets pinned
+    assert len(rows) >= B // 2
+    probs = []
+    for b in rows:
+        order = np.lexsort((np.arange(wl.V), -x[b]))[:k]
+        q = softmax(x[b, order])
+        excl = np.concatenate([[0.0], np.cumsum(q)[:-1]])
+        kept = order[excl < top_p]
+        pb = np.zeros(wl.V)
+        pb[kept] = softmax(x[b, kept])
+        probs.append(pb)
+        assert np.all(np.isin(draws[:, b], kept))
+    pv = chi_square_rows_p([draws[:, b] for b in rows], probs)
+    log(f"top-{k} top-p {top_p}: pooled chi-square over {len(rows)} rows x {steps} steps: "
+        f"p = {pv:.3f}")
+    assert pv > 0.01

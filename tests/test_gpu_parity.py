@@ -15,9 +15,9 @@ from lm_head_gumbel_amd.inputs import (bf16_bits_to_f32, f32_to_bf16_bits, hidde
                                        normal_f32, tiny_reference, weights_bf16)
 from oracle import fs_oracle as O
 from oracle import philox as px
-from gpu_util import (Inputs, TOL_GAP, TOL_VALUE, check_index_rows, check_values, log,
+from gpu_util import (Inputs, TOL_CUT, TOL_GAP, TOL_VALUE, check_index_rows, check_values, log,
                       run_flat, run_grouped, run_logits, run_merge, run_multinomial, run_topk,
-                      torch)
+                      run_topp, torch)
 from stats_util import chi_square_p, chi_square_rows_p, softmax
 
 pytestmark = pytest.mark.gpu
@@ -130,6 +130,15 @@ def compare_all(Hb, Wb, temp=None, n_valid=None, allow=None, tile_v=128, v_offse
                     assert tk[b] == -1
                 else:
                     assert np.isfinite(r["x"][b, tk[b] - v_offset])
+            # top-p after top-k; top_p = 1 is the top-k sample itself
+            assert np.array_equal(run_topp(x_in, p, k, 1.0), tk)
+            for top_p in (0.9, 0.5):
+                tp = run_topp(x_in, p, k, top_p)
+                oi, ogap, omarg, ocut = O.topk_topp_sample(r["x"], r["s"], k, top_p, v_offset)
+                pin = (ogap > TOL_GAP) & (omarg > 1e-3) & (ocut > TOL_CUT)
+                bad = np.nonzero(pin & (tp != oi))[0]
+                assert bad.size == 0, f"top-{k} top-p {top_p} rows {bad} got {tp[bad]} want {oi[bad]}"
+                assert np.all((tp == -1) == (oi == -1))
         # unfused baseline on the GPU's own logits
         if check_logits:
             mi = run_multinomial(x_in, p, gl_dev)
@@ -322,6 +331,15 @@ def test_topk_all_logits_equal(V, k):
     pin[2] = True   # greedy row: equal scores, the lowest id
     assert want[2] == 0
     assert np.array_equal(got[pin], want[pin])
+    # top-p 0.5 on k equal masses keeps the first ceil(k / 2): ids 0 .. ceil(k/2) - 1
+    kept = (k + 1) // 2
+    tp = run_topp(x_in, p, k, 0.5)
+    assert np.all((tp >= 0) & (tp < kept)), tp
+    want = np.argmax(sc[:, :kept], axis=1)
+    top2 = np.sort(sc[:, :kept], axis=1)
+    pin = (top2[:, -1] - top2[:, -2]) > TOL_GAP if kept > 1 else np.ones(B, bool)
+    pin[2] = True
+    assert np.array_equal(tp[pin], want[pin])
 
 
 def test_repeated_calls_bit_identical():
