@@ -97,6 +97,17 @@ typedef struct {
     uint64_t seed;    /* Philox key                                             */
     uint32_t step;    /* decode step: Philox counter word 2                     */
     uint32_t flags;   /* FS_NO_NOISE                                            */
+    /* Calls a HIP graph can replay with fresh noise (graph-friendly decode
+     * loops; the cake_sampling page's correctness contract keeps the generator
+     * out of a captured region and takes explicit seed and offset instead):
+     * seeds: NULL, or device [B] uint64: row b's Philox key is seeds[b]
+     *        (per-request seeds), replacing `seed`;
+     * step_ptr: NULL, or a device uint32 read when the kernels run, replacing
+     *        `step` (the caller advances it on the device between replays).
+     * Both are read, never written; they must stay valid until the call's
+     * work on the stream completes. */
+    const uint64_t* seeds;
+    const uint32_t* step_ptr;
 } fs_params;
 
 /* Human-readable name of a status code (static storage). */
@@ -186,6 +197,15 @@ fs_status fs_sample_topk_topp(const fs_params* p, const void* H, const void* W, 
 fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L,
                           const float* temp, uint64_t seed, uint32_t step, uint32_t flags,
                           int32_t* out_idx, float* out_L, void* stream);
+
+/* fs_merge_online_dev -- fs_merge_online with its noise key and step taken
+ * as fs_params takes them for graph replay: seeds NULL (then `seed` for
+ * every row) or device [B] uint64 per-row keys; step_ptr NULL (then `step`)
+ * or a device uint32 read when the kernel runs. */
+fs_status fs_merge_online_dev(int32_t B, int32_t C, const int32_t* z, const float* L,
+                              const float* temp, uint64_t seed, const uint64_t* seeds,
+                              uint32_t step, const uint32_t* step_ptr, uint32_t flags,
+                              int32_t* out_idx, float* out_L, void* stream);
 
 /* fs_logits -- unfused baseline, step 1: writes l[b, j] (FP32, no
  * temperature, no mask) to device logits [B, V] row-major.  This is the

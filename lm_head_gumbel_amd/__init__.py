@@ -24,15 +24,19 @@ class fs_params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("d", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("n_valid", ctypes.c_int32), ("v_offset", ctypes.c_int32),
                 ("tile_v", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("step", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+                ("step", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("seeds", ctypes.c_void_p), ("step_ptr", ctypes.c_void_p)]
 
 
-def params(B, d, V, n_valid=None, v_offset=0, tile_v=0, seed=0, step=0, flags=0):
-    """Build an fs_params; n_valid defaults to v_offset + V (nothing masked)."""
+def params(B, d, V, n_valid=None, v_offset=0, tile_v=0, seed=0, step=0, flags=0, seeds=None,
+           step_ptr=None):
+    """Build an fs_params; n_valid defaults to v_offset + V (nothing masked).
+    seeds / step_ptr: optional device uint64 [B] per-row keys and device uint32
+    step (tensors or raw addresses)."""
     if n_valid is None:
         n_valid = v_offset + V
     return fs_params(B, d, V, n_valid, v_offset, tile_v, seed & 0xFFFFFFFFFFFFFFFF,
-                     step & 0xFFFFFFFF, flags)
+                     step & 0xFFFFFFFF, flags, _ptr(seeds), _ptr(step_ptr))
 
 
 class FsError(RuntimeError):
@@ -63,6 +67,9 @@ _SIGS = {
     "fs_merge_online": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, _P, _P,
                                        _P]),
+    "fs_merge_online_dev": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                           ctypes.c_uint64, _P, ctypes.c_uint32, _P,
+                                           ctypes.c_uint32, _P, _P, _P]),
     "fs_logits": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, ctypes.c_size_t,
                                  _P]),
     "fs_multinomial": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, _P,
@@ -176,6 +183,14 @@ def fs_merge_online(B, C, z, L, temp, seed, step, flags, out_idx, out_L=None, st
     return lib().fs_merge_online(B, C, _ptr(z), _ptr(L), _ptr(temp),
                                  seed & 0xFFFFFFFFFFFFFFFF, step & 0xFFFFFFFF, flags,
                                  _ptr(out_idx), _ptr(out_L), _stream(stream))
+
+
+def fs_merge_online_dev(B, C, z, L, temp, seed, seeds, step, step_ptr, flags, out_idx, out_L=None,
+                        stream=None):
+    return lib().fs_merge_online_dev(B, C, _ptr(z), _ptr(L), _ptr(temp),
+                                     seed & 0xFFFFFFFFFFFFFFFF, _ptr(seeds), step & 0xFFFFFFFF,
+                                     _ptr(step_ptr), flags, _ptr(out_idx), _ptr(out_L),
+                                     _stream(stream))
 
 
 def fs_logits(p, H, W, logits, ws=None, ws_bytes=None, stream=None):

@@ -304,6 +304,10 @@ size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
 
 fs_status from_hip(hipError_t e) { return e == hipSuccess ? FS_OK : FS_ERR_HIP; }
 
+NoiseSrc noise_src(const Plan& pl, const fs_params* p) {
+    return NoiseSrc{pl.k0, pl.k1, p->step, p->seeds, p->step_ptr};
+}
+
 Stage1Args stage1_args(const Plan& pl, const fs_params* p, const void* H, const void* W,
                        const float* temp, const uint32_t* allow) {
     Stage1Args a{};
@@ -322,9 +326,7 @@ Stage1Args stage1_args(const Plan& pl, const fs_params* p, const void* H, const 
     a.ny = pl.grid_y;
     a.xcd_pair = pl.xcd_pair;
     a.P = pl.P;
-    a.k0 = pl.k0;
-    a.k1 = pl.k1;
-    a.step = p->step;
+    a.noise = noise_src(pl, p);
     a.flags = p->flags;
     return a;
 }
@@ -365,8 +367,8 @@ fs_status sample_topk(const fs_params* p, const void* H, const void* W, const fl
     hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
                                         : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
-    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, pl.B, k, top_p, temp, p->flags, pl.k0,
-                                       pl.k1, p->step, out_idx, s));
+    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, pl.B, k, top_p, temp, p->flags,
+                                       noise_src(pl, p), out_idx, s));
 }
 
 }  // namespace
@@ -497,8 +499,8 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     const int units = pl.stream ? 4 * pl.nmb : pl.nmb;
     const int tile_units = pl.stream ? 4 * pl.tile_mb : pl.tile_mb;
     return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.P, pl.B, pl.T, workers, units,
-                                          tile_units, temp, p->flags, pl.k0, pl.k1, p->step,
-                                          tile_max, tile_idx, tile_logmass, out_idx, s));
+                                          tile_units, temp, p->flags, noise_src(pl, p), tile_max,
+                                          tile_idx, tile_logmass, out_idx, s));
 }
 
 
@@ -514,18 +516,27 @@ fs_status fs_sample_topk_topp(const fs_params* p, const void* H, const void* W, 
     return sample_topk(p, H, W, temp, allow, k, top_p, out_idx, ws, ws_bytes, stream);
 }
 
-fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L,
-                          const float* temp, uint64_t seed, uint32_t step, uint32_t flags,
-                          int32_t* out_idx, float* out_L, void* stream) {
+fs_status fs_merge_online_dev(int32_t B, int32_t C, const int32_t* z, const float* L,
+                              const float* temp, uint64_t seed, const uint64_t* seeds,
+                              uint32_t step, const uint32_t* step_ptr, uint32_t flags,
+                              int32_t* out_idx, float* out_L, void* stream) {
     if (B < 0 || C < 0) return FS_ERR_INVALID_ARG;
     if (flags & ~kFlagNoNoise) return FS_ERR_INVALID_ARG;
     if (B == 0) return FS_OK;
     if (!out_idx || (C > 0 && (!z || !L))) return FS_ERR_INVALID_ARG;
     DeviceInfo dev;
     if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
-    return from_hip(launch_merge_online(B, C, z, L, temp, (uint32_t)(seed & 0xFFFFFFFFu),
-                                        (uint32_t)(seed >> 32), step, flags, out_idx, out_L,
+    const NoiseSrc noise{(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), step, seeds,
+                         step_ptr};
+    return from_hip(launch_merge_online(B, C, z, L, temp, noise, flags, out_idx, out_L,
                                         static_cast<hipStream_t>(stream)));
+}
+
+fs_status fs_merge_online(int32_t B, int32_t C, const int32_t* z, const float* L,
+                          const float* temp, uint64_t seed, uint32_t step, uint32_t flags,
+                          int32_t* out_idx, float* out_L, void* stream) {
+    return fs_merge_online_dev(B, C, z, L, temp, seed, nullptr, step, nullptr, flags, out_idx,
+                               out_L, stream);
 }
 
 fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* logits,
@@ -578,7 +589,7 @@ fs_status fs_multinomial(const fs_params* p, const float* logits, const float* t
     layout(FS_VARIANT_MULTINOMIAL, pl, 0, static_cast<char*>(ws), &w);
     const int nchunk = (p->V + kMultinomialChunk - 1) / kMultinomialChunk;
     return from_hip(launch_multinomial(logits, temp, allow, p->B, p->V, p->n_valid, p->v_offset,
-                                       pl.k0, pl.k1, p->step, p->flags, nchunk,
+                                       noise_src(pl, p), p->flags, nchunk,
                                        kMultinomialChunk, w.mm, w.ms, w.mkey, out_idx, s));
 }
 

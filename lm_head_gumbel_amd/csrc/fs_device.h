@@ -56,6 +56,28 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t r) {
     return -__builtin_amdgcn_logf(e) * kLn2;
 }
 
+// Where a call's noise comes from: the Philox key (the call's seed) and the
+// decode step, or, when given, one seed per batch row (seeds[b]) and a step
+// read from device memory at run time (calls that a graph can replay).
+struct NoiseSrc {
+    uint32_t k0, k1, step;
+    const uint64_t* seeds;      // [B] or null
+    const uint32_t* step_ptr;   // or null
+};
+struct RowKey {
+    uint32_t k0, k1, step;
+};
+__device__ __forceinline__ RowKey row_key(const NoiseSrc& n, int b) {
+    RowKey r{n.k0, n.k1, n.step};
+    if (n.seeds) {
+        const uint64_t s = n.seeds[b];
+        r.k0 = (uint32_t)s;
+        r.k1 = (uint32_t)(s >> 32);
+    }
+    if (n.step_ptr) r.step = *n.step_ptr;
+    return r;
+}
+
 // Uniform on (0, 1) from one word: (r + 1/2) 2^-32, rounded to FP32.
 __device__ __forceinline__ float uniform_from_word(uint32_t r) {
     return fmaf((float)r, 0x1p-32f, 0x1p-33f);

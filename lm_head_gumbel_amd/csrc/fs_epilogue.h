@@ -17,6 +17,7 @@ struct ColCtx {
     bool greedy;
     float inv_t;
     const uint32_t* allow_row;
+    RowKey key;   // Philox key and step of the column's batch row
 };
 
 __device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
@@ -31,6 +32,7 @@ __device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
         c.inv_t = c.greedy ? 1.f : 1.f / T;
     }
     c.allow_row = (a.allow && c.ok) ? a.allow + (size_t)col * ((a.V + 31) >> 5) : nullptr;
+    c.key = c.ok ? row_key(a.noise, col) : RowKey{a.noise.k0, a.noise.k1, a.noise.step};
     return c;
 }
 
@@ -60,7 +62,8 @@ __device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c
     for (int r = 0; r < 4; ++r) s[r] = x[r];
     if (!c.greedy && blk_ok && c.ok) {
         const uint4 rw = philox4x32_10(
-            make_uint4((uint32_t)gid0 >> 2, (uint32_t)c.col, a.step, kStreamToken), a.k0, a.k1);
+            make_uint4((uint32_t)gid0 >> 2, (uint32_t)c.col, c.key.step, kStreamToken), c.key.k0,
+            c.key.k1);
         s[0] += gumbel_from_word(rw.x);
         s[1] += gumbel_from_word(rw.y);
         s[2] += gumbel_from_word(rw.z);

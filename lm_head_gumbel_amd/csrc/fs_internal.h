@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fs_device.h"
+
 namespace fs {
 
 constexpr int kMBlock = 16;        // vocab rows per MFMA block (M of 16x16x32)
@@ -56,7 +58,8 @@ struct Stage1Args {
     int nmb;                // ceil(V / 16)
     int G;                  // workgroups along the vocabulary (gridDim.x)
     int tile_mb;            // blocks per record tile (flat: one segment)
-    uint32_t k0, k1, step, flags;
+    NoiseSrc noise;         // Philox key and step (per row when given)
+    uint32_t flags;
     int topk;               // k of the top-k variant
     int ny;                 // resident kernel: batch groups sharing one row range
     int xcd_pair;           // resident kernel: 1-D grid, groups of a range on one XCD
@@ -119,24 +122,25 @@ hipError_t launch_stream(int variant, const Stage1Args& a, int grid_y, const Sta
 hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
                               int32_t* out_idx, float* out_score, hipStream_t stream);
 
-hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P, int B,
+hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
+                                 int B,
                                  int T, int G, int nmb, int tile_mb, const float* temp,
-                                 uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
+                                 uint32_t flags, const NoiseSrc& noise,
                                  float* tile_max, int32_t* tile_idx, float* tile_L,
                                  int32_t* out_idx, hipStream_t stream);
 
 // top_p >= 1: plain top-k; 0 < top_p < 1: top-p after top-k.
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
-                              float top_p, const float* temp, uint32_t flags, uint32_t k0,
-                              uint32_t k1, uint32_t step, int32_t* out_idx, hipStream_t stream);
+                              float top_p, const float* temp, uint32_t flags,
+                              const NoiseSrc& noise, int32_t* out_idx, hipStream_t stream);
 
 hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
-                               uint32_t k0, uint32_t k1, uint32_t step, uint32_t flags,
+                               const NoiseSrc& noise, uint32_t flags,
                                int32_t* out_idx, float* out_L, hipStream_t stream);
 
 hipError_t launch_multinomial(const float* logits, const float* temp, const uint32_t* allow,
-                              int B, int V, int n_valid, int v_offset, uint32_t k0, uint32_t k1,
-                              uint32_t step, uint32_t flags, int nchunk, int chunk,
+                              int B, int V, int n_valid, int v_offset, const NoiseSrc& noise,
+                              uint32_t flags, int nchunk, int chunk,
                               float* ws_m, float* ws_s, uint64_t* ws_key, int32_t* out_idx,
                               hipStream_t stream);
 

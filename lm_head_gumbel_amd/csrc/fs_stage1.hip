@@ -113,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
         inv_t = greedy ? 1.f : 1.f / T;
     }
     const int allow_words = (a.V + 31) >> 5;
+    const RowKey rk = col_ok ? row_key(a.noise, col) : RowKey{0u, 0u, 0u};
     const uint32_t* allow_row = (a.allow && col_ok) ? a.allow + (size_t)col * allow_words : nullptr;
 
     if constexpr (VAR == kVarTopk) {
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
                 float s[4] = {x[0], x[1], x[2], x[3]};
                 if (VAR != kVarTopk && !greedy && blk_ok && col_ok) {
                     const uint4 rw = philox4x32_10(
-                        make_uint4((uint32_t)gid0 >> 2, (uint32_t)col, a.step, kStreamToken),
-                        a.k0, a.k1);
+                        make_uint4((uint32_t)gid0 >> 2, (uint32_t)col, rk.step, kStreamToken),
+                        rk.k0, rk.k1);
                     s[0] += gumbel_from_word(rw.x);
                     s[1] += gumbel_from_word(rw.y);
                     s[2] += gumbel_from_word(rw.z);

@@ -55,10 +55,11 @@ __device__ __forceinline__ bool row_is_greedy(const float* temp, int b, uint32_t
 
 __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
     const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int G, int nmb,
-    int tile_mb, const float* temp, uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
-    float* tile_max, int32_t* tile_idx, float* tile_L, int32_t* out_idx) {
+    int tile_mb, const float* temp, uint32_t flags, NoiseSrc noise, float* tile_max,
+    int32_t* tile_idx, float* tile_L, int32_t* out_idx) {
     const int b = blockIdx.x;
     const bool greedy = row_is_greedy(temp, b, flags);
+    const RowKey rk = row_key(noise, b);
     uint64_t best = pack_key(-INFINITY, -1);
     for (int t = threadIdx.x; t < T; t += kRedThreads) {
         const int first = t * tile_mb;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
             float sc = L;
             if (!greedy) {
                 const uint4 rw = philox4x32_10(
-                    make_uint4((uint32_t)t >> 2, (uint32_t)b, step, kStreamGroup), k0, k1);
+                    make_uint4((uint32_t)t >> 2, (uint32_t)b, rk.step, kStreamGroup), rk.k0, rk.k1);
                 const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
                 sc += gumbel_from_word(words[t & 3]);
             }
@@ -152,9 +153,9 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
 // Key (s, id) of a selected candidate of row b: s = x + Gumbel, or x on a
 // greedy row.
 __device__ __forceinline__ uint64_t scored_key(uint32_t u, int32_t id, int b, bool greedy,
-                                               uint32_t k0, uint32_t k1, uint32_t step) {
+                                               const RowKey& rk) {
     const float x = ordered_to_float(u);
-    const float s = greedy ? x : x + token_gumbel(k0, k1, step, b, id);
+    const float s = greedy ? x : x + token_gumbel(rk.k0, rk.k1, rk.step, b, id);
     return pack_key(s, id);
 }
 
@@ -180,8 +181,8 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
 // below top_p times the set's mass are kept ("flashinfer.cake_sampling",
 // launch forms).  The noise is drawn for the kept candidates only.  Returns
 // the winning id in every lane (-1 when there is none).
-__device__ int32_t finish_topk(uint64_t key, int b, bool greedy, float top_p, uint32_t k0,
-                               uint32_t k1, uint32_t step) {
+__device__ int32_t finish_topk(uint64_t key, int b, bool greedy, float top_p,
+                               const RowKey& rk) {
     const int lane = threadIdx.x & 63;
     bool keep = key != 0ull;
     if (top_p < 1.f) {
@@ -201,14 +202,14 @@ __device__ int32_t finish_topk(uint64_t key, int b, bool greedy, float top_p, ui
     }
     uint64_t best = pack_key(-INFINITY, -1);
     if (keep)
-        best = scored_key((uint32_t)(key >> 32), (int32_t)~(uint32_t)key, b, greedy, k0, k1, step);
+        best = scored_key((uint32_t)(key >> 32), (int32_t)~(uint32_t)key, b, greedy, rk);
     return key_index(wave_max_key(best));
 }
 
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
     const float* cx, const int32_t* cidx, int G, int B, int k, float top_p, const float* temp,
-    uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
+    uint32_t flags, NoiseSrc noise, int32_t* out_idx) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             if (lane < base) key = ((uint64_t)g_u[lane] << 32) | g_tb[lane];
         }
-        const int32_t id = finish_topk(key, b, greedy, top_p, k0, k1, step);
+        const int32_t id = finish_topk(key, b, greedy, top_p, row_key(noise, b));
         if (lane == 0) out_idx[b] = id;
         return;
     }
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
     if (wave == 0) {
         const int nsel = g_n < 64 ? g_n : 64;
         const uint64_t key = lane < nsel ? ((uint64_t)g_u[lane] << 32) | g_tb[lane] : 0ull;
-        const int32_t id = finish_topk(key, b, greedy, top_p, k0, k1, step);
+        const int32_t id = finish_topk(key, b, greedy, top_p, row_key(noise, b));
         if (lane == 0) out_idx[b] = id;
     }
 }
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
 // then argmax s over the keys >= it: any number of candidates.
 __global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
     const float* cx, const int32_t* cidx, int G, int B, int k, float top_p, const float* temp,
-    uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step, int32_t* out_idx) {
+    uint32_t flags, NoiseSrc noise, int32_t* out_idx) {
     const int b = blockIdx.x;
     __shared__ uint32_t hist[256];
     __shared__ uint64_t s_prefix;
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
         const int lane = threadIdx.x;
         const uint64_t key = lane < min(nsel, 64) ? sel[lane] : 0ull;
         const int32_t id =
-            finish_topk(key, b, row_is_greedy(temp, b, flags), top_p, k0, k1, step);
+            finish_topk(key, b, row_is_greedy(temp, b, flags), top_p, row_key(noise, b));
         if (lane == 0) out_idx[b] = id;
     }
 }
@@ -506,11 +507,12 @@ __global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
 // online binary merge: one thread per row, chunks in order
 // ---------------------------------------------------------------------------
 __global__ void merge_online_kernel(int B, int C, const int32_t* z, const float* L,
-                                    const float* temp, uint32_t k0, uint32_t k1, uint32_t step,
-                                    uint32_t flags, int32_t* out_idx, float* out_L) {
+                                    const float* temp, NoiseSrc noise, uint32_t flags,
+                                    int32_t* out_idx, float* out_L) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
     const bool greedy = row_is_greedy(temp, b, flags);
+    const RowKey rk = row_key(noise, b);
     int32_t zz = C > 0 ? z[(size_t)b * C] : -1;
     float A = C > 0 ? L[(size_t)b * C] : -INFINITY;
     for (int c = 1; c < C; ++c) {
@@ -525,7 +527,7 @@ __global__ void merge_online_kernel(int B, int C, const int32_t* z, const float*
         const float A_new = hi + log1pf(expf(-fabsf(A - Lc)));   // logaddexp(A, L_c)
         const float p = expf(Lc - A_new);
         const uint4 rw = philox4x32_10(
-            make_uint4((uint32_t)c >> 2, (uint32_t)b, step, kStreamMerge), k0, k1);
+            make_uint4((uint32_t)c >> 2, (uint32_t)b, rk.step, kStreamMerge), rk.k0, rk.k1);
         const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
         const float u = uniform_from_word(words[c & 3]);
         if (u < p) zz = zc;
@@ -608,8 +610,7 @@ __global__ __launch_bounds__(kRedThreads) void multinomial_pass2(XArgs a, int ch
                                                                  const float* ws_m,
                                                                  const float* ws_s,
                                                                  const uint64_t* ws_key,
-                                                                 uint32_t k0, uint32_t k1,
-                                                                 uint32_t step,
+                                                                 NoiseSrc noise,
                                                                  int32_t* out_idx) {
     const int b = blockIdx.x;
     bool greedy;
@@ -636,8 +637,9 @@ __global__ __launch_bounds__(kRedThreads) void multinomial_pass2(XArgs a, int ch
                 const float m = ws_m[(size_t)b * nchunk + c];
                 if (m > -INFINITY) Z += ws_s[(size_t)b * nchunk + c] * __expf(m - M);
             }
+            const RowKey rk = row_key(noise, b);
             const uint4 rw =
-                philox4x32_10(make_uint4(0u, (uint32_t)b, step, kStreamMultinomial), k0, k1);
+                philox4x32_10(make_uint4(0u, (uint32_t)b, rk.step, kStreamMultinomial), rk.k0, rk.k1);
             const float target = uniform_from_word(rw.x) * Z;
             float acc = 0.f, acc_last = 0.f;
             int last = -1, sel = -1;
@@ -736,22 +738,22 @@ hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B
 
 hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
                                  int B, int T, int G, int nmb, int tile_mb, const float* temp,
-                                 uint32_t flags, uint32_t k0, uint32_t k1, uint32_t step,
-                                 float* tile_max, int32_t* tile_idx, float* tile_L,
-                                 int32_t* out_idx, hipStream_t stream) {
+                                 uint32_t flags, const NoiseSrc& noise, float* tile_max,
+                                 int32_t* tile_idx, float* tile_L, int32_t* out_idx,
+                                 hipStream_t stream) {
     hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kRedThreads), 0, stream, pm, pidx,
-                       pL, P, B, T, G, nmb, tile_mb, temp, flags, k0, k1, step, tile_max, tile_idx,
+                       pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,
                        tile_L, out_idx);
     return hipGetLastError();
 }
 
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
-                              float top_p, const float* temp, uint32_t flags, uint32_t k0,
-                              uint32_t k1, uint32_t step, int32_t* out_idx, hipStream_t stream) {
+                              float top_p, const float* temp, uint32_t flags,
+                              const NoiseSrc& noise, int32_t* out_idx, hipStream_t stream) {
 #define FS_TOPK2(PER_)                                                                       \
     if ((int64_t)G * k <= (int64_t)kTopkThreads * PER_) {                                   \
         hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \
-                           cx, cidx, G, B, k, top_p, temp, flags, k0, k1, step, out_idx);    \
+                           cx, cidx, G, B, k, top_p, temp, flags, noise, out_idx);           \
         return hipGetLastError();                                                            \
     }
     FS_TOPK2(4)
@@ -761,21 +763,21 @@ hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B
     FS_TOPK2(64)
 #undef FS_TOPK2
     hipLaunchKernelGGL(stage2_topk_radix_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cidx,
-                       G, B, k, top_p, temp, flags, k0, k1, step, out_idx);
+                       G, B, k, top_p, temp, flags, noise, out_idx);
     return hipGetLastError();
 }
 
 hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
-                               uint32_t k0, uint32_t k1, uint32_t step, uint32_t flags,
-                               int32_t* out_idx, float* out_L, hipStream_t stream) {
+                               const NoiseSrc& noise, uint32_t flags, int32_t* out_idx,
+                               float* out_L, hipStream_t stream) {
     hipLaunchKernelGGL(merge_online_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, B, C, z, L,
-                       temp, k0, k1, step, flags, out_idx, out_L);
+                       temp, noise, flags, out_idx, out_L);
     return hipGetLastError();
 }
 
 hipError_t launch_multinomial(const float* logits, const float* temp, const uint32_t* allow,
-                              int B, int V, int n_valid, int v_offset, uint32_t k0, uint32_t k1,
-                              uint32_t step, uint32_t flags, int nchunk, int chunk,
+                              int B, int V, int n_valid, int v_offset, const NoiseSrc& noise,
+                              uint32_t flags, int nchunk, int chunk,
                               float* ws_m, float* ws_s, uint64_t* ws_key, int32_t* out_idx,
                               hipStream_t stream) {
     XArgs a{logits, temp, allow, B, V, n_valid, v_offset, flags};
@@ -784,7 +786,7 @@ hipError_t launch_multinomial(const float* logits, const float* temp, const uint
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(multinomial_pass2, dim3(B), dim3(kRedThreads), 0, stream, a, chunk, nchunk,
-                       ws_m, ws_s, ws_key, k0, k1, step, out_idx);
+                       ws_m, ws_s, ws_key, noise, out_idx);
     return hipGetLastError();
 }
 

@@ -129,10 +129,12 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
     // context is rebuilt in the epilogue without memory reads
     float inv_t[NF];
     uint64_t best[NF];
+    RowKey key[NF];
 #pragma unroll
     for (int n = 0; n < NF; ++n) {
         const ColCtx c = col_ctx(a, bbase + wn * (NT / WN) + n * 16 + r16);
         inv_t[n] = c.greedy ? 0.f : c.inv_t;   // 0 marks a greedy column
+        key[n] = c.key;
         best[n] = pack_key(-INFINITY, -1);
     }
     Lse unused = lse_empty();
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
                     cx.inv_t = cx.greedy ? 1.f : inv_t[n];
                     cx.allow_row = (a.allow && cx.ok)
                                        ? a.allow + (size_t)cx.col * ((a.V + 31) >> 5) : nullptr;
+                    cx.key = key[n];
                     if constexpr (VAR == kVarLogits) {
                         if (cx.ok) {
                             float* dst = a.logits + (size_t)cx.col * a.V;

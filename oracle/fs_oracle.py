@@ -39,6 +39,9 @@ What is computed (all in float64; every helper is a direct definition):
                 set's mass, then argmax s over the kept prefix     [FS-kr top-p; CAKE]
   multinomial   inverse CDF of softmax(x) at a stream-3 uniform    [FS-kr problem statement]
 
+Every function taking `seed` also accepts one seed per batch row (a
+length-B sequence): row b then draws all its noise under key seed[b].
+
 Readings taken where the pages leave a step open (each is listed in the design doc):
   * Temperature divides the logit before the noise is added (x/T + g) as the
     Stage 1 paragraph orders it; the x + T*g form of [GMX] picks the same id.
@@ -62,6 +65,14 @@ import numpy as np
 from . import philox as px
 
 NO_NOISE = 1          # flag bit: seed-less operation, every row greedy [GMX]
+
+
+def row_seed(seed, b):
+    """The Philox seed of batch row b: `seed` itself, or seed[b] when one seed
+    per row is given (per-request seeds, as a serving engine would pass)."""
+    if np.ndim(seed) == 0:
+        return int(seed)
+    return int(np.asarray(seed, dtype=np.uint64)[b])
 NEG_INF = -np.inf
 TWO_M32 = 2.0 ** -32
 
@@ -151,7 +162,7 @@ def token_noise(seed, step, B, V, id0=0):
     ids = id0 + np.arange(V, dtype=np.int64)
     g = np.empty((B, V), np.float64)
     for b in range(B):
-        g[b] = gumbel_from_word(px.noise_words(seed, b, ids, step, px.STREAM_TOKEN))
+        g[b] = gumbel_from_word(px.noise_words(row_seed(seed, b), b, ids, step, px.STREAM_TOKEN))
     return g
 
 
@@ -254,7 +265,7 @@ def group_noise(seed, step, B, T):
     G = np.empty((B, T), np.float64)
     ts = np.arange(T, dtype=np.int64)
     for b in range(B):
-        G[b] = gumbel_from_word(px.noise_words(seed, b, ts, step, px.STREAM_GROUP))
+        G[b] = gumbel_from_word(px.noise_words(row_seed(seed, b), b, ts, step, px.STREAM_GROUP))
     return G
 
 
@@ -302,7 +313,7 @@ def online_merge(z, L, temp=None, seed=0, step=0, flags=0):
     margin = np.full(B, math.inf)
     cs = np.arange(C, dtype=np.int64)
     for b in range(B):
-        u_all = uniform_from_word(px.noise_words(seed, b, cs, step, px.STREAM_MERGE))
+        u_all = uniform_from_word(px.noise_words(row_seed(seed, b), b, cs, step, px.STREAM_MERGE))
         for c in range(1, C):
             Lc = L[b, c]
             if greedy[b]:
@@ -416,7 +427,7 @@ def multinomial(x, temp=None, seed=0, step=0, flags=0, id0=0):
             continue
         p = np.exp(x[b] - lse)
         cdf = np.cumsum(p)
-        u = float(uniform_from_word(px.noise_words(seed, b, np.array([0]), step,
+        u = float(uniform_from_word(px.noise_words(row_seed(seed, b), b, np.array([0]), step,
                                                    px.STREAM_MULTINOMIAL))[0])
         j = int(np.searchsorted(cdf, u, side="right"))
         if j >= V:                       # u beyond the rounded total: last valid id

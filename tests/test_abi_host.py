@@ -48,8 +48,9 @@ def test_status_strings_and_version():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(fs.fs_params) == 40
+    assert ctypes.sizeof(fs.fs_params) == 56
     assert fs.fs_params.seed.offset == 24
+    assert fs.fs_params.seeds.offset == 40 and fs.fs_params.step_ptr.offset == 48
 
 
 def test_num_tiles():

@@ -445,3 +445,27 @@ def test_planted_mistake_is_caught(name):
     with np.errstate(all="ignore"):
         with pytest.raises((AssertionError, ValueError, IndexError)):
             MUTANTS[name](mod)
+
+
+def test_per_row_seeds_select_each_rows_key():
+    """One seed per row: row b's noise in every stream is the noise that the
+    single seed seeds[b] gives that row (keys are per row, counters unchanged)."""
+    seeds = np.array([7, 2 ** 40 + 3, 7, 0], dtype=np.uint64)
+    B, V, T = 4, 37, 6
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(B, V))
+    g = O.token_noise(seeds, 5, B, V)
+    G = O.group_noise(seeds, 5, B, T)
+    s_rows = O.scores(x, None, seeds, 5)
+    z = rng.integers(0, V, size=(B, T))
+    L = rng.normal(size=(B, T))
+    zm, Am, _ = O.online_merge(z, L, None, seeds, 5)
+    mi, _ = O.multinomial(x, None, seeds, 5)
+    for b in range(B):
+        sb = int(seeds[b])
+        assert np.array_equal(g[b], O.token_noise(sb, 5, B, V)[b])
+        assert np.array_equal(G[b], O.group_noise(sb, 5, B, T)[b])
+        assert np.array_equal(s_rows[b], O.scores(x, None, sb, 5)[b])
+        assert zm[b] == O.online_merge(z, L, None, sb, 5)[0][b]
+        assert mi[b] == O.multinomial(x, None, sb, 5)[0][b]
+    assert not np.array_equal(g[0], g[1]) and np.array_equal(g[0][:0], g[2][:0])
