@@ -266,6 +266,23 @@ def bench_workloads(torch, fs, steps, W_head):
                 fs.check(fs.fs_sample_topk_topp(p, H, W, temp, None, wl.k, 0.9, idx, kws), name)
 
             line(name, wl, f"top-{wl.k} then top-p 0.9 fs_sample_topk_topp", timed(topp))
+            # the pages' largest benchmarked k
+            kl = 1000
+            lws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, kl),
+                              dtype=torch.uint8, device="cuda")
+
+            def topk_l(i):
+                p.step = i
+                fs.check(fs.fs_sample_topk(p, H, W, temp, None, kl, idx, lws), name)
+
+            line(name, wl, f"top-{kl} fs_sample_topk", timed(topk_l))
+
+            def topp_l(i):
+                p.step = i
+                fs.check(fs.fs_sample_topk_topp(p, H, W, temp, None, kl, 0.9, idx, lws), name)
+
+            line(name, wl, f"top-{kl} then top-p 0.9 fs_sample_topk_topp", timed(topp_l))
+            del lws
             chunk = wl.V // wl.chunks
             pc = fs.params(wl.B, wl.d, wl.V, tile_v=chunk, seed=SEED)
             C = fs.fs_num_tiles(pc)

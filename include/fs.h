@@ -166,7 +166,11 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
 /* fs_sample_topk -- top-k restricted sample (FlashSampling explainer,
  * implementation paragraph: the tile scheme extends to top-k).  S_b = the k
  * valid ids with the largest x (lowest id on ties; every valid id when fewer
- * than k); out_idx[b] = argmax over S_b of s.  1 <= k <= 64.
+ * than k); out_idx[b] = argmax over S_b of s.  1 <= k <= 1024 (else
+ * FS_ERR_INVALID_ARG below 1, FS_ERR_UNSUPPORTED above).  k > 64 needs the
+ * register-resident stage-1 kernel: ceil(d / 32) * 32 one of 512, 1024, 2048,
+ * 4096 or 5120; other hidden sizes return FS_ERR_UNSUPPORTED for such k, and
+ * fs_workspace_bytes returns 0 for them.
  * ws: fs_workspace_bytes(p, FS_VARIANT_TOPK, k) bytes. */
 fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const float* temp,
                          const uint32_t* allow, int32_t k, int32_t* out_idx,
@@ -180,7 +184,8 @@ fs_status fs_sample_topk(const fs_params* p, const void* H, const void* W, const
  * order is kept when the mass of the elements before it is below top_p
  * (computed in float64 from the FP32 x); out_idx[b] = argmax over the kept
  * elements of s.  0 < top_p <= 1 (else FS_ERR_INVALID_ARG); top_p = 1 gives
- * fs_sample_topk's result.  1 <= k <= 64.  Same workspace as fs_sample_topk. */
+ * fs_sample_topk's result.  k as for fs_sample_topk.  Same workspace as
+ * fs_sample_topk. */
 fs_status fs_sample_topk_topp(const fs_params* p, const void* H, const void* W, const float* temp,
                               const uint32_t* allow, int32_t k, float top_p, int32_t* out_idx,
                               void* ws, size_t ws_bytes, void* stream);

@@ -17,7 +17,8 @@ namespace {
 using namespace fs;
 
 constexpr int kDefaultTileV = 128;
-constexpr int kMaxTopK = 64;
+constexpr int kMaxTopK = 1024;
+constexpr int kMaxTopKCoop = 64;   // the cooperative kernel keeps sorted lists of at most 64
 constexpr int kMultinomialChunk = 2048;
 constexpr int kMaxB = 1 << 20;
 constexpr size_t kAlign = 256;
@@ -261,12 +262,29 @@ struct Workspace {
     float* ms = nullptr;
     uint64_t* mkey = nullptr;
     void* part = nullptr;   // streaming stage 1: parked partial sums of split blocks
+    void* sel = nullptr;    // top-k: lists of the intermediate selection levels
 };
 
 // Partial sums parked by the streaming kernel: per y-block, worker and side
 // (head, tail), nb 16x16 FP32 tiles.
 size_t part_bytes(const Plan& pl) {
     return (size_t)pl.grid_y * (4 * pl.G) * 2 * pl.cfg.nb * 1024;
+}
+
+// Entries per top-k candidate list: a range of the resident kernel holds at
+// most ceil(nmb / G) blocks, so a list never needs more than its rows.
+int topk_len(const Plan& pl, int k) {
+    if (pl.kind != kResident) return k;
+    const int64_t rows = (int64_t)((pl.nmb + pl.G - 1) / pl.G) * kMBlock;
+    return (int)std::min<int64_t>(k, rows);
+}
+
+// Dense lists: for k above 64 that reaches every row of the longest range,
+// stage 1 writes the x of each whole range in row order and no ids (the
+// selection happens in stage 2 alone).
+bool topk_dense(const Plan& pl, int k) {
+    return pl.kind == kResident && k > kMaxTopKCoop &&
+           (int64_t)k >= (int64_t)((pl.nmb + pl.G - 1) / pl.G) * kMBlock;
 }
 
 size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
@@ -285,10 +303,14 @@ size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
         char* d = pl.stream ? take(part_bytes(pl)) : nullptr;
         if (w) { w->pm = (float*)a; w->pidx = (int32_t*)b; w->pL = (float*)c; w->part = d; }
     } else if (variant == FS_VARIANT_TOPK) {
-        const size_t n = (size_t)pl.G * B * (size_t)k;
+        const int L = topk_len(pl, k);
+        const bool dense = topk_dense(pl, k);
+        const size_t n = (size_t)pl.G * B * (size_t)L;
         char* a = take(n * 4);
-        char* c = take(n * 4);
-        if (w) { w->cx = (float*)a; w->cidx = (int32_t*)c; }
+        char* c = dense ? nullptr : take(n * 4);
+        const size_t sb = stage2_topk_scratch_bytes(pl.G, L, pl.B, k, dense);
+        char* d = sb ? take(sb) : nullptr;
+        if (w) { w->cx = (float*)a; w->cidx = (int32_t*)c; w->sel = d; }
     } else if (variant == FS_VARIANT_LOGITS) {
         char* a = pl.stream ? take(part_bytes(pl)) : nullptr;
         if (w) w->part = a;
@@ -356,19 +378,23 @@ fs_status sample_topk(const fs_params* p, const void* H, const void* W, const fl
     if (p->V == 0) return from_hip(launch_fill_idx(out_idx, p->B, -1, nullptr, s));
     Plan pl;
     make_plan(p, kVarTopk, dev.cus, pl);
+    if (pl.kind != kResident && k > kMaxTopKCoop) return FS_ERR_UNSUPPORTED;
     Workspace w;
     const size_t need = layout(FS_VARIANT_TOPK, pl, k, nullptr, nullptr);
     if (!ws || ws_bytes < need) return FS_ERR_WORKSPACE;
     layout(FS_VARIANT_TOPK, pl, k, static_cast<char*>(ws), &w);
     Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
     a.topk = k;
+    a.topk_len = topk_len(pl, k);
+    a.topk_dense = topk_dense(pl, k) ? 1 : 0;
     a.cx = w.cx;
     a.cidx = w.cidx;
     hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
                                         : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
-    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, pl.B, k, top_p, temp, p->flags,
-                                       noise_src(pl, p), out_idx, s));
+    const DenseIds dn{a.topk_dense ? pl.nmb : 0, pl.G, pl.v_offset};
+    return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, a.topk_len, pl.B, k, dn, top_p, temp,
+                                       p->flags, noise_src(pl, p), out_idx, w.sel, s));
 }
 
 }  // namespace
@@ -406,6 +432,7 @@ size_t fs_workspace_bytes(const fs_params* p, int variant, int32_t k) {
                  : variant == FS_VARIANT_LOGITS ? kVarLogits
                                                 : kVarFlat,
               dev.cus, pl);
+    if (variant == FS_VARIANT_TOPK && pl.kind != kResident && k > kMaxTopKCoop) return 0;
     return std::max(kAlign, layout(variant, pl, k, nullptr, nullptr));
 }
 

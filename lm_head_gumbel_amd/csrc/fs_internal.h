@@ -61,6 +61,8 @@ struct Stage1Args {
     NoiseSrc noise;         // Philox key and step (per row when given)
     uint32_t flags;
     int topk;               // k of the top-k variant
+    int topk_len;           // entries per candidate list: min(k, rows of the longest range)
+    int topk_dense;         // lists are whole ranges: every row's x in row order, no ids
     int ny;                 // resident kernel: batch groups sharing one row range
     int xcd_pair;           // resident kernel: 1-D grid, groups of a range on one XCD
     // partial records [B][P] (P slots per row: the workers for flat, workers
@@ -69,7 +71,8 @@ struct Stage1Args {
     float* pm;
     int32_t* pidx;
     float* pL;
-    // top-k candidates [G][B][k]: tempered logit and id
+    // top-k candidates [B][G][topk_len] (row-major: a row's lists are one
+    // contiguous run): tempered logit and id
     float* cx;
     int32_t* cidx;
     // unfused baseline output [B, V]
@@ -129,10 +132,21 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                                  float* tile_max, int32_t* tile_idx, float* tile_L,
                                  int32_t* out_idx, hipStream_t stream);
 
-// top_p >= 1: plain top-k; 0 < top_p < 1: top-p after top-k.
-hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
-                              float top_p, const float* temp, uint32_t flags,
-                              const NoiseSrc& noise, int32_t* out_idx, hipStream_t stream);
+// Candidates [B][G][L] (L entries per list); 1 <= k <= 1024.  With
+// dn.nmb > 0 the lists are dense: list w holds the x of every row of
+// workgroup range w in row order (padded with -inf) and cidx is not read;
+// entry r is id dn.v_offset + 16 part_begin(w, dn.nmb, G) + r.  top_p >= 1:
+// plain top-k; 0 < top_p < 1: top-p after top-k.  scratch: device memory of
+// stage2_topk_scratch_bytes(G, L, B, k, dense) bytes (256-byte aligned; may be null
+// when that is 0) for the lists of the intermediate selection levels.
+struct DenseIds {
+    int nmb, G, v_offset;   // nmb > 0: dense lists, see launch_stage2_topk
+};
+size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense);
+hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,
+                              DenseIds dn, float top_p, const float* temp, uint32_t flags,
+                              const NoiseSrc& noise, int32_t* out_idx, void* scratch,
+                              hipStream_t stream);
 
 hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
                                const NoiseSrc& noise, uint32_t flags,

@@ -314,11 +314,15 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             const bool ok = cl < 16 * NB && bbase + cl < a.B;
             nc += ok ? 1 : 0;   // valid columns come first
             xc[q] = tk.x[ok ? cl : wave];
-            o[q] = ((size_t)w * a.B + bbase + (ok ? cl : 0)) * a.topk;
+            o[q] = ((size_t)(bbase + (ok ? cl : 0)) * a.G + w) * a.topk_len;
         }
-        if (nc > 0)
-            topk_select_columns<C, TopkRows<NB, HL>::kRows / 64>(a, nc, xc, (mb1 - mb0) * kMBlock,
-                                                             a.v_offset + mb0 * kMBlock, o);
+        if (nc > 0) {
+            if (a.topk_dense)
+                topk_write_dense<C>(a, nc, xc, (mb1 - mb0) * kMBlock, o);
+            else
+                topk_select_columns<C, TopkRows<NB, HL>::kRows / 64>(
+                    a, nc, xc, (mb1 - mb0) * kMBlock, a.v_offset + mb0 * kMBlock, o);
+        }
     }
 }
 

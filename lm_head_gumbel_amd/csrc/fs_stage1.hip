@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
             const int b = bbase + c;
             if (b >= a.B) continue;
             const uint64_t k = tk.key[c][r];
-            const size_t o = ((size_t)w * a.B + b) * a.topk + r;
+            const size_t o = ((size_t)b * a.G + w) * a.topk_len + r;   // topk_len == topk here
             const bool live = k != 0ull;
             a.cx[o] = live ? key_score(k) : -INFINITY;
             a.cidx[o] = live ? key_index(k) : -1;

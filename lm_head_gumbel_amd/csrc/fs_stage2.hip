@@ -103,20 +103,20 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// top-k: candidates [G][B][k] (x, id) from stage 1, one list per workgroup
+// top-k: candidates [B][G][L] (x, id) from stage 1, one list per workgroup
 // (unused entries have id -1).  The row's k largest (x, -id) over all lists
 // are selected exactly; optionally only the top-p prefix of them is kept;
 // the noise s = x + Gumbel is drawn for the kept only and the largest s wins.
 //
-// stage2_topk_kernel: one workgroup of 512 threads per row holds the G*k
-// candidates in registers (PER per thread).  A lower bound
-// prunes the candidates: in each wave the k-th largest of the 64 lane maxima
-// is at most the row's k-th largest x, and so is the largest of these wave
-// bounds.  The few candidates that reach it are gathered in LDS and one wave
-// selects among them (a bound once more, from the lanes' two largest, then
-// an exact bitwise search with ties to the lower id).  When too many reach it, the whole block runs
-// the exact search on all candidates.  More than 512 * 64 candidates use the
-// radix-select kernel below.
+// stage2_topk_kernel (k <= 64): one workgroup of 512 threads per row holds
+// the G*L candidates in registers (PER per thread).  A lower bound prunes
+// the candidates: in each wave the k-th largest of the 64 lane maxima is at
+// most the row's k-th largest x, and so is the largest of these wave bounds.
+// The few candidates that reach it are gathered in LDS and one wave selects
+// among them (a bound once more, from the lanes' two largest, then an exact
+// bitwise search with ties to the lower id).  When too many reach it, the
+// whole block runs the exact search on all candidates.  Larger k, or more
+// than 512 * 64 candidates, take the sliced selection below.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
@@ -208,8 +208,8 @@ __device__ int32_t finish_topk(uint64_t key, int b, bool greedy, float top_p,
 
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
-    const float* cx, const int32_t* cidx, int G, int B, int k, float top_p, const float* temp,
-    uint32_t flags, NoiseSrc noise, int32_t* out_idx) {
+    const float* cx, const int32_t* cidx, int G, int L, int B, int k, float top_p,
+    const float* temp, uint32_t flags, NoiseSrc noise, int32_t* out_idx) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -220,32 +220,24 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
     __shared__ uint32_t g_tb[kTopkGather];
     __shared__ int g_n;
     int parity = 0;
-    // candidate e = threadIdx.x + 512 * i is entry e % k of list e / k; the
-    // (list, entry) pair advances by (512 / k, 512 % k) per i.  Every
-    // candidate is loaded up front, unconditionally (slots past the end
-    // re-read candidate 0 and are then ignored), so the loads of a thread are
-    // all in flight together.
-    const int n = G * k;
-    const int dq = kTopkThreads / k, dr = kTopkThreads % k;
-    int lw = threadIdx.x / k, lr = threadIdx.x % k;
+    // candidate e = threadIdx.x + 512 * i of the row's G * L (its lists are
+    // contiguous).  Every candidate is loaded up front, unconditionally
+    // (slots past the end re-read candidate 0 and are then ignored), so the
+    // loads of a thread are all in flight together.
+    const int n = G * L;
+    const size_t row = (size_t)b * n;
     uint32_t u[PER];
     int32_t iv[PER];
     uint32_t lmax = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const bool ok = threadIdx.x + kTopkThreads * i < n;
-        const size_t o = ok ? ((size_t)lw * B + b) * k + lr : (size_t)b * k;
+        const size_t o = row + (ok ? threadIdx.x + kTopkThreads * i : 0);
         const int32_t id = cidx[o];
         const float xv = cx[o];
         iv[i] = ok ? id : -1;
         u[i] = iv[i] >= 0 ? topk_order(xv) : 0u;
         lmax = u[i] > lmax ? u[i] : lmax;
-        lw += dq;
-        lr += dr;
-        if (lr >= k) {
-            lr -= k;
-            ++lw;
-        }
     }
 
     // lower bound and gathering of the candidates that reach it
@@ -416,90 +408,391 @@ __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
     }
 }
 
-// Radix select of the k-th largest packed (x, id) key over the row's G*k
-// candidates (8 passes of 8 bits, candidates re-read from memory each pass),
-// then argmax s over the keys >= it: any number of candidates.
-__global__ __launch_bounds__(kRedThreads) void stage2_topk_radix_kernel(
-    const float* cx, const int32_t* cidx, int G, int B, int k, float top_p, const float* temp,
-    uint32_t flags, NoiseSrc noise, int32_t* out_idx) {
-    const int b = blockIdx.x;
-    __shared__ uint32_t hist[256];
-    __shared__ uint64_t s_prefix;
-    __shared__ int s_need;
-    const int n = G * k;
-    auto cand_key = [&](int e, uint64_t& key) -> bool {
-        const int w = e / k, r = e % k;
-        const size_t o = ((size_t)w * B + b) * k + r;
-        const int32_t id = cidx[o];
-        if (id < 0) return false;
-        key = pack_key(cx[o], id);
-        return true;
-    };
-    // count valid candidates
-    uint32_t cnt = 0;
-    for (int e = threadIdx.x; e < n; e += kRedThreads) {
-        uint64_t key;
-        cnt += cand_key(e, key) ? 1u : 0u;
-    }
-    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
-    if (threadIdx.x == 0) { s_prefix = 0; s_need = 0; }
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) atomicAdd(&s_need, (int)cnt);
-    __syncthreads();
-    const int total = s_need;
-    __syncthreads();
-    uint64_t thresh = 0;   // keep keys >= thresh
-    if (total > k) {
-        // find the k-th largest key, digit by digit from the top
-        uint64_t prefix = 0;
-        int need = k;
-        for (int pass = 0; pass < 8; ++pass) {
-            const int shift = 56 - 8 * pass;
-            for (int i = threadIdx.x; i < 256; i += kRedThreads) hist[i] = 0;
-            __syncthreads();
-            const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
-            for (int e = threadIdx.x; e < n; e += kRedThreads) {
-                uint64_t key;
-                if (cand_key(e, key) && (key & hi_mask) == prefix)
-                    atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
-            }
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                int acc = 0;
-                int digit = 255;
-                for (; digit > 0; --digit) {
-                    if (acc + (int)hist[digit] >= need) break;
-                    acc += hist[digit];
+// ---------------------------------------------------------------------------
+// Large-k selection: any k up to kMaxK over any number of candidates.  The
+// row's candidates (G lists of L entries) are cut into slices of at most
+// kSliceCap; one workgroup of 1024 threads per (slice, row) holds its slice
+// in registers and selects the slice's k largest (x, ~id) keys exactly, writing
+// them as a new list; the S new lists per row are selected from again until
+// one workgroup holds the whole row, which selects, applies the optional
+// top-p cut and draws.  (The k largest of a row are among the k largest of
+// every part that holds them.)
+//
+// Selection of one slice: the range [min, max] of its valid x is cut into
+// kBins equal-width bins (monotone in x) and counted; the bin where the count
+// from the top first reaches k is the tie bin.  Entries of higher bins are
+// selected outright; the tie bin's entries are sorted by key in LDS and the
+// first (k - above) of them complete the selection.  The top of a logit
+// distribution is sparse, so the tie bin usually holds few entries; when it
+// holds more than kTieCap (many equal x), an exact radix search over the tie
+// bin's keys (eight passes of eight bits) finds the cut instead.  A slice
+// with at most k valid entries keeps them all.  With top-p the finishing
+// workgroup sorts its selection, keeps the prefix whose exclusive mass
+// (float64) is below top_p times the selection's mass, and draws.
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kMaxK = kSelThreads;   // the finish holds one selected entry per thread
+constexpr int kSelPer = 16;          // candidates per thread, in registers
+constexpr int kSliceCap = kSelThreads * kSelPer;   // candidates per workgroup
+constexpr int kBins = 2048;          // two per thread
+constexpr int kTieCap = 4096;
+
+// Block-wide bitonic sort of keys[0, N) in LDS, N a power of two, descending.
+__device__ __forceinline__ void block_sort_desc(uint64_t* keys, int N) {
+    for (int size = 2; size <= N; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int p = threadIdx.x; p < N / 2; p += kSelThreads) {
+                const int i = 2 * p - (p & (stride - 1));
+                const int j = i + stride;
+                const bool desc = (i & size) == 0;
+                const uint64_t ki = keys[i], kj = keys[j];
+                if ((ki < kj) == desc) {
+                    keys[i] = kj;
+                    keys[j] = ki;
                 }
-                s_prefix = prefix | ((uint64_t)digit << shift);
-                s_need = need - acc;
             }
             __syncthreads();
-            prefix = s_prefix;
-            need = s_need;
+        }
+}
+
+// Pads keys[n, N) with 0 (N the next power of two) and sorts keys[0, N).
+__device__ __forceinline__ void block_sort_prefix(uint64_t* keys, int n) {
+    int N = 1;
+    while (N < n) N <<= 1;
+    for (int i = n + threadIdx.x; i < N; i += kSelThreads) keys[i] = 0ull;
+    __syncthreads();
+    block_sort_desc(keys, N);
+}
+
+// Inclusive and exclusive prefix sums of v over the threads of the block, in
+// thread order (slot: one entry per wave).  Ends with a barrier.
+template <typename T>
+__device__ __forceinline__ void block_scan(T v, T* slot, T& incl, T& excl) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T s = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const T o = __shfl_up(s, off, 64);
+        if (lane >= off) s += o;
+    }
+    T e = __shfl_up(s, 1, 64);
+    if (lane == 0) e = T(0);
+    if (lane == 63) slot[wave] = s;
+    __syncthreads();
+    T before = T(0);
+#pragma unroll
+    for (int i = 0; i < kSelWaves - 1; ++i) before += i < wave ? slot[i] : T(0);
+    __syncthreads();
+    incl = before + s;
+    excl = before + e;
+}
+
+struct SelSmem {
+    uint64_t gk[kMaxK];        // the selection
+    uint64_t tk[kTieCap];      // the tie bin's keys
+    uint32_t hist[kBins];
+    int wbase[kSliceCap / 16 + 2];   // dense lists: first id of each list of the slice
+    int islot[kSelWaves];
+    double dslot[kSelWaves];
+    uint64_t kslot[kSelWaves];
+    uint32_t mn, mx;
+    int cnt, bin, above, need;
+    uint64_t prefix;
+    double total;
+};
+
+// Slice blockIdx.x of row blockIdx.y: candidates e in [e0, e0 + n) of the
+// row's G lists of L entries (candidate e is entry e % L of list e / L, at
+// offset b * G * L + e: a row's lists are contiguous); thread t holds entries
+// t + 1024 j in registers.  DENSE: the lists are whole vocabulary ranges in
+// row order and carry no ids (entry r of list w is id v_offset + 16
+// part_begin(w, nmb, G) + r).  FINISH == false: writes the slice's selection
+// as list blockIdx.x of length k of ox / oidx ([B][S][k], padding (-inf,
+// -1)).  FINISH == true (one slice): the draw, to out_idx[b].
+template <bool FINISH, bool DENSE>
+__global__ __launch_bounds__(kSelThreads) void stage2_topk_select_kernel(
+    const float* cx, const int32_t* cidx, int G, int L, int B, int k, int per_slice,
+    DenseIds dn, float* ox, int32_t* oidx, float top_p, const float* temp, uint32_t flags,
+    NoiseSrc noise, int32_t* out_idx) {
+    __shared__ SelSmem sm;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int e0 = blockIdx.x * per_slice;
+    const int n = min(per_slice, G * L - e0);   // 1 .. kSliceCap by the launch
+    if (threadIdx.x == 0) {
+        sm.mn = 0xFFFFFFFFu;
+        sm.mx = 0u;
+        sm.cnt = 0;
+    }
+    for (int i = threadIdx.x; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
+    if constexpr (DENSE) {
+        // the first id of each list the slice touches
+        const int nw = (e0 + n - 1) / L - e0 / L + 1;
+        for (int i = threadIdx.x; i < nw; i += kSelThreads)
+            sm.wbase[i] = dn.v_offset + part_begin(e0 / L + i, dn.nmb, dn.G) * kMBlock;
+        __syncthreads();
+    }
+
+    // the slice into registers.  The loads are unconditional (slots past the
+    // slice re-read its first entry and are then dropped), so that all of
+    // them are in flight together.  x = -inf: no candidate.
+    float x[kSelPer];
+    int32_t id[DENSE ? 1 : kSelPer];   // dense lists: ids from sm.wbase
+    {
+        const float* xs = cx + (size_t)b * G * L + e0;
+        const int32_t* is = cidx + (size_t)b * G * L + e0;
+#pragma unroll
+        for (int j = 0; j < kSelPer; ++j) {
+            const int i = j * kSelThreads + (int)threadIdx.x;
+            const bool ok = i < n;
+            const float xv = xs[ok ? i : 0];
+            x[j] = ok ? xv : -INFINITY;
+            if constexpr (!DENSE) {
+                const int32_t iv = is[ok ? i : 0];
+                id[j] = ok ? iv : -1;
+            }
+        }
+    }
+    // (list, entry) of entry j: steps of (1024 / L, 1024 % L) from the first
+    const int dq = kSelThreads / L, dr = kSelThreads % L;
+    const int w_lo = e0 / L;
+    const int w_start = (e0 + (int)threadIdx.x) / L;
+    const int r_start = e0 + (int)threadIdx.x - w_start * L;
+    // Visits this thread's entries in order: fn(j, id_of), id_of() giving
+    // the id of entry j (for dense lists the list's first id plus the
+    // position, with (list, entry) stepped along, so that it is only read
+    // where it is used).
+    auto walk = [&](auto fn) {
+        int w = w_start, r = r_start;
+        if constexpr (DENSE) {
+            // a fresh copy per walk: the steps are recomputed, not kept live
+            // in registers across the kernel
+            asm volatile("" : "+v"(w), "+v"(r));
+        }
+#pragma unroll
+        for (int j = 0; j < kSelPer; ++j) {
+            auto id_of = [&]() -> int32_t {
+                if constexpr (DENSE)
+                    return sm.wbase[w - w_lo] + r;
+                else
+                    return id[j];
+            };
+            fn(j, id_of);
+            w += dq;
+            r += dr;
+            if (r >= L) {
+                r -= L;
+                ++w;
+            }
+        }
+    };
+    // Writes the keys of the entries where pred(j, id_of) holds to
+    // dst[base, ...) in thread order: a block scan of the per-thread counts
+    // gives each thread its first position.  Positions >= cap are dropped.
+    // The caller synchronises before reading dst.
+    auto compact = [&](auto pred, uint64_t* dst, int base, int cap) {
+        int c = 0;
+        walk([&](int j, auto id_of) { c += pred(j, id_of) ? 1 : 0; });
+        int incl, excl;
+        block_scan(c, sm.islot, incl, excl);
+        int pos = base + excl;
+        walk([&](int j, auto id_of) {
+            if (pred(j, id_of)) {
+                if (pos < cap) dst[pos] = pack_key(x[j], id_of());
+                ++pos;
+            }
+        });
+    };
+
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+        if (x[j] > -INFINITY) {
+            const uint32_t u = float_to_ordered(x[j]);
+            mn = u < mn ? u : mn;
+            mx = u > mx ? u : mx;
+            ++cnt;
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint32_t a1 = __shfl_xor(mn, m, 64), a2 = __shfl_xor(mx, m, 64);
+        mn = a1 < mn ? a1 : mn;
+        mx = a2 > mx ? a2 : mx;
+        cnt += __shfl_xor(cnt, m, 64);
+    }
+    __syncthreads();   // the counters are set
+    if (lane == 0 && cnt > 0) {
+        atomicMin(&sm.mn, mn);
+        atomicMax(&sm.mx, mx);
+        atomicAdd(&sm.cnt, cnt);
+    }
+    __syncthreads();
+    const int total = sm.cnt;
+    const int nsel = total < k ? total : k;   // the selection is gk[0, nsel)
+
+    if (total <= k) {
+        compact([&](int j, auto) { return x[j] > -INFINITY; }, sm.gk, 0, kMaxK);
+        __syncthreads();
+    } else {
+        const float fmin = ordered_to_float(sm.mn), fmax = ordered_to_float(sm.mx);
+        const float scale = fmax > fmin ? (float)kBins / (fmax - fmin) : 0.f;
+        // bin of entry j (-1: none); monotone in x, and a NaN (inf * 0 when
+        // the range overflows) lands in bin 0
+        auto bin_at = [&](int j) {
+            const float t = fminf(fmaxf((x[j] - fmin) * scale, 0.f), (float)(kBins - 1));
+            return x[j] > -INFINITY ? (int)t : -1;
+        };
+#pragma unroll
+        for (int j = 0; j < kSelPer; ++j) {
+            const int bn = bin_at(j);
+            if (bn >= 0) atomicAdd(&sm.hist[bn], 1u);
+        }
+        __syncthreads();
+        {
+            // counts from the top bin down: thread t owns bins kBins - 1 - 2t
+            // and kBins - 2 - 2t; exactly one thread holds the bin where the
+            // running count first reaches k
+            const int hb = kBins - 1 - 2 * (int)threadIdx.x;
+            const int c = (int)sm.hist[hb] + (int)sm.hist[hb - 1];
+            int incl, excl;
+            block_scan(c, sm.islot, incl, excl);
+            if (excl < k && incl >= k) {
+                const bool upper = excl + (int)sm.hist[hb] >= k;
+                sm.bin = upper ? hb : hb - 1;
+                sm.above = upper ? excl : excl + (int)sm.hist[hb];   // in bins above the tie bin
+            }
             __syncthreads();
         }
-        thresh = prefix;   // keys are distinct, so exactly k keys are >= prefix
-    }
-    // gather the (at most k) selected keys, then one wave finishes
-    __shared__ uint64_t sel[64];
-    __shared__ int nsel;
-    if (threadIdx.x == 0) nsel = 0;
-    __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kRedThreads) {
-        uint64_t key;
-        if (cand_key(e, key) && key >= thresh) {
-            const int pos = atomicAdd(&nsel, 1);
-            if (pos < 64) sel[pos] = key;
+        const int bk = sm.bin, above = sm.above;
+        const int need = k - above;   // 1 .. entries of the tie bin
+        const int ntie = (int)sm.hist[bk];
+        if (ntie <= kTieCap) {
+            // entries above the tie bin are selected, the tie bin's gathered:
+            // one scan of both counts (16 bits each)
+            int ch = 0, ct = 0;
+#pragma unroll
+            for (int j = 0; j < kSelPer; ++j) {
+                const int bn = bin_at(j);
+                ch += bn > bk ? 1 : 0;
+                ct += bn == bk ? 1 : 0;
+            }
+            int incl, excl;
+            block_scan(ch | (ct << 16), sm.islot, incl, excl);
+            int ph = excl & 0xFFFF, pt = excl >> 16;
+            walk([&](int j, auto id_of) {
+                const int bn = bin_at(j);
+                if (bn > bk) sm.gk[ph++] = pack_key(x[j], id_of());
+                if (bn == bk) sm.tk[pt++] = pack_key(x[j], id_of());
+            });
+            __syncthreads();
+            if (ntie > need) {
+                if (ntie <= 64) {
+                    if (threadIdx.x < 64) {   // one wave sorts the few ties
+                        const uint64_t key = wave_sort_desc(lane < ntie ? sm.tk[lane] : 0ull);
+                        if (lane < need) sm.gk[above + lane] = key;
+                    }
+                } else {
+                    block_sort_prefix(sm.tk, ntie);
+                    for (int i = threadIdx.x; i < need; i += kSelThreads)
+                        sm.gk[above + i] = sm.tk[i];
+                }
+            } else {
+                for (int i = threadIdx.x; i < need; i += kSelThreads) sm.gk[above + i] = sm.tk[i];
+            }
+            __syncthreads();
+        } else {
+            compact([&](int j, auto) { return bin_at(j) > bk; }, sm.gk, 0, kMaxK);
+            // exact radix search for the need-th largest (x, ~id) key of the
+            // tie bin, eight bits at a time from the top: first the order
+            // image u of x, then ~id among the entries at that u; thread
+            // t < 256 owns digit 255 - t
+            uint32_t ucut = 0u, tcut = 0u;
+            int left = need;
+            for (int pass = 0; pass < 8; ++pass) {
+                const bool on_id = pass >= 4;
+                const int shift = 24 - 8 * (pass & 3);
+                const uint32_t hi_mask = (pass & 3) == 0 ? 0u : (~0u << (shift + 8));
+                const uint32_t cut = on_id ? tcut : ucut;
+                __syncthreads();   // every thread is done with hist
+                for (int i = threadIdx.x; i < 256; i += kSelThreads) sm.hist[i] = 0u;
+                __syncthreads();
+                walk([&](int j, auto id_of) {
+                    if (bin_at(j) == bk) {
+                        const uint32_t u = float_to_ordered(x[j]);
+                        if (on_id ? u == ucut : true) {
+                            const uint32_t v = on_id ? ~(uint32_t)id_of() : u;
+                            if ((v & hi_mask) == cut) atomicAdd(&sm.hist[(v >> shift) & 0xFFu], 1u);
+                        }
+                    }
+                });
+                __syncthreads();
+                const int c = threadIdx.x < 256 ? (int)sm.hist[255 - threadIdx.x] : 0;
+                int incl, excl;
+                block_scan(c, sm.islot, incl, excl);
+                if (excl < left && incl >= left) {
+                    sm.prefix = (uint64_t)(cut | ((255u - threadIdx.x) << shift));
+                    sm.need = left - excl;
+                }
+                __syncthreads();
+                if (on_id)
+                    tcut = (uint32_t)sm.prefix;
+                else
+                    ucut = (uint32_t)sm.prefix;
+                left = sm.need;
+            }
+            // the keys are distinct: exactly `need` of the tie bin are >= (ucut, tcut)
+            compact(
+                [&](int j, auto id_of) {
+                    if (bin_at(j) != bk) return false;
+                    const uint32_t u = float_to_ordered(x[j]);
+                    return u > ucut || (u == ucut && ~(uint32_t)id_of() >= tcut);
+                },
+                sm.gk, above, kMaxK);
+            __syncthreads();
         }
     }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const uint64_t key = lane < min(nsel, 64) ? sel[lane] : 0ull;
-        const int32_t id =
-            finish_topk(key, b, row_is_greedy(temp, b, flags), top_p, row_key(noise, b));
-        if (lane == 0) out_idx[b] = id;
+
+    const int t = threadIdx.x;
+    if constexpr (!FINISH) {
+        // the slice's list: its selection, then padding
+        const size_t o = ((size_t)b * gridDim.x + blockIdx.x) * k;
+        for (int i = t; i < k; i += kSelThreads) {
+            const uint64_t key = i < nsel ? sm.gk[i] : 0ull;
+            ox[o + i] = i < nsel ? key_score(key) : -INFINITY;
+            oidx[o + i] = i < nsel ? key_index(key) : -1;
+        }
+    } else {
+        // the optional top-p cut over the sorted selection, then the draw
+        const bool greedy = row_is_greedy(temp, b, flags);
+        const bool topp = top_p < 1.f && nsel > 0;
+        if (topp) block_sort_prefix(sm.gk, nsel);
+        const uint64_t mine = t < nsel ? sm.gk[t] : 0ull;
+        bool keep = t < nsel;
+        if (topp) {
+            const double x0 = key_score(sm.gk[0]);   // the largest
+            const double q = keep ? exp((double)key_score(mine) - x0) : 0.0;
+            double incl, excl;
+            block_scan(q, sm.dslot, incl, excl);
+            if (t == kSelThreads - 1) sm.total = incl;
+            __syncthreads();
+            keep = keep && excl < (double)top_p * sm.total;
+        }
+        uint64_t best = pack_key(-INFINITY, -1);
+        if (keep)
+            best = scored_key((uint32_t)(mine >> 32), (int32_t)~(uint32_t)mine, b, greedy,
+                              row_key(noise, b));
+        best = wave_max_key(best);
+        if (lane == 0) sm.kslot[t >> 6] = best;
+        __syncthreads();
+        if (t == 0) {
+            uint64_t r = sm.kslot[0];
+#pragma unroll
+            for (int i = 1; i < kSelWaves; ++i) r = key_max(r, sm.kslot[i]);
+            out_idx[b] = key_index(r);
+        }
     }
 }
 
@@ -747,13 +1040,30 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
     return hipGetLastError();
 }
 
-hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B, int k,
-                              float top_p, const float* temp, uint32_t flags,
-                              const NoiseSrc& noise, int32_t* out_idx, hipStream_t stream) {
+namespace {
+bool topk_small_path(int G, int L, int k) {   // the dense form never takes it
+    return k <= 64 && (int64_t)G * L <= (int64_t)kTopkThreads * 64;
+}
+size_t align_256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense) {
+    const int64_t n = (int64_t)G * L;
+    if ((topk_small_path(G, L, k) && !dense) || n <= kSliceCap) return 0;
+    const int64_t S = (n + kSliceCap - 1) / kSliceCap;
+    return 4 * align_256((size_t)S * B * k * 4);   // lists of two levels: x and ids
+}
+
+hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,
+                              DenseIds dn, float top_p, const float* temp, uint32_t flags,
+                              const NoiseSrc& noise, int32_t* out_idx, void* scratch,
+                              hipStream_t stream) {
+    if (k < 1 || k > kMaxK || L < 1 || G < 1) return hipErrorInvalidValue;
+    const bool dense = dn.nmb > 0;
 #define FS_TOPK2(PER_)                                                                       \
-    if ((int64_t)G * k <= (int64_t)kTopkThreads * PER_) {                                   \
+    if (!dense && k <= 64 && (int64_t)G * L <= (int64_t)kTopkThreads * PER_) {             \
         hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \
-                           cx, cidx, G, B, k, top_p, temp, flags, noise, out_idx);           \
+                           cx, cidx, G, L, B, k, top_p, temp, flags, noise, out_idx);        \
         return hipGetLastError();                                                            \
     }
     FS_TOPK2(4)
@@ -762,8 +1072,47 @@ hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int B
     FS_TOPK2(32)
     FS_TOPK2(64)
 #undef FS_TOPK2
-    hipLaunchKernelGGL(stage2_topk_radix_kernel, dim3(B), dim3(kRedThreads), 0, stream, cx, cidx,
-                       G, B, k, top_p, temp, flags, noise, out_idx);
+    if ((int64_t)G * L > INT32_MAX / 4) return hipErrorInvalidValue;
+    // selection levels over slices until one workgroup holds a row
+    const size_t list = stage2_topk_scratch_bytes(G, L, B, k, dense) / 4;
+    if (list > 0 && !scratch) return hipErrorInvalidValue;
+    char* base = static_cast<char*>(scratch);
+    const float* ix = cx;
+    const int32_t* ii = cidx;
+    int g = G, l = L;
+    bool first_dense = dense;   // only the first level reads dense lists
+    for (int level = 0; (int64_t)g * l > kSliceCap; ++level) {
+        const int n = g * l;
+        const int S0 = (n + kSliceCap - 1) / kSliceCap;
+        const int per = (n + S0 - 1) / S0;   // balanced slices of at most kSliceCap
+        const int S = (n + per - 1) / per;   // every slice non-empty
+        char* lv = base + (size_t)(level & 1) * 2 * list;
+        float* ox = reinterpret_cast<float*>(lv);
+        int32_t* oi = reinterpret_cast<int32_t*>(lv + list);
+        if (first_dense)
+            hipLaunchKernelGGL((stage2_topk_select_kernel<false, true>), dim3(S, B),
+                               dim3(kSelThreads), 0, stream, ix, ii, g, l, B, k, per, dn, ox, oi,
+                               top_p, temp, flags, noise, out_idx);
+        else
+            hipLaunchKernelGGL((stage2_topk_select_kernel<false, false>), dim3(S, B),
+                               dim3(kSelThreads), 0, stream, ix, ii, g, l, B, k, per, dn, ox, oi,
+                               top_p, temp, flags, noise, out_idx);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ix = ox;
+        ii = oi;
+        g = S;
+        l = k;
+        first_dense = false;
+    }
+    if (first_dense)
+        hipLaunchKernelGGL((stage2_topk_select_kernel<true, true>), dim3(1, B), dim3(kSelThreads),
+                           0, stream, ix, ii, g, l, B, k, g * l, dn, nullptr, nullptr, top_p,
+                           temp, flags, noise, out_idx);
+    else
+        hipLaunchKernelGGL((stage2_topk_select_kernel<true, false>), dim3(1, B),
+                           dim3(kSelThreads), 0, stream, ix, ii, g, l, B, k, g * l, dn, nullptr,
+                           nullptr, top_p, temp, flags, noise, out_idx);
     return hipGetLastError();
 }
 

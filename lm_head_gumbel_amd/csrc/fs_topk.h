@@ -98,7 +98,11 @@ __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uin
         t[c] = 0;
         tt[c] = 0;
     }
-    for (int bit = 31; bit >= 0; --bit) {
+    bool any_big = false;
+#pragma unroll
+    for (int c = 0; c < C; ++c) any_big = any_big || big[c];
+    // (with at most k real entries in every set there is nothing to search)
+    for (int bit = 31; any_big && bit >= 0; --bit) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const uint32_t cand = t[c] | (1u << bit);
@@ -133,11 +137,12 @@ __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uin
             sel[c][i] = u[c][i] > t[c] || (t[c] > 0 && u[c][i] == t[c] && tb[c][i] >= tt[c]);
 }
 
-// Writes the (row, x) of the marked entries of set c to staging (ballot-
-// prefix order); returns their number.  rowx(c, i, row, x) gives an entry.
+// Writes the (x, id) of the marked entries of set c to its candidate list
+// (ballot-prefix order, positions 0, 1, ...); returns their number.
+// rowx(c, i, row, x) gives an entry; ids are gid0 + row.
 template <int C, int M, typename RowX>
-__device__ __forceinline__ int stage_selected(const bool (&sel)[C][M], int c, RowX rowx, float* sx,
-                                              int* sid) {
+__device__ __forceinline__ int write_selected(const Stage1Args& a, const bool (&sel)[C][M], int c,
+                                              RowX rowx, int gid0, size_t o) {
     const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
     int nsel = 0;
 #pragma unroll
@@ -148,24 +153,46 @@ __device__ __forceinline__ int stage_selected(const bool (&sel)[C][M], int c, Ro
             int row;
             float x;
             rowx(c, i, row, x);
-            sx[pos] = x;
-            sid[pos] = row;
+            a.cx[o + pos] = x;
+            a.cidx[o + pos] = gid0 + row;
         }
         nsel += __popcll(sb);
     }
     return nsel;
 }
 
+// Dense lists (k reaches every row of the longest range): the x of rows
+// [0, nr) of each of the nc columns, in row order, then -inf up to
+// a.topk_len; the ids are implied by the position.  a.topk_len and nr are
+// multiples of 16 and the list offsets o[c] multiples of a.topk_len.
+template <int C>
+__device__ __forceinline__ void topk_write_dense(const Stage1Args& a, int nc,
+                                                 float* const (&xc)[C], int nr,
+                                                 const size_t (&o)[C]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (c >= nc) break;
+        for (int r = 4 * lane; r < a.topk_len; r += 256) {
+            const f32x4 v = r < nr ? *reinterpret_cast<const f32x4*>(xc[c] + r)
+                                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            *reinterpret_cast<f32x4*>(a.cx + o[c] + r) = v;
+        }
+    }
+}
+
 // One wave, C columns at once: the top-k candidates of rows [0, nr) of C
 // columns (c < nc are real) whose x sit in LDS at xc[c][row] (row r is
 // global id gid0 + r; each xc[c] is 16-byte aligned, holds NR * 64 >= 640
-// entries plus at least two of padding, and is overwritten).  Writes a.topk candidates (x, id) of column c
-// at offset o[c] of a.cx / a.cidx, unused slots as (-inf, -1).  The noise is
-// drawn later, for the row's final k only.
+// entries plus at least two of padding, and is overwritten).  Writes the
+// min(k, valid rows) candidates (x, id) of column c at offset o[c] of a.cx /
+// a.cidx and fills the list's other slots, up to a.topk_len >= min(k, nr),
+// with (-inf, -1).  The noise is drawn later, for the row's final k only.
 //
 // A lower bound cuts the work: the k-th largest of the lanes' two largest
 // values is at most the column's k-th largest value (k of the column's
-// values are at least that large).  Usually little more than k values reach
+// values are at least that large; for k > 128 there is no such bound and
+// every valid value is a survivor).  Usually little more than k values reach
 // it; those are compacted to one per lane and the exact selection runs on
 // them, all C columns interleaved (other paths take up to four per lane, or
 // all entries, one column at a time).
@@ -224,8 +251,9 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
         nmax = n > nmax ? n : nmax;
     }
 
-    // staging of the selected: x at xc[c][512, 576), rows at xc[c][576, 640)
     int nsel[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) nsel[c] = 0;
     if (nmax <= 256) {
         // compact the values >= lo: x to xc[c][0, 256), rows to xc[c][256, 512)
         // (every lane has read its entries above)
@@ -265,9 +293,10 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
             wave_select<C, 1>(v, tb, k, sel);
 #pragma unroll
             for (int c = 0; c < C; ++c)
-                nsel[c] = stage_selected<C, 1>(
-                    sel, c, [&](int cc, int, int& row, float& x) { row = vr[cc][0]; x = vx[cc][0]; },
-                    xc[c] + 512, reinterpret_cast<int*>(xc[c] + 576));
+                if (c < nc)
+                    nsel[c] = write_selected<C, 1>(
+                        a, sel, c, [&](int cc, int, int& row, float& x) { row = vr[cc][0]; x = vx[cc][0]; },
+                        gid0, o[c]);
         } else {
             // one column at a time, up to two or four survivors per lane
             auto run1 = [&](int c, auto m_tag) {
@@ -285,14 +314,15 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
                     tb[0][j] = ~(uint32_t)vr[j];
                 }
                 wave_select<1, M>(v, tb, k, sel);
-                return stage_selected<1, M>(
-                    sel, 0, [&](int, int j, int& row, float& x) { row = vr[j]; x = vx[j]; },
-                    xc[c] + 512, reinterpret_cast<int*>(xc[c] + 576));
+                return write_selected<1, M>(
+                    a, sel, 0, [&](int, int j, int& row, float& x) { row = vr[j]; x = vx[j]; }, gid0,
+                    o[c]);
             };
 #pragma unroll
             for (int c = 0; c < C; ++c)
-                nsel[c] = cnt[c] <= 128 ? run1(c, std::integral_constant<int, 2>{})
-                                        : run1(c, std::integral_constant<int, 4>{});
+                if (c < nc)
+                    nsel[c] = cnt[c] <= 128 ? run1(c, std::integral_constant<int, 2>{})
+                                            : run1(c, std::integral_constant<int, 4>{});
         }
     } else {
         // more than 256 values reach the bound (many equal values): the
@@ -307,27 +337,22 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
                 tb[0][i] = ~(uint32_t)row_of(i);
             }
             wave_select<1, NR>(uc, tb, k, sel);
-            // the staging area overlaps rows 512..639: every lane has read them
-            nsel[c] = stage_selected<1, NR>(
-                sel, 0, [&](int, int i, int& row, float& x) {
-                    row = row_of(i);
-                    x = ordered_to_float(uc[0][i]);
-                },
-                xc[c] + 512, reinterpret_cast<int*>(xc[c] + 576));
+            if (c < nc)
+                nsel[c] = write_selected<1, NR>(
+                    a, sel, 0, [&](int, int i, int& row, float& x) {
+                        row = row_of(i);
+                        x = ordered_to_float(uc[0][i]);
+                    },
+                    gid0, o[c]);
         }
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-
-    // the selected, one candidate per lane
-    if (lane < k) {
+    // unused slots of the lists
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            if (c >= nc) break;
-            const bool live = lane < nsel[c];
-            a.cx[o[c] + lane] = live ? xc[c][512 + lane] : -INFINITY;
-            a.cidx[o[c] + lane] =
-                live ? gid0 + reinterpret_cast<const int*>(xc[c] + 576)[lane] : -1;
+    for (int c = 0; c < C; ++c) {
+        if (c >= nc) break;
+        for (int q = nsel[c] + lane; q < a.topk_len; q += 64) {
+            a.cx[o[c] + q] = -INFINITY;
+            a.cidx[o[c] + q] = -1;
         }
     }
 }

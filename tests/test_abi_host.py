@@ -89,7 +89,9 @@ def test_unsupported_requests_are_reported():
         fs.FS_ERR_UNSUPPORTED
     assert fs.fs_sample_grouped(fs.params(2, 64, 128, tile_v=100), 16, 16, None, None,
                                 16, 16, 16) == fs.FS_ERR_UNSUPPORTED
-    assert fs.fs_sample_topk(fs.params(2, 64, 128), 16, 16, None, None, 65, 16) == \
+    assert fs.fs_sample_topk(fs.params(2, 64, 128), 16, 16, None, None, 1025, 16) == \
+        fs.FS_ERR_UNSUPPORTED
+    assert fs.fs_sample_topk_topp(fs.params(2, 64, 128), 16, 16, None, None, 1025, 0.5, 16) == \
         fs.FS_ERR_UNSUPPORTED
     # misaligned operands (16-byte loads)
     assert fs.fs_sample(fs.params(2, 64, 128), 18, 16, None, None, 16) == fs.FS_ERR_UNSUPPORTED

@@ -9,8 +9,8 @@ Workloads (synthetic stand-ins for the pages' Qwen3-class decode LM heads):
   mid-size      d=4096, V=151936, B in {1, 4, 16, 64}, T=1, last 285 ids
                 masked, grouped records and hierarchical resample
   compute-lean  d=4096, V=128256, B in {128, 256}, T_b ~ U[0.3, 1.5]
-  top-k/online  d=5120, V=152064, B=32, top-40, online merge over 8 chunks of
-                19008 ids
+  top-k/online  d=5120, V=152064, B=32, top-40 (and top-1000), online merge
+                over 8 chunks of 19008 ids
 """
 import numpy as np
 import pytest
@@ -19,7 +19,7 @@ import lm_head_gumbel_amd as fs
 from lm_head_gumbel_amd.inputs import WORKLOADS, PHILOX_SEED, hidden_bf16, weights_bf16
 from oracle import fs_oracle as O
 from gpu_util import (Inputs, TOL_GAP, check_index_rows, check_values, log, run_flat,
-                      run_grouped, run_merge, run_topk, torch)
+                      run_grouped, run_merge, run_topk, run_topp, torch, TOL_CUT)
 from stats_util import chi_square_rows_p, softmax
 
 pytestmark = pytest.mark.gpu
@@ -167,6 +167,18 @@ def test_topk_and_online_merge():
     pin = (ogap > TOL_GAP) & (omarg > 1e-3)
     assert np.array_equal(tk[pin], oi[pin])
     log(f"  top-{wl.k}: {pin.sum()}/{wl.B} rows pinned")
+    # the pages' largest benchmarked k: lists of whole workgroup ranges and
+    # the binned stage-2 selection, also under a top-p cut
+    k = 1000
+    tk = run_topk(x_in, p, k)
+    oi, ogap, omarg = O.topk_sample(x, s, k)
+    pin = (ogap > TOL_GAP) & (omarg > 1e-3)
+    assert np.array_equal(tk[pin], oi[pin])
+    tp = run_topp(x_in, p, k, 0.95)
+    oi, ogap, omarg, ocut = O.topk_topp_sample(x, s, k, 0.95)
+    pin2 = (ogap > TOL_GAP) & (omarg > 1e-3) & (ocut > TOL_CUT)
+    assert np.array_equal(tp[pin2], oi[pin2])
+    log(f"  top-{k}: {pin.sum()}/{wl.B} rows pinned; top-p 0.95: {pin2.sum()}/{wl.B}")
     # online merge over 8 sequential chunks of V/8 ids: chunk records from the
     # grouped entry point with one tile per chunk, then the binary merge
     chunk = wl.V // wl.chunks

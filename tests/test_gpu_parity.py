@@ -77,6 +77,31 @@ def test_gumbel_extreme_words():
 # ---------------------------------------------------------------------------
 # one full comparison of every entry point on one problem
 # ---------------------------------------------------------------------------
+def check_topk(x_in, p, r, k, v_offset=0, top_ps=(0.9, 0.5)):
+    """Top-k and top-p after top-k against the oracle on the oracle's x and s."""
+    B = x_in.B
+    tk = run_topk(x_in, p, k)
+    oi, ogap, omarg = O.topk_sample(r["x"], r["s"], k, v_offset)
+    pin = (ogap > TOL_GAP) & (omarg > 1e-3)
+    bad = np.nonzero(pin & (tk != oi))[0]
+    assert bad.size == 0, f"top-{k} rows {bad} got {tk[bad]} want {oi[bad]}"
+    for b in range(B):
+        if oi[b] < 0:
+            assert tk[b] == -1
+        else:
+            assert np.isfinite(r["x"][b, tk[b] - v_offset])
+    # top-p after top-k; top_p = 1 is the top-k sample itself
+    assert np.array_equal(run_topp(x_in, p, k, 1.0), tk)
+    for top_p in top_ps:
+        tp = run_topp(x_in, p, k, top_p)
+        oi, ogap, omarg, ocut = O.topk_topp_sample(r["x"], r["s"], k, top_p, v_offset)
+        pin = (ogap > TOL_GAP) & (omarg > 1e-3) & (ocut > TOL_CUT)
+        bad = np.nonzero(pin & (tp != oi))[0]
+        assert bad.size == 0, f"top-{k} top-p {top_p} rows {bad} got {tp[bad]} want {oi[bad]}"
+        assert np.all((tp == -1) == (oi == -1))
+    return int(pin.sum())
+
+
 def compare_all(Hb, Wb, temp=None, n_valid=None, allow=None, tile_v=128, v_offset=0,
                 seed=SEED, steps=(0,), flags=0, topk=(1, 7, 40), check_logits=True):
     B, d = Hb.shape
@@ -118,27 +143,8 @@ def compare_all(Hb, Wb, temp=None, n_valid=None, allow=None, tile_v=128, v_offse
         for b in np.nonzero(~pinned)[0]:
             assert go[b] == -1 or go[b] in set(ti[b].tolist())
         # top-k
-        greedy = O.greedy_rows(temp, B, flags)
         for k in topk:
-            tk = run_topk(x_in, p, k)
-            oi, ogap, omarg = O.topk_sample(r["x"], r["s"], k, v_offset)
-            pin = (ogap > TOL_GAP) & (omarg > 1e-3)
-            bad = np.nonzero(pin & (tk != oi))[0]
-            assert bad.size == 0, f"top-{k} rows {bad} got {tk[bad]} want {oi[bad]}"
-            for b in range(B):
-                if oi[b] < 0:
-                    assert tk[b] == -1
-                else:
-                    assert np.isfinite(r["x"][b, tk[b] - v_offset])
-            # top-p after top-k; top_p = 1 is the top-k sample itself
-            assert np.array_equal(run_topp(x_in, p, k, 1.0), tk)
-            for top_p in (0.9, 0.5):
-                tp = run_topp(x_in, p, k, top_p)
-                oi, ogap, omarg, ocut = O.topk_topp_sample(r["x"], r["s"], k, top_p, v_offset)
-                pin = (ogap > TOL_GAP) & (omarg > 1e-3) & (ocut > TOL_CUT)
-                bad = np.nonzero(pin & (tp != oi))[0]
-                assert bad.size == 0, f"top-{k} top-p {top_p} rows {bad} got {tp[bad]} want {oi[bad]}"
-                assert np.all((tp == -1) == (oi == -1))
+            check_topk(x_in, p, r, k, v_offset)
         # unfused baseline on the GPU's own logits
         if check_logits:
             mi = run_multinomial(x_in, p, gl_dev)
@@ -203,6 +209,52 @@ def test_parity_small(case):
     Hb, Wb, temp, allow = make_case(B, d, V, tk, al)
     compare_all(Hb, Wb, temp, n_valid=v_off + V - cut, allow=allow, tile_v=tile_v,
                 v_offset=v_off, steps=(0, 1))
+
+
+# k above 64: lists of up to a whole workgroup range per row (the resident
+# stage-1 kernel) and the binned stage-2 selection; k >= the valid ids keeps
+# them all
+LARGE_K_CASES = [
+    # (B, d, V, n_valid_cut, v_offset, temp kind, allow, ks)
+    (7, 1024, 3000, 7, 0, "mixed", True, (65, 300, 1024)),
+    (25, 1024, 2600, 0, 32, "range", False, (100, 1000)),
+    (24, 5120, 2000, 3, 16, "mixed", True, (128, 700)),
+    (2, 2048, 1111, 1, 16, "range", True, (1024,)),
+    (20, 512, 20000, 5, 0, "range", False, (200, 1024)),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_K_CASES, ids=lambda c: f"B{c[0]}_d{c[1]}_V{c[2]}")
+def test_topk_large_k(case):
+    B, d, V, cut, v_off, tk, al, ks = case
+    Hb, Wb, temp, allow = make_case(B, d, V, tk, al)
+    x_in = Inputs(Hb, Wb, temp, allow)
+    l = O.logits_bf16(Hb, Wb)
+    nv = v_off + V - cut
+    for step in (0, 1):
+        p = x_in.params(n_valid=nv, v_offset=v_off, tile_v=128, seed=SEED, step=step)
+        r = O.run_call(l, temp, nv, allow, SEED, step, 0, 128, v_off)
+        for k in ks:
+            log(f"large k: B={B} d={d} V={V} k={k} step={step}")
+            npin = check_topk(x_in, p, r, k, v_off, top_ps=(0.95, 0.6))
+            log(f"  {npin}/{B} rows pinned")
+
+
+def test_topk_large_k_needs_the_resident_kernel():
+    """k > 64 on a hidden size that only the cooperative kernel covers is
+    reported, not run."""
+    t = torch()
+    Hb, Wb, temp, _ = make_case(3, 136, 900, "one", False)
+    x = Inputs(Hb, Wb, temp)
+    p = x.params(seed=SEED)
+    assert fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, 65) == 0
+    assert fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, 64) > 0
+    idx = t.full((3,), -7, dtype=t.int32, device="cuda")
+    ws = t.empty(1 << 24, dtype=t.uint8, device="cuda")
+    assert fs.fs_sample_topk(p, x.H, x.W, x.temp, None, 65, idx, ws) == fs.FS_ERR_UNSUPPORTED
+    assert fs.fs_sample_topk(p, x.H, x.W, x.temp, None, 1025, idx, ws) == fs.FS_ERR_UNSUPPORTED
+    t.cuda.synchronize()
+    assert np.all(idx.cpu().numpy() == -7)
 
 
 def test_tiny_reference_config():
@@ -305,13 +357,15 @@ def test_topk_exact_ties_take_lowest_ids(B, d):
             assert np.array_equal(oi[pin], want[pin])
 
 
-@pytest.mark.parametrize("V,k", [(200000, 64), (40000, 40), (1024, 8)])
+@pytest.mark.parametrize("V,k", [(200000, 64), (40000, 40), (1024, 8), (200000, 1024),
+                                 (3000, 1000), (900, 1024)])
 def test_topk_all_logits_equal(V, k):
     """Every W row is the same row, so all V logits of a batch row are equal
     and the top-k set is ids 0 .. k-1.  The sizes drive the selection into its
     less common branches: whole workgroup ranges of ties (768 and 160 rows
-    per workgroup) and stage-2 candidate sets that the lower bound cannot
-    prune."""
+    per workgroup), stage-2 candidate sets that the lower bound cannot prune,
+    and for large k the exact radix search (all candidates in one bin), the
+    gathered sort and a row with fewer valid ids than k."""
     B, d = 3, 512
     Hb = hidden_bf16(B, d, seed=21)
     row = weights_bf16(1, d, std=0.05, seed=22)
@@ -322,6 +376,7 @@ def test_topk_all_logits_equal(V, k):
     p = x_in.params(seed=SEED, step=2)
     log(f"all-equal logits V={V} k={k}")
     got = run_topk(x_in, p, k)
+    k_req, k = k, min(k, V)   # every id when there are fewer than k
     assert np.all((got >= 0) & (got < k)), got
     x = O.tempered(np.repeat(l, k, axis=1), temp)
     sc = O.scores(x, temp, SEED, 2, 0, 0)
@@ -333,7 +388,7 @@ def test_topk_all_logits_equal(V, k):
     assert np.array_equal(got[pin], want[pin])
     # top-p 0.5 on k equal masses keeps the first ceil(k / 2): ids 0 .. ceil(k/2) - 1
     kept = (k + 1) // 2
-    tp = run_topp(x_in, p, k, 0.5)
+    tp = run_topp(x_in, p, k_req, 0.5)
     assert np.all((tp >= 0) & (tp < kept)), tp
     want = np.argmax(sc[:, :kept], axis=1)
     top2 = np.sort(sc[:, :kept], axis=1)
