@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfs.so")
-SOURCES = ["fs_api.hip", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip", "fs_stage2.hip", "fs_probe.hip"]
+SOURCES = ["fs_api.hip", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip",
+           "fs_stage2.hip", "fs_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -22,25 +23,60 @@ def hipcc():
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-def command(out=LIB):
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+# Extra device-compiler flags per source (none at present).
+EXTRA_FLAGS = {}
+
+
+def common_flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             # no packed-FP32 instructions in device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def compile_commands(objdir):
+    """(source, object, command) per source file."""
+    out = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + \
+            ["-c", os.path.join(CSRC, src), "-o", obj]
+        out.append((src, obj, cmd))
+    return out
 
 
 def build(verbose=False):
-    """Compile every HIP source into libfs.so next to this file (atomic replace)."""
+    """Compile every HIP source (in parallel) and link libfs.so next to this
+    file (atomic replace)."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libfs.so")
+    with tempfile.TemporaryDirectory(prefix="fs_build_") as objdir:
+        jobs = compile_commands(objdir)
+
+        def run(job):
+            src, obj, cmd = job
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return src, subprocess.run(cmd, capture_output=True, text=True)
+
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(run, jobs))
+        failed = [(src, r) for src, r in results if r.returncode != 0]
+        for src, r in failed:
+            sys.stderr.write(f"--- {src}\n" + r.stdout + r.stderr)
+        if failed:
+            raise RuntimeError("hipcc failed building libfs.so: " + ", ".join(s for s, _ in failed))
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + \
+            [obj for _, obj, _ in jobs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed linking libfs.so")
     os.replace(tmp, LIB)
     return LIB
 
