@@ -202,6 +202,17 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
             pl.kind = kWide;
             pl.nt = p->B <= 64 ? 64 : 128;
         }
+        // grouped records up to 64 columns: one workgroup per CU, each range
+        // meeting at most 16 vocabulary tiles (its per-tile slots live in LDS)
+        if (variant == kVarGrouped && p->B > 32 && p->B <= 64 && p->d > 0 && p->d % 64 == 0 &&
+            forced < 0 && wide_enabled()) {
+            const int g = std::max(1, std::min(pl.nmb, cus));
+            const int blocks = (pl.nmb + g - 1) / g;   // longest range
+            if ((blocks - 1 + pl.tile_mb - 1) / pl.tile_mb + 1 <= kWideMaxTiles) {
+                pl.kind = kWide;
+                pl.nt = 64;
+            }
+        }
     }
     pl.stream = pl.kind == kStream;
     pl.cfg = pick_config(pl.stream, p->B);
@@ -516,9 +527,10 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     a.pidx = w.pidx;
     a.pL = w.pL;
     hipError_t e =
-        pl.kind == kResident ? launch_resident(kVarGrouped, a, pl.grid_y, pl.rcfg, s)
-        : pl.stream          ? launch_stream(kVarGrouped, a, pl.grid_y, pl.cfg, w.part, true, s)
-                             : launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);
+        pl.kind == kWide       ? launch_wide(kVarGrouped, a, pl.nt, pl.grid_y, s)
+        : pl.kind == kResident ? launch_resident(kVarGrouped, a, pl.grid_y, pl.rcfg, s)
+        : pl.stream            ? launch_stream(kVarGrouped, a, pl.grid_y, pl.cfg, w.part, true, s)
+                               : launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
     // record slot (worker w, tile t) is w + t; the streaming kernel's workers
     // own ranges of (block, quarter) units, the cooperative kernel's of blocks

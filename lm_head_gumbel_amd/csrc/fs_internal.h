@@ -114,6 +114,10 @@ hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const R
 
 // LDS-tiled stage 1 for large batches (flat and logits variants): nt batch
 // columns per workgroup (64 or 128); requires d % 64 == 0.
+// The LDS-tiled stage 1 (fs_wide.hip): flat and logits with nt = 64 or 128;
+// grouped with nt = 64 when every workgroup range meets at most
+// kWideMaxTiles vocabulary tiles.
+constexpr int kWideMaxTiles = 16;
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream);
 
 // Streaming stage 1 (flat, grouped or logits) over a.G workgroups of four

@@ -38,10 +38,22 @@ struct WideSmem {
     uint64_t fkey[2][NT];
 };
 
+// Grouped variant: per (row-half, vocabulary tile of the range, column) the
+// winner and log-mass gathered so far; a range meets at most kWideMaxTiles
+// tiles (the host checks).
+template <int NT>
+struct WideTileSmem {
+    uint64_t key[2][kWideMaxTiles][NT];
+    float mx[2][kWideMaxTiles][NT];
+    float sm[2][kWideMaxTiles][NT];
+};
+struct NoWideTiles {};
+
 template <int NT, int NTHR, int VAR>
 __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
     static_assert((NT == 64 || NT == 128) && NTHR == 512, "column tile and workgroup size");
-    static_assert(VAR == kVarFlat || VAR == kVarLogits, "variant");
+    static_assert(VAR == kVarFlat || VAR == kVarLogits || (VAR == kVarGrouped && NT == 64),
+                  "variant");
     constexpr int WM = 2, WN = NTHR / 64 / WM;   // wave grid: 2 x 4
     constexpr int RW = kMT / WM;          // 128 rows per wave
     constexpr int MF = RW / 16;           // 8 A fragments
@@ -49,6 +61,9 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
     constexpr int WP = kMT * 8 / NTHR;    // W pieces of 16 B per thread per chunk
     constexpr int HP = NT * 8 / NTHR;     // H pieces
     __shared__ WideSmem<NT> sm;
+    using TileSmem =
+        typename std::conditional<VAR == kVarGrouped, WideTileSmem<NT>, NoWideTiles>::type;
+    __shared__ TileSmem tsm;
 
     // row range w and column group y (see resident_kernel for the XCD pairing)
     int w, y;
@@ -156,6 +171,18 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
         set_tile_rows(t);
         load_chunk(r, c);
     };
+    // grouped: vocabulary tiles t_first .. t_last meet this range
+    const int t_first = VAR == kVarGrouped ? mb0 / a.tile_mb : 0;
+    const int ntl = VAR == kVarGrouped ? (mb1 - 1) / a.tile_mb - t_first + 1 : 0;
+    if constexpr (VAR == kVarGrouped) {
+        for (int e = tid; e < 2 * kWideMaxTiles * NT; e += NTHR) {
+            const int h = e / (kWideMaxTiles * NT), tl = (e / NT) % kWideMaxTiles, col = e % NT;
+            tsm.key[h][tl][col] = pack_key(-INFINITY, -1);
+            tsm.mx[h][tl][col] = -INFINITY;
+            tsm.sm[h][tl][col] = 0.f;
+        }
+    }
+
     load_seq(0, 0);
     load_seq(1, 1);
     store_chunk(0, 0);
@@ -198,7 +225,54 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        if (c + 1 == nchunks) {
+        if constexpr (VAR == kVarGrouped) {
+          if (c + 1 == nchunks) {
+            // the tile is complete: this wave's 16-row blocks in order; a
+            // record segment (vocabulary tile) ends where the tile index
+            // changes, and its column winners and log-mass are merged into
+            // the range's per-tile slots of this row-half
+            int t_cur = -1;
+            uint64_t gbest = pack_key(-INFINITY, -1);
+            Lse glse = lse_empty();
+            const int col = wn * (NT / WN) + r16;   // one B fragment per wave
+            auto flush = [&]() {
+                column_reduce<kVarGrouped>(gbest, glse);
+                if (lane < 16) {
+                    const int tl = t_cur - t_first;
+                    tsm.key[wm][tl][col] = key_max(tsm.key[wm][tl][col], gbest);
+                    const Lse o = lse_merge(Lse{tsm.mx[wm][tl][col], tsm.sm[wm][tl][col]}, glse);
+                    tsm.mx[wm][tl][col] = o.mx;
+                    tsm.sm[wm][tl][col] = o.sm;
+                }
+            };
+            ColCtx cx;
+            cx.col = bbase + col;
+            cx.ok = cx.col < a.B;
+            cx.greedy = !(inv_t[0] > 0.f);
+            cx.inv_t = cx.greedy ? 1.f : inv_t[0];
+            cx.allow_row =
+                (a.allow && cx.ok) ? a.allow + (size_t)cx.col * ((a.V + 31) >> 5) : nullptr;
+            cx.key = key[0];
+#pragma unroll
+            for (int j = 0; j < MF; ++j) {
+                if (j >= nvalid) continue;   // uniform
+                const int t = (blk0 + j) / a.tile_mb;
+                if (t != t_cur) {   // uniform
+                    if (t_cur >= 0) flush();
+                    t_cur = t;
+                    gbest = pack_key(-INFINITY, -1);
+                    glse = lse_empty();
+                }
+                const int row0 = (blk0 + j) * kMBlock + 4 * kg;
+                float x[4], sc[4];
+                lane_scores(a, cx, acc[j][0], row0, true, x, sc);
+                fold<kVarGrouped>(gbest, glse, x, sc, a.v_offset + row0);
+            }
+            if (t_cur >= 0) flush();
+#pragma unroll
+            for (int j = 0; j < MF; ++j) acc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        } else if (c + 1 == nchunks) {
             // the tile is complete: fold its logits into the column winners
 #pragma unroll
             for (int j = 0; j < MF; ++j) {
@@ -247,6 +321,20 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
     // before the registers go away
     __builtin_amdgcn_s_waitcnt(0);
 
+    if constexpr (VAR == kVarGrouped) {
+        // one record per (column, vocabulary tile of the range): the two
+        // row-halves' slots merged, at record slot w + t
+        __syncthreads();
+        for (int e = tid; e < ntl * NT; e += NTHR) {
+            const int tl = e / NT, col = e % NT;
+            const ColCtx c = col_ctx(a, bbase + col);
+            const uint64_t k = key_max(tsm.key[0][tl][col], tsm.key[1][tl][col]);
+            const Lse l = lse_merge(Lse{tsm.mx[0][tl][col], tsm.sm[0][tl][col]},
+                                    Lse{tsm.mx[1][tl][col], tsm.sm[1][tl][col]});
+            put_record<kVarGrouped, false>(a, w + t_first + tl, c, k, l);
+        }
+    }
+
     if constexpr (VAR == kVarFlat) {
         // the two row-halves' column winners meet in LDS
 #pragma unroll
@@ -272,6 +360,10 @@ static hipError_t launch_wide_nt(const Stage1Args& a, int grid_y, hipStream_t st
 }
 
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream) {
+    if (variant == kVarGrouped) {
+        if (nt == 64) return launch_wide_nt<64, kVarGrouped>(a, grid_y, stream);
+        return hipErrorInvalidValue;
+    }
     if (variant == kVarFlat) {
         if (nt == 64) return launch_wide_nt<64, kVarFlat>(a, grid_y, stream);
         if (nt == 128) return launch_wide_nt<128, kVarFlat>(a, grid_y, stream);

@@ -176,6 +176,11 @@ CASES = [
     # B > 32 with d % 64 == 0: the LDS-tiled kernel (one and two column groups)
     (100, 192, 1700, 64, 0, 16, "range", False),
     (150, 256, 2000, 128, 5, 0, "mixed", True),
+    # 32 < B <= 64: grouped records from the LDS-tiled kernel too; ranges of
+    # 320 rows (two 256-row tiles) meeting several vocabulary tiles, and
+    # 16-row vocabulary tiles (eight per range)
+    (48, 256, 80000, 64, 7, 16, "mixed", True),
+    (64, 128, 30000, 16, 0, 0, "range", False),
 ]
 
 
