@@ -234,6 +234,14 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         pl.G = std::max(1, std::min(pl.nmb, cus * per_cu));
         workers = pl.G;
     }
+    // resident flat and logits stride units of mpi blocks over the workgroups:
+    // at most one workgroup per unit
+    const bool strided = pl.kind == kResident && (variant == kVarFlat || variant == kVarLogits);
+    const int max_g = strided ? (pl.nmb + pl.rcfg.mpi - 1) / pl.rcfg.mpi : pl.nmb;
+    if (pl.G > max_g) {
+        pl.G = max_g;
+        workers = max_g;
+    }
     // resident top-k keeps the x of its whole range in LDS: enough workgroups
     // that no range exceeds that store
     int min_g = 1;
@@ -251,7 +259,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         const int per_cu = pl.kind == kWide ? 1 : wg_per_cu();
         int g = (cus * per_cu / pl.grid_y) / 8 * 8;
         if (g < min_g) g = (min_g + 7) / 8 * 8;
-        if (g >= 8 && g <= pl.nmb) {
+        if (g >= 8 && g <= max_g) {
             pl.G = g;
             workers = g;
             pl.xcd_pair = 1;
