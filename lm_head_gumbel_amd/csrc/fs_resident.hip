@@ -152,8 +152,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // which streams HBM better than one contiguous range per workgroup (6.10
     // against 5.78 TB/s at B = 32, d = 4096, V = 151936).  Any partition gives
     // the same flat sample (the noise is keyed by the global id).  Grouped
-    // records and the top-k row store need contiguous ranges [mb0, mb1).
-    // Strided: mb0 is the first block, mb1 one past the last unit's blocks.
+    // records (one per workgroup and tile) and the top-k row store need a
+    // contiguous range [mb0, mb1).  Strided: mb0 is the first block, mb1 one
+    // past the last unit's blocks.
     constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits;
     int mb0, mb1;
     if constexpr (kStrided) {
