@@ -197,14 +197,15 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
             pl.kind = kStream;
         if (forced == kCoop || (forced == kStream && pl.nmb >= 4)) pl.kind = forced;
         // large batches: the LDS-tiled kernel shares each W tile among all columns
+        // (chunks of d: 128 deep for 64 columns, 64 deep for 128)
         if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
-            p->d % 64 == 0 && forced < 0 && wide_enabled()) {
+            p->d % (p->B <= 64 ? 128 : 64) == 0 && forced < 0 && wide_enabled()) {
             pl.kind = kWide;
             pl.nt = p->B <= 64 ? 64 : 128;
         }
         // grouped records up to 64 columns: one workgroup per CU, each range
         // meeting at most 16 vocabulary tiles (its per-tile slots live in LDS)
-        if (variant == kVarGrouped && p->B > 32 && p->B <= 64 && p->d > 0 && p->d % 64 == 0 &&
+        if (variant == kVarGrouped && p->B > 32 && p->B <= 64 && p->d > 0 && p->d % 128 == 0 &&
             forced < 0 && wide_enabled()) {
             const int g = std::max(1, std::min(pl.nmb, cus));
             const int blocks = (pl.nmb + g - 1) / g;   // longest range

@@ -3,17 +3,17 @@
 // Sampling", Abstract; FlashSampling explainer on aitrends.kr, Stage 1).
 //
 // A workgroup (8 waves) owns a balanced range of 16-row vocabulary blocks and
-// walks it in tiles of MT = 256 rows.  For each tile it contracts over the
-// hidden dimension in chunks of KC = 64: the W tile (256 rows x 128 bytes) and
-// the H tile (NT batch rows x 128 bytes) are loaded cooperatively as whole
-// 128-byte lines (eight lanes per row), written to a double-buffered LDS area
-// with a 144-byte row stride (conflict-free MFMA fragment reads), and each wave
-// computes a 128 x NT/4 sub-tile with v_mfma_f32_16x16x32_bf16 (NT = 64 or
-// 128; wider tiles would not fit the accumulators in 256 registers per lane).  W is read
-// from HBM once; H (at most 256 x d bf16) stays in L2.  After the last chunk
-// of a tile the waves fold their logits into per-column winners (temperature,
-// masks, Philox-Gumbel noise); the column winners of the two row-halves meet
-// in LDS at the end and become the workgroup's record.
+// walks it in tiles of MT rows (128 for NT = 64 batch columns, 256 for 128).
+// For each tile it contracts over the hidden dimension in chunks of KC (128 or
+// 64): the W tile (MT rows x 2 KC bytes) and the H tile (NT batch rows x 2 KC
+// bytes) are loaded cooperatively, one row run per group of lanes, written to
+// a double-buffered LDS area with 16 bytes of padding per row (conflict-free
+// fragment reads), and each wave computes an MT/2 x NT/4 sub-tile with
+// v_mfma_f32_16x16x32_bf16.  W is read from HBM once; H (at most 256 x d bf16)
+// stays in L2.  After the last chunk of a tile the waves fold their logits into
+// per-column winners (temperature, masks, Philox-Gumbel noise); the column
+// winners of the two row-halves meet in LDS at the end and become the
+// workgroup's record.
 //
 // Global loads run two chunks ahead: the loads of chunk s+2 are issued before
 // the MFMAs of chunk s into one of two register stages, and chunk s+1 (in the
@@ -28,13 +28,23 @@
 
 namespace fs {
 
-constexpr int kMT = 256;         // rows per tile
-constexpr int kKC = 64;          // k per chunk
-constexpr int kRowBytes = 144;   // LDS row stride: 128 data bytes + 16 pad
+// Tile geometry per column count: rows per tile and k per chunk.  NT = 64
+// takes 128 x 128 (256-byte runs per W row); NT = 128 keeps 256 x 64, where
+// the taller tile's reuse of each H chunk matters more (measured: B = 64
+// 5.09 against 4.96 TB/s, B = 128 4.21 against 3.88).
+template <int NT>
+struct WideGeom {
+    static constexpr int kMT = NT == 64 ? 128 : 256;   // rows per tile
+    static constexpr int kKC = NT == 64 ? 128 : 64;    // k per chunk
+    static constexpr int kTB = kMT / 16;               // 16-row blocks per tile
+    static constexpr int kKS = kKC / 32;               // MFMA k-steps per chunk
+    static constexpr int kPR = kKC * 2 / 16;           // 16-byte pieces per row and chunk
+    static constexpr int kRowBytes = kKC * 2 + 16;     // LDS row stride (16 bytes of pad)
+};
 
 template <int NT>
 struct WideSmem {
-    char buf[2][(kMT + NT) * kRowBytes];
+    char buf[2][(WideGeom<NT>::kMT + NT) * WideGeom<NT>::kRowBytes];
     uint64_t fkey[2][NT];
 };
 
@@ -54,12 +64,15 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
     static_assert((NT == 64 || NT == 128) && NTHR == 512, "column tile and workgroup size");
     static_assert(VAR == kVarFlat || VAR == kVarLogits || (VAR == kVarGrouped && NT == 64),
                   "variant");
+    using Geo = WideGeom<NT>;
+    constexpr int kMT = Geo::kMT, kKC = Geo::kKC, kTB = Geo::kTB, kKS = Geo::kKS;
+    constexpr int kPR = Geo::kPR, kRowBytes = Geo::kRowBytes;
     constexpr int WM = 2, WN = NTHR / 64 / WM;   // wave grid: 2 x 4
-    constexpr int RW = kMT / WM;          // 128 rows per wave
-    constexpr int MF = RW / 16;           // 8 A fragments
+    constexpr int RW = kMT / WM;          // rows per wave
+    constexpr int MF = RW / 16;           // A fragments
     constexpr int NF = NT / WN / 16;      // 1 or 2 B fragments
-    constexpr int WP = kMT * 8 / NTHR;    // W pieces of 16 B per thread per chunk
-    constexpr int HP = NT * 8 / NTHR;     // H pieces
+    constexpr int WP = kMT * kPR / NTHR;  // W pieces of 16 B per thread per chunk
+    constexpr int HP = NT * kPR / NTHR;   // H pieces
     __shared__ WideSmem<NT> sm;
     using TileSmem =
         typename std::conditional<VAR == kVarGrouped, WideTileSmem<NT>, NoWideTiles>::type;
@@ -88,11 +101,13 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
     const int row_end = min(mb1 * kMBlock, a.V);          // one past this range's last row
     const int bbase = y * NT;
     const int nchunks = a.d / kKC;
-    const int ntiles = (mb1 - mb0 + 15) / 16;
+    const int ntiles = (mb1 - mb0 + kTB - 1) / kTB;
     const int total = ntiles * nchunks;
 
-    // cooperative loader: piece q = tid + 512 i covers 16 bytes of row q >> 3
-    // at byte (q & 7) * 16 of the chunk; eight lanes read one whole line.
+    // cooperative loader: piece q = tid + 512 i covers 16 bytes of row q / kPR
+    // at byte (q % kPR) * 16 of the chunk; kPR lanes read a row's whole run
+    // (longer runs per row stream HBM better: a probe of this pattern reads
+    // 5.99 TB/s with 256-byte runs, 5.59 with 128-byte runs).
     // Offsets are 32-bit element offsets from the range's first W row and
     // from H (a range spans a few hundred rows, H at most 256 rows).
     const uint16_t* wbase = a.W + (size_t)mb0 * kMBlock * a.d;
@@ -102,23 +117,23 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
         const int q = tid + NTHR * i;
-        int b = bbase + (q >> 3);
+        int b = bbase + q / kPR;
         b = b < a.B ? b : a.B - 1;   // padding columns reuse row B - 1, discarded later
-        hofs[i] = b * a.d + (q & 7) * 8;
+        hofs[i] = b * a.d + (q % kPR) * 8;
     }
     auto set_tile_rows = [&](int tile) {
 #pragma unroll
         for (int i = 0; i < WP; ++i) {
             const int q = tid + NTHR * i;
-            int row = (mb0 + tile * 16) * kMBlock + (q >> 3);
+            int row = (mb0 + tile * kTB) * kMBlock + q / kPR;
             row = row < row_end ? row : row_end - 1;   // never read another range's rows
-            wofs[i] = (row - first_row) * a.d + (q & 7) * 8;
+            wofs[i] = (row - first_row) * a.d + (q % kPR) * 8;
         }
     };
     // LDS byte offset of piece i of this thread (W rows first, then H rows)
     auto lds_off = [&](int i, int row_base) {
         const int q = tid + NTHR * i;
-        return (row_base + (q >> 3)) * kRowBytes + (q & 7) * 16;
+        return (row_base + q / kPR) * kRowBytes + (q % kPR) * 16;
     };
 
     // two register stages: chunk s+1 waits in one while chunk s+2 is fetched
@@ -198,12 +213,12 @@ __global__ __launch_bounds__(NTHR, 1) void wide_kernel(Stage1Args a) {
         __builtin_amdgcn_sched_barrier(0);
 
         // blocks of this wave that hold rows of the range (the last tile may be short)
-        const int blk0 = mb0 + tile * 16 + wm * MF;
+        const int blk0 = mb0 + tile * kTB + wm * MF;
         const int nvalid = min(MF, mb1 - blk0);
         if (nvalid > 0) {
             const char* base = sm.buf[s & 1];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
+            for (int kk = 0; kk < kKS; ++kk) {
                 bf16x8 bf[NF];
 #pragma unroll
                 for (int n = 0; n < NF; ++n) {
