@@ -201,7 +201,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
             p->d % (p->B <= 64 ? 128 : 64) == 0 && forced < 0 && wide_enabled()) {
             pl.kind = kWide;
-            pl.nt = p->B <= 64 ? 64 : 128;
+            pl.nt = p->B <= 64 ? 64 : p->B <= 128 ? 128 : 256;
         }
         // grouped records up to 64 columns: one workgroup per CU, each range
         // meeting at most 16 vocabulary tiles (its per-tile slots live in LDS)

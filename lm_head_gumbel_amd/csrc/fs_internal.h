@@ -119,6 +119,10 @@ hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const R
 // kWideMaxTiles vocabulary tiles.
 constexpr int kWideMaxTiles = 16;
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream);
+// The same contraction fed by direct-to-LDS loads (fs_wide_dma.hip): flat and
+// logits, nt = 256, d % 32 == 0.
+hipError_t launch_wide_dma(int variant, const Stage1Args& a, int nt, int grid_y,
+                           hipStream_t stream);
 
 // Streaming stage 1 (flat, grouped or logits) over a.G workgroups of four
 // worker waves; `part` holds grid_y * 4 * a.G * 2 * nb KiB of partial sums.

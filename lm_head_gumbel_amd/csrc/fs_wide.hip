@@ -375,6 +375,7 @@ static hipError_t launch_wide_nt(const Stage1Args& a, int grid_y, hipStream_t st
 }
 
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream) {
+    if (nt == 256) return launch_wide_dma(variant, a, nt, grid_y, stream);
     if (variant == kVarGrouped) {
         if (nt == 64) return launch_wide_nt<64, kVarGrouped>(a, grid_y, stream);
         return hipErrorInvalidValue;
