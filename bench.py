@@ -392,16 +392,21 @@ def hbm_probe(torch, fs, W):
             "read_grid": 256, "copy_grid": 1024, "copy_bytes": n}
 
 
+# The sources the headline stage-1 kernel (resident_kernel) and its launch
+# plan are built from.
+DIGEST_SOURCES = ("fs_api.hip", "fs_device.h", "fs_epilogue.h", "fs_internal.h", "fs_mfma.h",
+                  "fs_resident.hip", "fs_topk.h")
+
+
 def source_digest():
-    """sha256 over the stage-1 kernel sources, to tell whether a stored
-    counter summary still describes the kernel being timed."""
+    """sha256 over the headline stage-1 kernel's sources, to tell whether a
+    stored counter summary still describes the kernel being timed."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lm_head_gumbel_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in DIGEST_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
