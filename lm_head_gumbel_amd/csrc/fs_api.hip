@@ -235,20 +235,21 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         pl.G = std::max(1, std::min(pl.nmb, cus * per_cu));
         workers = pl.G;
     }
-    // resident flat and logits stride units of mpi blocks over the workgroups:
-    // at most one workgroup per unit
-    const bool strided = pl.kind == kResident && (variant == kVarFlat || variant == kVarLogits);
-    const int max_g = strided ? (pl.nmb + pl.rcfg.mpi - 1) / pl.rcfg.mpi : pl.nmb;
+    // resident flat, logits and top-k stride units of mpi blocks over the
+    // workgroups: at most one workgroup per unit
+    const bool strided = pl.kind == kResident && variant != kVarGrouped;
+    const int nunits = strided ? (pl.nmb + pl.rcfg.mpi - 1) / pl.rcfg.mpi : pl.nmb;
+    const int max_g = nunits;
     if (pl.G > max_g) {
         pl.G = max_g;
         workers = max_g;
     }
-    // resident top-k keeps the x of its whole range in LDS: enough workgroups
-    // that no range exceeds that store
+    // resident top-k keeps the x of all its units in LDS: enough workgroups
+    // that none holds more units than that store
     int min_g = 1;
     if (variant == kVarTopk && pl.kind == kResident) {
-        const int cap_mb = resident_topk_rows(pl.rcfg) / kMBlock;
-        min_g = (pl.nmb + cap_mb - 1) / cap_mb;
+        const int cap_units = resident_topk_rows(pl.rcfg) / (kMBlock * pl.rcfg.mpi);
+        min_g = (nunits + cap_units - 1) / cap_units;
         if (pl.G < min_g) {
             pl.G = min_g;
             workers = min_g;
@@ -291,20 +292,26 @@ size_t part_bytes(const Plan& pl) {
     return (size_t)pl.grid_y * (4 * pl.G) * 2 * pl.cfg.nb * 1024;
 }
 
-// Entries per top-k candidate list: a range of the resident kernel holds at
-// most ceil(nmb / G) blocks, so a list never needs more than its rows.
-int topk_len(const Plan& pl, int k) {
-    if (pl.kind != kResident) return k;
-    const int64_t rows = (int64_t)((pl.nmb + pl.G - 1) / pl.G) * kMBlock;
-    return (int)std::min<int64_t>(k, rows);
+// Rows a resident top-k workgroup keeps at most: ceil(units / G) units of
+// mpi blocks.
+int64_t resident_topk_wg_rows(const Plan& pl) {
+    const int mpi = pl.rcfg.mpi;
+    const int nunits = (pl.nmb + mpi - 1) / mpi;
+    return (int64_t)((nunits + pl.G - 1) / pl.G) * mpi * kMBlock;
 }
 
-// Dense lists: for k above 64 that reaches every row of the longest range,
-// stage 1 writes the x of each whole range in row order and no ids (the
-// selection happens in stage 2 alone).
+// Entries per top-k candidate list: a list never needs more than the rows of
+// its workgroup.
+int topk_len(const Plan& pl, int k) {
+    if (pl.kind != kResident) return k;
+    return (int)std::min<int64_t>(k, resident_topk_wg_rows(pl));
+}
+
+// Dense lists: for k above 64 that reaches every row of the fullest
+// workgroup, stage 1 writes the x of all its rows in store order and no ids
+// (the selection happens in stage 2 alone).
 bool topk_dense(const Plan& pl, int k) {
-    return pl.kind == kResident && k > kMaxTopKCoop &&
-           (int64_t)k >= (int64_t)((pl.nmb + pl.G - 1) / pl.G) * kMBlock;
+    return pl.kind == kResident && k > kMaxTopKCoop && (int64_t)k >= resident_topk_wg_rows(pl);
 }
 
 size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
@@ -412,7 +419,8 @@ fs_status sample_topk(const fs_params* p, const void* H, const void* W, const fl
     hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
                                         : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
-    const DenseIds dn{a.topk_dense ? pl.nmb : 0, pl.G, pl.v_offset};
+    const int unit_rows = pl.kind == kResident ? pl.rcfg.mpi * kMBlock : kMBlock;
+    const DenseIds dn{a.topk_dense, pl.v_offset, unit_rows, pl.G * unit_rows};
     return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, a.topk_len, pl.B, k, dn, top_p, temp,
                                        p->flags, noise_src(pl, p), out_idx, w.sel, s));
 }

@@ -140,15 +140,26 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                                  float* tile_max, int32_t* tile_idx, float* tile_L,
                                  int32_t* out_idx, hipStream_t stream);
 
-// Candidates [B][G][L] (L entries per list); 1 <= k <= 1024.  With
-// dn.nmb > 0 the lists are dense: list w holds the x of every row of
-// workgroup range w in row order (padded with -inf) and cidx is not read;
-// entry r is id dn.v_offset + 16 part_begin(w, dn.nmb, G) + r.  top_p >= 1:
+// Candidates [B][G][L] (L entries per list); 1 <= k <= 1024.  With dn.on
+// the lists are dense: list w holds the x of every row workgroup w kept, in
+// its store order (padded with -inf), and cidx is not read (ids as DenseIds
+// says).  top_p >= 1:
 // plain top-k; 0 < top_p < 1: top-p after top-k.  scratch: device memory of
 // stage2_topk_scratch_bytes(G, L, B, k, dense) bytes (256-byte aligned; may be null
 // when that is 0) for the lists of the intermediate selection levels.
+// Global ids of the rows a top-k workgroup keeps, in its store order: units of
+// unit_rows consecutive ids, unit_stride apart, the first at base.
+struct RowIds {
+    int base, unit_rows, unit_stride;
+};
+__host__ __device__ inline int row_id(const RowIds& m, int r) {
+    return m.base + (r / m.unit_rows) * m.unit_stride + r % m.unit_rows;
+}
+
+// Dense top-k lists (on != 0): entry r of list w has id row_id({v_offset +
+// w unit_rows, unit_rows, unit_stride}, r).
 struct DenseIds {
-    int nmb, G, v_offset;   // nmb > 0: dense lists, see launch_stage2_topk
+    int on, v_offset, unit_rows, unit_stride;
 };
 size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense);
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,

@@ -147,15 +147,16 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15;
     const int kg = lane >> 4;
-    // Flat and logits walk units of MPI blocks strided by G (unit w, w + G,
-    // w + 2G, ...): at any moment the workgroups read neighbouring parts of W,
-    // which streams HBM better than one contiguous range per workgroup (6.10
-    // against 5.78 TB/s at B = 32, d = 4096, V = 151936).  Any partition gives
-    // the same flat sample (the noise is keyed by the global id).  Grouped
-    // records (one per workgroup and tile) and the top-k row store need a
-    // contiguous range [mb0, mb1).  Strided: mb0 is the first block, mb1 one
-    // past the last unit's blocks.
-    constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits;
+    // Flat, logits and top-k walk units of MPI blocks strided by G (unit w,
+    // w + G, w + 2G, ...): at any moment the workgroups read neighbouring
+    // parts of W, which streams HBM better than one contiguous range per
+    // workgroup (6.10 against 5.78 TB/s at B = 32, d = 4096, V = 151936).  Any
+    // partition gives the same flat sample (the noise is keyed by the global
+    // id) and the same top-k set (the row store maps back to global ids).
+    // Grouped records (one per workgroup and tile) need a contiguous range
+    // [mb0, mb1).  Strided: mb0 is the first block, mb1 one past the last
+    // unit's blocks.
+    constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits || VAR == kVarTopk;
     int mb0, mb1;
     if constexpr (kStrided) {
         const int nunits = (a.nmb + MPI - 1) / MPI;   // the host keeps G <= nunits
@@ -209,6 +210,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     uint64_t best = pack_key(-INFINITY, -1);
     Lse lse = lse_empty();
     int buf = 0;
+    int stored = 0;   // top-k: blocks in the row store (the workgroup's blocks in walk order)
     while (true) {
         // (strided: only a workgroup's last unit can be short, so the group
         // and its record segment end together there)
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             } else if constexpr (VAR == kVarTopk) {
                 float x[4];
                 lane_x(a, cc, v, row0, true, x);
-                *reinterpret_cast<f32x4*>(&tk.x[ncol * 16 + r16][row0 - mb0 * kMBlock]) =
+                *reinterpret_cast<f32x4*>(&tk.x[ncol * 16 + r16][(stored + j) * kMBlock + 4 * kg]) =
                     f32x4{x[0], x[1], x[2], x[3]};
             } else {
                 float x[4], s[4];
@@ -285,6 +287,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // the next group writes the other buffer; this one is rewritten two
         // groups on, after every wave has passed the next group's barrier
         buf ^= 1;
+        stored += cur.nvm;
 
         if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
             if (cur.g + cur.nvm == cur.seg_end) {   // a record segment ends here
@@ -320,8 +323,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     }
 
     if constexpr (VAR == kVarTopk) {
-        // every row of the range is in LDS: each wave selects for its columns
-        // wave, wave + NW, ... all at once
+        // every row of the workgroup's units is in LDS, store row r being
+        // global id row_id(ids, r): each wave selects for its columns wave,
+        // wave + NW, ... all at once
         constexpr int C = (16 * NB + NW - 1) / NW;
         __syncthreads();
         float* xc[C];
@@ -335,12 +339,13 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             xc[q] = tk.x[ok ? cl : wave];
             o[q] = ((size_t)(bbase + (ok ? cl : 0)) * a.G + w) * a.topk_len;
         }
+        const RowIds ids{a.v_offset + mb0 * kMBlock, MPI * kMBlock, a.G * MPI * kMBlock};
         if (nc > 0) {
             if (a.topk_dense)
-                topk_write_dense<C>(a, nc, xc, (mb1 - mb0) * kMBlock, o);
+                topk_write_dense<C>(a, nc, xc, stored * kMBlock, o);
             else
-                topk_select_columns<C, TopkRows<NB, HL>::kRows / 64>(
-                    a, nc, xc, (mb1 - mb0) * kMBlock, a.v_offset + mb0 * kMBlock, o);
+                topk_select_columns<C, TopkRows<NB, HL>::kRows / 64>(a, nc, xc, stored * kMBlock,
+                                                                     ids, o);
         }
     }
 }

@@ -492,7 +492,6 @@ struct SelSmem {
     uint64_t gk[kMaxK];        // the selection
     uint64_t tk[kTieCap];      // the tie bin's keys
     uint32_t hist[kBins];
-    int wbase[kSliceCap / 16 + 2];   // dense lists: first id of each list of the slice
     int islot[kSelWaves];
     double dslot[kSelWaves];
     uint64_t kslot[kSelWaves];
@@ -505,11 +504,12 @@ struct SelSmem {
 // Slice blockIdx.x of row blockIdx.y: candidates e in [e0, e0 + n) of the
 // row's G lists of L entries (candidate e is entry e % L of list e / L, at
 // offset b * G * L + e: a row's lists are contiguous); thread t holds entries
-// t + 1024 j in registers.  DENSE: the lists are whole vocabulary ranges in
-// row order and carry no ids (entry r of list w is id v_offset + 16
-// part_begin(w, nmb, G) + r).  FINISH == false: writes the slice's selection
-// as list blockIdx.x of length k of ox / oidx ([B][S][k], padding (-inf,
-// -1)).  FINISH == true (one slice): the draw, to out_idx[b].
+// t + 1024 j in registers.  DENSE: list w holds every row stage-1
+// workgroup w kept, in its store order, and no ids (entry r is id v_offset +
+// w u + (r / u) unit_stride + r % u, u = unit_rows, a power of two).
+// FINISH == false: writes the slice's selection as list blockIdx.x of
+// length k of ox / oidx ([B][S][k], padding (-inf, -1)).  FINISH == true
+// (one slice): the draw, to out_idx[b].
 template <bool FINISH, bool DENSE>
 __global__ __launch_bounds__(kSelThreads) void stage2_topk_select_kernel(
     const float* cx, const int32_t* cidx, int G, int L, int B, int k, int per_slice,
@@ -526,19 +526,12 @@ __global__ __launch_bounds__(kSelThreads) void stage2_topk_select_kernel(
         sm.cnt = 0;
     }
     for (int i = threadIdx.x; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
-    if constexpr (DENSE) {
-        // the first id of each list the slice touches
-        const int nw = (e0 + n - 1) / L - e0 / L + 1;
-        for (int i = threadIdx.x; i < nw; i += kSelThreads)
-            sm.wbase[i] = dn.v_offset + part_begin(e0 / L + i, dn.nmb, dn.G) * kMBlock;
-        __syncthreads();
-    }
 
     // the slice into registers.  The loads are unconditional (slots past the
     // slice re-read its first entry and are then dropped), so that all of
     // them are in flight together.  x = -inf: no candidate.
     float x[kSelPer];
-    int32_t id[DENSE ? 1 : kSelPer];   // dense lists: ids from sm.wbase
+    int32_t id[DENSE ? 1 : kSelPer];   // dense lists: ids from the position
     {
         const float* xs = cx + (size_t)b * G * L + e0;
         const int32_t* is = cidx + (size_t)b * G * L + e0;
@@ -556,13 +549,13 @@ __global__ __launch_bounds__(kSelThreads) void stage2_topk_select_kernel(
     }
     // (list, entry) of entry j: steps of (1024 / L, 1024 % L) from the first
     const int dq = kSelThreads / L, dr = kSelThreads % L;
-    const int w_lo = e0 / L;
+    const int ush = __builtin_ctz((unsigned)dn.unit_rows);   // dense: unit_rows = 2^ush
+    const int umask = dn.unit_rows - 1;
     const int w_start = (e0 + (int)threadIdx.x) / L;
     const int r_start = e0 + (int)threadIdx.x - w_start * L;
     // Visits this thread's entries in order: fn(j, id_of), id_of() giving
-    // the id of entry j (for dense lists the list's first id plus the
-    // position, with (list, entry) stepped along, so that it is only read
-    // where it is used).
+    // the id of entry j (for dense lists computed from (list, entry),
+    // stepped along, so that it is only formed where it is used).
     auto walk = [&](auto fn) {
         int w = w_start, r = r_start;
         if constexpr (DENSE) {
@@ -574,7 +567,7 @@ __global__ __launch_bounds__(kSelThreads) void stage2_topk_select_kernel(
         for (int j = 0; j < kSelPer; ++j) {
             auto id_of = [&]() -> int32_t {
                 if constexpr (DENSE)
-                    return sm.wbase[w - w_lo] + r;
+                    return dn.v_offset + (w << ush) + (r >> ush) * dn.unit_stride + (r & umask);
                 else
                     return id[j];
             };
@@ -1059,7 +1052,7 @@ hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L
                               const NoiseSrc& noise, int32_t* out_idx, void* scratch,
                               hipStream_t stream) {
     if (k < 1 || k > kMaxK || L < 1 || G < 1) return hipErrorInvalidValue;
-    const bool dense = dn.nmb > 0;
+    const bool dense = dn.on != 0;
 #define FS_TOPK2(PER_)                                                                       \
     if (!dense && k <= 64 && (int64_t)G * L <= (int64_t)kTopkThreads * PER_) {             \
         hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \

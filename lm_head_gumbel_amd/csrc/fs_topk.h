@@ -139,10 +139,10 @@ __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uin
 
 // Writes the (x, id) of the marked entries of set c to its candidate list
 // (ballot-prefix order, positions 0, 1, ...); returns their number.
-// rowx(c, i, row, x) gives an entry; ids are gid0 + row.
+// rowx(c, i, row, x) gives an entry; ids are row_id(ids, row).
 template <int C, int M, typename RowX>
 __device__ __forceinline__ int write_selected(const Stage1Args& a, const bool (&sel)[C][M], int c,
-                                              RowX rowx, int gid0, size_t o) {
+                                              RowX rowx, const RowIds& ids, size_t o) {
     const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
     int nsel = 0;
 #pragma unroll
@@ -154,7 +154,7 @@ __device__ __forceinline__ int write_selected(const Stage1Args& a, const bool (&
             float x;
             rowx(c, i, row, x);
             a.cx[o + pos] = x;
-            a.cidx[o + pos] = gid0 + row;
+            a.cidx[o + pos] = row_id(ids, row);
         }
         nsel += __popcll(sb);
     }
@@ -183,7 +183,7 @@ __device__ __forceinline__ void topk_write_dense(const Stage1Args& a, int nc,
 
 // One wave, C columns at once: the top-k candidates of rows [0, nr) of C
 // columns (c < nc are real) whose x sit in LDS at xc[c][row] (row r is
-// global id gid0 + r; each xc[c] is 16-byte aligned, holds NR * 64 >= 640
+// global id row_id(ids, r), increasing in r; each xc[c] is 16-byte aligned, holds NR * 64 >= 640
 // entries plus at least two of padding, and is overwritten).  Writes the
 // min(k, valid rows) candidates (x, id) of column c at offset o[c] of a.cx /
 // a.cidx and fills the list's other slots, up to a.topk_len >= min(k, nr),
@@ -198,8 +198,8 @@ __device__ __forceinline__ void topk_write_dense(const Stage1Args& a, int nc,
 // all entries, one column at a time).
 template <int C, int NR>
 __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
-                                                   float* const (&xc)[C], int nr, int gid0,
-                                                   const size_t (&o)[C]) {
+                                                   float* const (&xc)[C], int nr,
+                                                   const RowIds& ids, const size_t (&o)[C]) {
     static_assert(NR % 2 == 0 && NR * 64 >= 640, "row store of at least 640 entries");
     constexpr int kDummy = 640;   // write target of lanes that keep nothing (padding)
     constexpr int PK = NR % 4 == 0 ? 4 : 2;   // entries per LDS read
@@ -296,7 +296,7 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
                 if (c < nc)
                     nsel[c] = write_selected<C, 1>(
                         a, sel, c, [&](int cc, int, int& row, float& x) { row = vr[cc][0]; x = vx[cc][0]; },
-                        gid0, o[c]);
+                        ids, o[c]);
         } else {
             // one column at a time, up to two or four survivors per lane
             auto run1 = [&](int c, auto m_tag) {
@@ -315,7 +315,7 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
                 }
                 wave_select<1, M>(v, tb, k, sel);
                 return write_selected<1, M>(
-                    a, sel, 0, [&](int, int j, int& row, float& x) { row = vr[j]; x = vx[j]; }, gid0,
+                    a, sel, 0, [&](int, int j, int& row, float& x) { row = vr[j]; x = vx[j]; }, ids,
                     o[c]);
             };
 #pragma unroll
@@ -343,7 +343,7 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
                         row = row_of(i);
                         x = ordered_to_float(uc[0][i]);
                     },
-                    gid0, o[c]);
+                    ids, o[c]);
         }
     }
     // unused slots of the lists
