@@ -91,11 +91,11 @@ struct ResidentSmem {
     float fsm[NW][16];
 };
 
-// Top-k: x of the workgroup's rows, one padded row of LDS per column (also
-// the scratch area of the column's selection).
+// Top-k: order images of the x of the workgroup's rows, one padded row of
+// LDS per column (also the scratch area of the column's selection).
 template <int NB, int NW, int HL>
 struct TopkRowsSmem {
-    alignas(16) float x[16 * NB][TopkRows<NB, HL>::kStride];
+    alignas(16) uint32_t u[16 * NB][TopkRows<NB, HL>::kStride];
 };
 struct NoTopkRows {};
 
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             } else if constexpr (VAR == kVarTopk) {
                 float x[4];
                 lane_x(a, cc, v, row0, true, x);
-                *reinterpret_cast<f32x4*>(&tk.x[ncol * 16 + r16][(stored + j) * kMBlock + 4 * kg]) =
-                    f32x4{x[0], x[1], x[2], x[3]};
+                *reinterpret_cast<uint4*>(&tk.u[ncol * 16 + r16][(stored + j) * kMBlock + 4 * kg]) =
+                    uint4{topk_order(x[0]), topk_order(x[1]), topk_order(x[2]), topk_order(x[3])};
             } else {
                 float x[4], s[4];
                 lane_scores(a, cc, v, row0, true, x, s);
@@ -326,26 +326,31 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // every row of the workgroup's units is in LDS, store row r being
         // global id row_id(ids, r): each wave selects for its columns wave,
         // wave + NW, ... all at once
-        constexpr int C = (16 * NB + NW - 1) / NW;
+        static_assert((16 * NB) % NW == 0, "every wave selects for the same number of columns");
+        constexpr int C = 16 * NB / NW;
+        constexpr int kRows = TopkRows<NB, HL>::kRows;
+        // rows past the workgroup's hold no candidate
+        const int nr = stored * kMBlock;
+        for (int e = threadIdx.x; e < 16 * NB * (kRows - nr); e += 64 * NW)
+            tk.u[e % (16 * NB)][nr + e / (16 * NB)] = 0u;
         __syncthreads();
-        float* xc[C];
+        uint32_t* uc[C];
         size_t o[C];
         int nc = 0;
 #pragma unroll
         for (int q = 0; q < C; ++q) {
             const int cl = wave + NW * q;
-            const bool ok = cl < 16 * NB && bbase + cl < a.B;
+            const bool ok = bbase + cl < a.B;
             nc += ok ? 1 : 0;   // valid columns come first
-            xc[q] = tk.x[ok ? cl : wave];
+            uc[q] = tk.u[cl];
             o[q] = ((size_t)(bbase + (ok ? cl : 0)) * a.G + w) * a.topk_len;
         }
         const RowIds ids{a.v_offset + mb0 * kMBlock, MPI * kMBlock, a.G * MPI * kMBlock};
         if (nc > 0) {
             if (a.topk_dense)
-                topk_write_dense<C>(a, nc, xc, stored * kMBlock, o);
+                topk_write_dense<C>(a, nc, uc, nr, o);
             else
-                topk_select_columns<C, TopkRows<NB, HL>::kRows / 64>(a, nc, xc, stored * kMBlock,
-                                                                     ids, o);
+                topk_select_columns<C, kRows / 64>(a, nc, uc, nr, ids, o);
         }
     }
 }

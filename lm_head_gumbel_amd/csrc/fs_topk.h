@@ -21,6 +21,9 @@
 
 namespace fs {
 
+// Order image of x for the selection: increasing in x, 0 for -inf (no
+// candidate).  (x is never -0: the MFMA sums start from +0, and a sum that
+// cancels to zero rounds to +0.)
 __device__ __forceinline__ uint32_t topk_order(float x) {
     return x > -INFINITY ? float_to_ordered(x) : 0u;
 }
@@ -51,25 +54,46 @@ __device__ __forceinline__ float token_gumbel(uint32_t k0, uint32_t k1, uint32_t
     return gumbel_from_word(word);
 }
 
+// Lanes where pred(i) holds, summed over a lane's M predicates: each
+// predicate is one compare straight into a lane mask and a scalar bit count
+// (the M compares are issued before the counts are added).
+template <int M, typename P>
+__device__ __forceinline__ int wave_count_each(P pred) {
+    uint64_t m[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) m[i] = __builtin_amdgcn_ballot_w64(pred(i));
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) n += __popcll(m[i]);
+    return n;
+}
+
 // The k-th largest of the 64 * M values of each of C sets (M per lane), or
 // 0 when a set holds fewer than k nonzero values; bit by bit from the top,
-// every count a wave ballot.  With LOW > 0 the search stops above bit LOW:
-// the result is then the k-th largest value with its low LOW bits cleared,
-// still a value that at least k entries reach (a lower bound).  The C
-// searches run interleaved: each step is a short chain of vector compare,
-// ballot count and scalar select, so interleaving hides its latency.
+// every count a set of wave ballots.  With LOW > 0 the search stops above
+// bit LOW: the result is then the k-th largest value with its low LOW bits
+// cleared, still a value that at least k entries reach (a lower bound).  The
+// C searches are independent chains of compare, bit count and scalar select;
+// their compares are issued together.
 template <int C, int M, int LOW = 0>
 __device__ __forceinline__ void wave_kth(const uint32_t (&v)[C][M], int k, uint32_t (&t)[C]) {
 #pragma unroll
     for (int c = 0; c < C; ++c) t[c] = 0;
     for (int bit = 31; bit >= LOW; --bit) {
+        uint32_t cand[C];
+        uint64_t m[C][M];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const uint32_t cand = t[c] | (1u << bit);
+            cand[c] = t[c] | (1u << bit);
+#pragma unroll
+            for (int i = 0; i < M; ++i) m[c][i] = __builtin_amdgcn_ballot_w64(v[c][i] >= cand[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
             int n = 0;
 #pragma unroll
-            for (int i = 0; i < M; ++i) n += v[c][i] >= cand ? 1 : 0;
-            if (wave_sum<M>(n) >= k) t[c] = cand;
+            for (int i = 0; i < M; ++i) n += __popcll(m[c][i]);
+            if (n >= k) t[c] = cand[c];
         }
     }
 }
@@ -82,19 +106,13 @@ __device__ __forceinline__ void wave_kth(const uint32_t (&v)[C][M], int k, uint3
 template <int C, int M>
 __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uint32_t (&tb)[C][M],
                                             int k, bool (&sel)[C][M]) {
-    auto count = [&](int c, auto pred) {
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < M; ++i) n += pred(c, i) ? 1 : 0;
-        return wave_sum<M>(n);
-    };
     // per set: take u > t, and u == t with tb >= tt (t, tt wave-uniform)
     uint32_t t[C], tt[C];
     bool big[C];
     int need[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        big[c] = count(c, [&](int cc, int i) { return u[cc][i] >= 1u; }) > k;
+        big[c] = wave_count_each<M>([&](int i) { return u[c][i] >= 1u; }) > k;
         t[c] = 0;
         tt[c] = 0;
     }
@@ -103,10 +121,20 @@ __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uin
     for (int c = 0; c < C; ++c) any_big = any_big || big[c];
     // (with at most k real entries in every set there is nothing to search)
     for (int bit = 31; any_big && bit >= 0; --bit) {
+        uint32_t cand[C];
+        uint64_t m[C][M];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const uint32_t cand = t[c] | (1u << bit);
-            if (count(c, [&](int cc, int i) { return u[cc][i] >= cand; }) >= k) t[c] = cand;
+            cand[c] = t[c] | (1u << bit);
+#pragma unroll
+            for (int i = 0; i < M; ++i) m[c][i] = __builtin_amdgcn_ballot_w64(u[c][i] >= cand[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < M; ++i) n += __popcll(m[c][i]);
+            if (n >= k) t[c] = cand[c];
         }
     }
     bool any_tie = false;
@@ -114,8 +142,8 @@ __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uin
     for (int c = 0; c < C; ++c) {
         if (!big[c]) t[c] = 0;   // at most k: every real entry
         // t >= 1 for a big set, and t + 1 does not wrap (t is at most the image of +inf)
-        need[c] = big[c] ? k - count(c, [&](int cc, int i) { return u[cc][i] > t[cc]; }) : 0;
-        big[c] = big[c] && count(c, [&](int cc, int i) { return u[cc][i] == t[cc]; }) > need[c];
+        need[c] = big[c] ? k - wave_count_each<M>([&](int i) { return u[c][i] > t[c]; }) : 0;
+        big[c] = big[c] && wave_count_each<M>([&](int i) { return u[c][i] == t[c]; }) > need[c];
         any_tie = any_tie || big[c];
     }
     if (any_tie) {   // more equal values at t than places: the largest tb among them
@@ -123,8 +151,8 @@ __device__ __forceinline__ void wave_select(const uint32_t (&u)[C][M], const uin
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const uint32_t cand = tt[c] | (1u << bit);
-                if (big[c] && count(c, [&](int cc, int i) {
-                        return u[cc][i] == t[cc] && tb[cc][i] >= cand;
+                if (big[c] && wave_count_each<M>([&](int i) {
+                        return u[c][i] == t[c] && tb[c][i] >= cand;
                     }) >= need[c])
                     tt[c] = cand;
             }
@@ -161,30 +189,39 @@ __device__ __forceinline__ int write_selected(const Stage1Args& a, const bool (&
     return nsel;
 }
 
-// Dense lists (k reaches every row of the longest range): the x of rows
-// [0, nr) of each of the nc columns, in row order, then -inf up to
-// a.topk_len; the ids are implied by the position.  a.topk_len and nr are
-// multiples of 16 and the list offsets o[c] multiples of a.topk_len.
+// x of an order image (0: no candidate, -inf).
+__device__ __forceinline__ float topk_value(uint32_t u) {
+    return u ? ordered_to_float(u) : -INFINITY;
+}
+
+// Dense lists (k reaches every row of the fullest workgroup): the x of rows
+// [0, nr) of each of the nc columns, in store order, then -inf up to
+// a.topk_len; the ids are implied by the position.  The store holds order
+// images (topk_order); a.topk_len and nr are multiples of 16 and the list
+// offsets o[c] multiples of a.topk_len.
 template <int C>
 __device__ __forceinline__ void topk_write_dense(const Stage1Args& a, int nc,
-                                                 float* const (&xc)[C], int nr,
+                                                 uint32_t* const (&uc)[C], int nr,
                                                  const size_t (&o)[C]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         if (c >= nc) break;
         for (int r = 4 * lane; r < a.topk_len; r += 256) {
-            const f32x4 v = r < nr ? *reinterpret_cast<const f32x4*>(xc[c] + r)
-                                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            *reinterpret_cast<f32x4*>(a.cx + o[c] + r) = v;
+            const uint4 v = r < nr ? *reinterpret_cast<const uint4*>(uc[c] + r)
+                                   : uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<f32x4*>(a.cx + o[c] + r) =
+                f32x4{topk_value(v.x), topk_value(v.y), topk_value(v.z), topk_value(v.w)};
         }
     }
 }
 
-// One wave, C columns at once: the top-k candidates of rows [0, nr) of C
-// columns (c < nc are real) whose x sit in LDS at xc[c][row] (row r is
-// global id row_id(ids, r), increasing in r; each xc[c] is 16-byte aligned, holds NR * 64 >= 640
-// entries plus at least two of padding, and is overwritten).  Writes the
+// One wave, C columns at once: the top-k candidates of the rows of C
+// columns whose order images (topk_order of x) sit in LDS at uc[c][row]:
+// rows [0, nr) are the workgroup's, rows [nr, 64 NR) hold 0, and row r is
+// global id row_id(ids, r), increasing in r.  Each uc[c] is 16-byte
+// aligned, belongs to this wave alone and is overwritten.  Columns c >= nc
+// are not real: their candidates are not written.  Writes the
 // min(k, valid rows) candidates (x, id) of column c at offset o[c] of a.cx /
 // a.cidx and fills the list's other slots, up to a.topk_len >= min(k, nr),
 // with (-inf, -1).  The noise is drawn later, for the row's final k only.
@@ -193,18 +230,20 @@ __device__ __forceinline__ void topk_write_dense(const Stage1Args& a, int nc,
 // values is at most the column's k-th largest value (k of the column's
 // values are at least that large; for k > 128 there is no such bound and
 // every valid value is a survivor).  Usually little more than k values reach
-// it; those are compacted to one per lane and the exact selection runs on
-// them, all C columns interleaved (other paths take up to four per lane, or
-// all entries, one column at a time).
+// it; those are compacted to one (value, row) pair per lane and the exact
+// selection runs on them, all C columns interleaved (other paths take up to
+// four per lane, or all entries, one column at a time).
 template <int C, int NR>
 __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
-                                                   float* const (&xc)[C], int nr,
+                                                   uint32_t* const (&uc)[C], int nr,
                                                    const RowIds& ids, const size_t (&o)[C]) {
     static_assert(NR % 2 == 0 && NR * 64 >= 640, "row store of at least 640 entries");
-    constexpr int kDummy = 640;   // write target of lanes that keep nothing (padding)
+    constexpr int kCap = 256;     // compacted pairs per column
+    constexpr int kDummy = 300;   // pair slot written by lanes that keep nothing
     constexpr int PK = NR % 4 == 0 ? 4 : 2;   // entries per LDS read
     const int lane = threadIdx.x & 63;
     const int k = a.topk;
+    (void)nr;
     // entry i = PK * q + j of this lane is row 64 PK q + PK lane + j
     auto row_of = [&](int i) { return 64 * PK * (i / PK) + PK * lane + (i % PK); };
     uint32_t u[C][NR];
@@ -214,23 +253,20 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
         top[c][0] = top[c][1] = 0;
 #pragma unroll
         for (int q = 0; q < NR / PK; ++q) {
-            float vq[PK];
             if constexpr (PK == 4) {
-                const f32x4 v4 = *reinterpret_cast<const f32x4*>(xc[c] + 256 * q + 4 * lane);
-                vq[0] = v4[0];
-                vq[1] = v4[1];
-                vq[2] = v4[2];
-                vq[3] = v4[3];
+                const uint4 v4 = *reinterpret_cast<const uint4*>(uc[c] + 256 * q + 4 * lane);
+                u[c][4 * q] = v4.x;
+                u[c][4 * q + 1] = v4.y;
+                u[c][4 * q + 2] = v4.z;
+                u[c][4 * q + 3] = v4.w;
             } else {
-                const float2 v2 = *reinterpret_cast<const float2*>(xc[c] + 128 * q + 2 * lane);
-                vq[0] = v2.x;
-                vq[1] = v2.y;
+                const uint2 v2 = *reinterpret_cast<const uint2*>(uc[c] + 128 * q + 2 * lane);
+                u[c][2 * q] = v2.x;
+                u[c][2 * q + 1] = v2.y;
             }
 #pragma unroll
             for (int j = 0; j < PK; ++j) {
-                const int i = PK * q + j;
-                const uint32_t v = (c < nc && row_of(i) < nr) ? topk_order(vq[j]) : 0u;
-                u[c][i] = v;
+                const uint32_t v = u[c][PK * q + j];
                 const uint32_t lo2 = v < top[c][0] ? v : top[c][0];
                 top[c][0] = v > top[c][0] ? v : top[c][0];
                 top[c][1] = lo2 > top[c][1] ? lo2 : top[c][1];
@@ -244,33 +280,28 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         lo[c] = lo[c] > 1u ? lo[c] : 1u;
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) n += u[c][i] >= lo[c] ? 1 : 0;
-        n = wave_sum<NR>(n);
-        nmax = n > nmax ? n : nmax;
+        const int n = wave_count_each<NR>([&](int i) { return u[c][i] >= lo[c]; });
+        if (c < nc) nmax = n > nmax ? n : nmax;
     }
 
     int nsel[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) nsel[c] = 0;
-    if (nmax <= 256) {
-        // compact the values >= lo: x to xc[c][0, 256), rows to xc[c][256, 512)
+    if (nmax <= kCap) {
+        // compact the values >= lo as (u, row) pairs to uc[c][0, 2 kCap)
         // (every lane has read its entries above)
         int cnt[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            int* crow = reinterpret_cast<int*>(xc[c]);
+            uint2* pair = reinterpret_cast<uint2*>(uc[c]);
             int base = 0;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const bool keep = u[c][i] >= lo[c];
-                const uint64_t kb = __ballot(keep);
-                const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                           (uint32_t)(kb >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0u));
-                xc[c][keep ? pos : kDummy] = ordered_to_float(u[c][i]);
-                crow[keep ? 256 + pos : kDummy + 1] = row_of(i);
+                const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+                const int pos = (int)__builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, (uint32_t)base));
+                pair[keep ? pos : kDummy] = uint2{u[c][i], (uint32_t)row_of(i)};
                 base += __popcll(kb);
             }
             cnt[c] = base;
@@ -280,43 +311,45 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
         if (nmax <= 64) {
             // the usual case: one survivor per lane, the C columns interleaved
             uint32_t v[C][1], tb[C][1];
-            float vx[C][1];
-            int vr[C][1];
             bool sel[C][1];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                vx[c][0] = xc[c][lane];
-                vr[c][0] = reinterpret_cast<const int*>(xc[c])[256 + lane];
-                v[c][0] = lane < cnt[c] ? topk_order(vx[c][0]) : 0u;
-                tb[c][0] = ~(uint32_t)vr[c][0];
+                const uint2 pr = reinterpret_cast<const uint2*>(uc[c])[lane];
+                v[c][0] = lane < cnt[c] ? pr.x : 0u;
+                tb[c][0] = ~pr.y;
             }
             wave_select<C, 1>(v, tb, k, sel);
 #pragma unroll
             for (int c = 0; c < C; ++c)
                 if (c < nc)
                     nsel[c] = write_selected<C, 1>(
-                        a, sel, c, [&](int cc, int, int& row, float& x) { row = vr[cc][0]; x = vx[cc][0]; },
+                        a, sel, c,
+                        [&](int cc, int, int& row, float& x) {
+                            row = (int)~tb[cc][0];
+                            x = topk_value(v[cc][0]);
+                        },
                         ids, o[c]);
         } else {
             // one column at a time, up to two or four survivors per lane
             auto run1 = [&](int c, auto m_tag) {
                 constexpr int M = decltype(m_tag)::value;
                 uint32_t v[1][M], tb[1][M];
-                float vx[M];
-                int vr[M];
                 bool sel[1][M];
 #pragma unroll
                 for (int j = 0; j < M; ++j) {
                     const int q = lane + 64 * j;
-                    vx[j] = xc[c][q];
-                    vr[j] = reinterpret_cast<const int*>(xc[c])[256 + q];
-                    v[0][j] = q < cnt[c] ? topk_order(vx[j]) : 0u;
-                    tb[0][j] = ~(uint32_t)vr[j];
+                    const uint2 pr = reinterpret_cast<const uint2*>(uc[c])[q];
+                    v[0][j] = q < cnt[c] ? pr.x : 0u;
+                    tb[0][j] = ~pr.y;
                 }
                 wave_select<1, M>(v, tb, k, sel);
                 return write_selected<1, M>(
-                    a, sel, 0, [&](int, int j, int& row, float& x) { row = vr[j]; x = vx[j]; }, ids,
-                    o[c]);
+                    a, sel, 0,
+                    [&](int, int j, int& row, float& x) {
+                        row = (int)~tb[0][j];
+                        x = topk_value(v[0][j]);
+                    },
+                    ids, o[c]);
             };
 #pragma unroll
             for (int c = 0; c < C; ++c)
@@ -329,21 +362,22 @@ __device__ __forceinline__ void topk_select_columns(const Stage1Args& a, int nc,
         // exact selection on every entry, one column at a time
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            uint32_t uc[1][NR], tb[1][NR];
+            if (c >= nc) break;
+            uint32_t ucol[1][NR], tb[1][NR];
             bool sel[1][NR];
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                uc[0][i] = u[c][i];
+                ucol[0][i] = u[c][i];
                 tb[0][i] = ~(uint32_t)row_of(i);
             }
-            wave_select<1, NR>(uc, tb, k, sel);
-            if (c < nc)
-                nsel[c] = write_selected<1, NR>(
-                    a, sel, 0, [&](int, int i, int& row, float& x) {
-                        row = row_of(i);
-                        x = ordered_to_float(uc[0][i]);
-                    },
-                    ids, o[c]);
+            wave_select<1, NR>(ucol, tb, k, sel);
+            nsel[c] = write_selected<1, NR>(
+                a, sel, 0,
+                [&](int, int i, int& row, float& x) {
+                    row = row_of(i);
+                    x = topk_value(ucol[0][i]);
+                },
+                ids, o[c]);
         }
     }
     // unused slots of the lists
