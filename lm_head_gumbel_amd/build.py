@@ -23,8 +23,10 @@ def hipcc():
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-# Extra device-compiler flags per source (none at present).
-EXTRA_FLAGS = {}
+# Extra device-compiler flags per source.  fs_resident.hip: no wave-level
+# rewriting of atomics (it would read the ticket back at once, waiting for
+# every load in flight; the kernel uses it only after the contraction).
+EXTRA_FLAGS = {"fs_resident.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def common_flags():

@@ -283,6 +283,7 @@ struct Workspace {
     float* ms = nullptr;
     uint64_t* mkey = nullptr;
     void* part = nullptr;   // streaming stage 1: parked partial sums of split blocks
+    SchedState* sched = nullptr;   // flat: unit scheduler block (kept from call to call)
     void* sel = nullptr;    // top-k: lists of the intermediate selection levels
 };
 
@@ -298,6 +299,25 @@ int64_t resident_topk_wg_rows(const Plan& pl) {
     const int mpi = pl.rcfg.mpi;
     const int nunits = (pl.nmb + mpi - 1) / mpi;
     return (int64_t)((nunits + pl.G - 1) / pl.G) * mpi * kMBlock;
+}
+
+// Units each workgroup of the resident flat stage 1 takes in the strided
+// order before it turns to the ticket counter (0: strided order only).  Each
+// ticket costs its workgroup a wait behind the ticket's round trip, so only
+// about the last kDynDepth units per workgroup come by ticket: enough to
+// even out the workgroups' finishing times.  One batch group and at least
+// three units per workgroup; FS_DYN=<depth> overrides the depth and FS_DYN=0
+// switches the tickets off (tuning experiments).
+int dynamic_k0(const Plan& pl) {
+    static const int depth = [] {
+        const char* e = std::getenv("FS_DYN");
+        return e ? std::atoi(e) : 2;
+    }();
+    if (depth <= 0 || pl.kind != kResident || pl.grid_y != 1 || pl.xcd_pair) return 0;
+    const int nunits = (pl.nmb + pl.rcfg.mpi - 1) / std::max(1, pl.rcfg.mpi);
+    const int per = nunits / pl.G;   // units every workgroup has in the strided order
+    const int k0 = std::max(3, per - depth);
+    return per >= 3 ? k0 : 0;
 }
 
 // Entries per top-k candidate list: a list never needs more than the rows of
@@ -328,7 +348,14 @@ size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
         char* b = take(P * B * 4);
         char* c = variant == FS_VARIANT_GROUPED ? take(P * B * 4) : nullptr;
         char* d = pl.stream ? take(part_bytes(pl)) : nullptr;
-        if (w) { w->pm = (float*)a; w->pidx = (int32_t*)b; w->pL = (float*)c; w->part = d; }
+        char* e = variant == FS_VARIANT_FLAT ? take(sizeof(SchedState)) : nullptr;
+        if (w) {
+            w->pm = (float*)a;
+            w->pidx = (int32_t*)b;
+            w->pL = (float*)c;
+            w->part = d;
+            w->sched = (SchedState*)e;
+        }
     } else if (variant == FS_VARIANT_TOPK) {
         const int L = topk_len(pl, k);
         const bool dense = topk_dense(pl, k);
@@ -488,6 +515,8 @@ static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, c
     Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
     a.pm = w.pm;
     a.pidx = w.pidx;
+    a.dyn_k0 = dynamic_k0(pl);
+    a.sched = a.dyn_k0 > 0 ? w.sched : nullptr;
     const hipError_t e =
         pl.kind == kWide       ? launch_wide(kVarFlat, a, pl.nt, pl.grid_y, s)
         : pl.kind == kResident ? launch_resident(kVarFlat, a, pl.grid_y, pl.rcfg, s)
@@ -508,7 +537,7 @@ fs_status fs_sample(const fs_params* p, const void* H, const void* W, const floa
     fs_status st = flat_stage1(p, H, W, temp, allow, out_idx, out_score, ws, ws_bytes, s, true,
                                pl, w, done);
     if (st != FS_OK || done) return st;
-    return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.P, pl.B, out_idx, out_score, s));
+    return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.P, pl.B, out_idx, out_score, w.sched, s));
 }
 
 fs_status fs_sample_stage1(const fs_params* p, const void* H, const void* W, const float* temp,

@@ -49,6 +49,23 @@ __host__ __device__ inline WorkerRange worker_range(int wk, int W, int nmb) {
     return r;
 }
 
+// Unit scheduler of the resident flat stage 1, kept in the workspace from
+// call to call.  Workgroups take their first units in the strided order and
+// the last ones from a ticket counter, so that workgroups that run faster
+// take more units.  tag == kSchedTag and the high half of word ==
+// kSchedTag32 mark an initialised block (the low half of word counts the
+// tickets, exits the workgroups done); any other content (a fresh or foreign
+// buffer) makes stage 1 keep the strided order for that call.  The flat
+// stage 2 writes (kSchedTag, kSchedTag32 << 32, 0) after every call, and the
+// last workgroup to finish a call's stage 1 sets both counts back to 0.
+struct SchedState {
+    unsigned long long tag;
+    unsigned long long word;
+    unsigned long long exits;
+};
+constexpr unsigned long long kSchedTag = 0x4c4d4847554d4231ull;
+constexpr unsigned int kSchedTag32 = 0x53434844u;
+
 struct Stage1Args {
     const uint16_t* H;      // [B, d] bf16
     const uint16_t* W;      // [V, d] bf16
@@ -77,6 +94,10 @@ struct Stage1Args {
     int32_t* cidx;
     // unfused baseline output [B, V]
     float* logits;
+    // resident flat: unit scheduler (null: strided order) and the units each
+    // workgroup takes in the strided order first (3 <= dyn_k0, dyn_k0 G <= nunits)
+    SchedState* sched;
+    int dyn_k0;
 };
 
 struct Stage1Config {
@@ -130,8 +151,10 @@ hipError_t launch_wide_dma(int variant, const Stage1Args& a, int nt, int grid_y,
 hipError_t launch_stream(int variant, const Stage1Args& a, int grid_y, const Stage1Config& cfg,
                          void* part, bool with_fixup, hipStream_t stream);
 
+// sched (may be null): the unit scheduler block, initialised by the kernel.
 hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
-                              int32_t* out_idx, float* out_score, hipStream_t stream);
+                              int32_t* out_idx, float* out_score, SchedState* sched,
+                              hipStream_t stream);
 
 hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
                                  int B,

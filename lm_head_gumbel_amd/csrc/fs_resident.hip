@@ -89,6 +89,8 @@ struct ResidentSmem {
     uint64_t fkey[NW][16];
     float fmx[NW][16];
     float fsm[NW][16];
+    int dyn;            // flat: units from the ticket counter
+    int next_unit[2];   // flat, ticket order: a unit taken by ticket (-1: none)
 };
 
 // Top-k: order images of the x of the workgroup's rows, one padded row of
@@ -156,13 +158,37 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // Grouped records (one per workgroup and tile) need a contiguous range
     // [mb0, mb1).  Strided: mb0 is the first block, mb1 one past the last
     // unit's blocks.
+    //
+    // Flat with a scheduler block (one batch group): the first a.dyn_k0 >= 3
+    // units of a workgroup are w, w + G, w + 2G, ... as in the strided order,
+    // every later one comes from a ticket t (unit k0 G + t), so that the
+    // workgroups that run faster take more of the last units and all finish
+    // close together.  The ticket taken in group i (after the group's last
+    // load, so that no load waits for it) is read in group i + 1 and names
+    // the unit of group i + 3.  Tickets are handed out in order, so a
+    // workgroup that has one past the end takes no more; the last workgroup
+    // to finish resets the counts.
     constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits || VAR == kVarTopk;
+    const int nunits = (a.nmb + MPI - 1) / MPI;   // strided: the host keeps G <= nunits
+    bool dyn = false;
+    if constexpr (VAR == kVarFlat) {
+        if (a.sched != nullptr) {   // uniform
+            if (threadIdx.x == 0) {
+                const unsigned long long tag =
+                    __hip_atomic_load(&a.sched->tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned long long word =
+                    __hip_atomic_load(&a.sched->word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.dyn = tag == kSchedTag && (unsigned int)(word >> 32) == kSchedTag32;
+            }
+            __syncthreads();
+            dyn = sm.dyn != 0;
+        }
+    }
     int mb0, mb1;
     if constexpr (kStrided) {
-        const int nunits = (a.nmb + MPI - 1) / MPI;   // the host keeps G <= nunits
         const int last = w + a.G * ((nunits - 1 - w) / a.G);
         mb0 = w * MPI;
-        mb1 = min(last * MPI + MPI, a.nmb);
+        mb1 = dyn ? a.nmb : min(last * MPI + MPI, a.nmb);
     } else {
         mb0 = part_begin(w, a.nmb, a.G);
         mb1 = part_begin(w + 1, a.nmb, a.G);
@@ -211,10 +237,16 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     Lse lse = lse_empty();
     int buf = 0;
     int stored = 0;   // top-k: blocks in the row store (the workgroup's blocks in walk order)
+    // ticket order: first block of the next group's unit (mb1: none)
+    int gi = 0;                 // group index
+    int dyn_next = (w + a.G) * MPI;
+    bool grabbing = dyn;        // no ticket past the end seen yet (uniform)
+    bool held = false;          // a ticket taken in the previous group (uniform)
+    unsigned int ticket = 0;    // (thread 0)
     while (true) {
         // (strided: only a workgroup's last unit can be short, so the group
         // and its record segment end together there)
-        const int gnext = kStrided ? cur.g + a.G * MPI : cur.g + cur.nvm;
+        const int gnext = dyn ? dyn_next : kStrided ? cur.g + a.G * MPI : cur.g + cur.nvm;
         const bool more = gnext < mb1;
         // after the last group the prefetch re-reads this group's first stage
         // (cache hits, never used), keeping every load unconditional
@@ -253,7 +285,31 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         for (int j = 0; j < MPI; ++j)
 #pragma unroll
             for (int n = 0; n < NB; ++n) sm.red[buf][wave][j][n][lane] = acc[j][n];
+        const bool take = grabbing && more && gi + 3 >= a.dyn_k0;   // uniform
+        if (threadIdx.x == 0) {
+            if (held) {   // the previous group's ticket has long returned
+                const int u = a.dyn_k0 * a.G + (int)ticket;
+                sm.next_unit[buf] = u < nunits ? u : -1;
+            }
+            if (take)
+                ticket = (unsigned int)__hip_atomic_fetch_add(&a.sched->word, 1ull,
+                                                              __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+        }
         __syncthreads();
+        if (dyn) {   // the unit of group i + 2
+            if (gi + 2 < a.dyn_k0) {
+                dyn_next = (w + (gi + 2) * a.G) * MPI;
+            } else if (held) {
+                const int u = sm.next_unit[buf];
+                if (u < 0) grabbing = false;
+                dyn_next = u >= 0 ? u * MPI : mb1;
+            } else {
+                dyn_next = mb1;
+            }
+            held = take;
+        }
+        ++gi;
 
 #pragma unroll
         for (int q = 0; q < (MPI * NB + NW - 1) / NW; ++q) {
@@ -290,7 +346,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         stored += cur.nvm;
 
         if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
-            if (cur.g + cur.nvm == cur.seg_end) {   // a record segment ends here
+            // flat: one record, after the workgroup's last group
+            if (VAR == kVarFlat ? !more : cur.g + cur.nvm == cur.seg_end) {   // a segment ends here
                 column_reduce<VAR>(best, lse);
                 if (lane < 16) {
                     sm.fkey[wave][lane] = best;
@@ -320,6 +377,17 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         cur = nxt;
 #pragma unroll
         for (int j = 0; j < MPI; ++j) wrow[j] = wnext[j];
+    }
+    if (dyn && threadIdx.x == 0) {
+        // every ticket of this workgroup has returned (each was read back);
+        // the last workgroup out resets the counts for the next call
+        const unsigned long long e = __hip_atomic_fetch_add(&a.sched->exits, 1ull, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+        if (e == (unsigned long long)(a.G - 1)) {
+            __hip_atomic_store(&a.sched->word, (unsigned long long)kSchedTag32 << 32,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.sched->exits, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 
     if constexpr (VAR == kVarTopk) {

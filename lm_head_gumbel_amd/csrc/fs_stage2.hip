@@ -32,8 +32,15 @@ __device__ uint64_t block_max_key(uint64_t k) {
 __global__ __launch_bounds__(kRedThreads) void stage2_flat_kernel(const float* pm,
                                                                   const int32_t* pidx, int P,
                                                                   int B, int32_t* out_idx,
-                                                                  float* out_score) {
+                                                                  float* out_score,
+                                                                  SchedState* sched) {
     const int b = blockIdx.x;
+    // stage 1 is done: mark the unit scheduler initialised for the next call
+    if (sched && b == 0 && threadIdx.x == 0) {
+        sched->word = (unsigned long long)kSchedTag32 << 32;
+        sched->exits = 0ull;
+        sched->tag = kSchedTag;
+    }
     uint64_t best = pack_key(-INFINITY, -1);
     for (int p = threadIdx.x; p < P; p += kRedThreads) {
         const int32_t id = pidx[(size_t)b * P + p];
@@ -1016,9 +1023,10 @@ __global__ void debug_noise_kernel(uint32_t k0, uint32_t k1, uint32_t step, uint
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B,
-                              int32_t* out_idx, float* out_score, hipStream_t stream) {
+                              int32_t* out_idx, float* out_score, SchedState* sched,
+                              hipStream_t stream) {
     hipLaunchKernelGGL(stage2_flat_kernel, dim3(B), dim3(kRedThreads), 0, stream, pm, pidx, P,
-                       B, out_idx, out_score);
+                       B, out_idx, out_score, sched);
     return hipGetLastError();
 }
 

@@ -135,3 +135,79 @@ def test_graph_replay_advances_the_device_step():
         # and against the oracle
         r = O.run_call(O.logits_bf16(Hb, Wb), temp, None, None, seeds_h, rep, 0, 128)
         check_index_rows(got_i, r["flat_idx"], r["flat_gap"], r["s"], what=f"replay {rep}")
+
+
+SCHED_TAG = 0x4C4D4847554D4231
+SCHED_TAG32 = 0x53434844
+
+
+def sched_block(ws):
+    """The unit scheduler block at the end of a flat workspace: (tag, word)."""
+    tail = host(ws[-256:-240]).view(np.uint64)
+    return int(tail[0]), int(tail[1])
+
+
+def test_flat_ticket_order_matches_fixed_order():
+    """A flat workspace used again hands stage-1 units out by ticket (the first
+    call, on a zeroed buffer, walks the fixed strided order and leaves the
+    scheduler block initialised).  Every call, eager and replayed from a
+    graph, equals the same call on a fresh zeroed workspace bit for bit and
+    the oracle; after each call the ticket count is back at 0."""
+    t = torch()
+    B, d, V = 32, 512, 40000   # 1250 units of two blocks: the ticket order applies
+    Hb = hidden_bf16(B, d, seed=71)
+    Wb = weights_bf16(V, d, std=0.05, seed=72)
+    temp = np.random.default_rng(73).uniform(0.5, 1.3, B).astype(np.float32)
+    x_in = Inputs(Hb, Wb, temp)
+    l = O.logits_bf16(Hb, Wb)
+
+    def fresh(step):
+        p = x_in.params(seed=11, step=step)
+        idx = t.full((B,), -7, dtype=t.int32, device="cuda")
+        score = t.zeros(B, dtype=t.float32, device="cuda")
+        ws0 = t.zeros(fs.fs_workspace_bytes(p, fs.FS_VARIANT_FLAT), dtype=t.uint8, device="cuda")
+        fs.check(fs.fs_sample(p, x_in.H, x_in.W, x_in.temp, None, idx, score, ws0), "fresh")
+        t.cuda.synchronize()
+        return host(idx).copy(), host(score).copy()
+
+    p = x_in.params(seed=11, step=0)
+    ws = t.zeros(fs.fs_workspace_bytes(p, fs.FS_VARIANT_FLAT), dtype=t.uint8, device="cuda")
+    assert sched_block(ws) == (0, 0)
+    idx = t.full((B,), -7, dtype=t.int32, device="cuda")
+    score = t.zeros(B, dtype=t.float32, device="cuda")
+    for step in range(4):
+        p.step = step
+        fs.check(fs.fs_sample(p, x_in.H, x_in.W, x_in.temp, None, idx, score, ws), "reused")
+        t.cuda.synchronize()
+        assert sched_block(ws) == (SCHED_TAG, SCHED_TAG32 << 32), "scheduler block after a call"
+        gi, gs = host(idx).copy(), host(score).copy()
+        wi, wsc = fresh(step)
+        log(f"step {step}: {np.count_nonzero(gi == wi)}/{B} equal to the fixed order")
+        assert np.array_equal(gi, wi) and np.array_equal(gs, wsc)
+        r = O.run_call(l, temp, None, None, 11, step, 0, 128)
+        check_index_rows(gi, r["flat_idx"], r["flat_gap"], r["s"], what=f"step {step}")
+
+    # graph replays with the device step advancing
+    step_t = t.zeros(1, dtype=t.int32, device="cuda")
+    pg = x_in.params(seed=11, step=0, step_ptr=step_t)
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):
+        fs.check(fs.fs_sample(pg, x_in.H, x_in.W, x_in.temp, None, idx, score, ws), "warm-up")
+    t.cuda.current_stream().wait_stream(s)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        fs.check(fs.fs_sample(pg, x_in.H, x_in.W, x_in.temp, None, idx, score, ws), "capture")
+        step_t.add_(1)
+    t.cuda.synchronize()
+    step_t.zero_()
+    t.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        t.cuda.synchronize()
+        assert sched_block(ws) == (SCHED_TAG, SCHED_TAG32 << 32), "scheduler block after a replay"
+        gi, gs = host(idx).copy(), host(score).copy()
+        wi, wsc = fresh(rep)
+        log(f"replay {rep}: {np.count_nonzero(gi == wi)}/{B} equal to the fixed order")
+        assert np.array_equal(gi, wi) and np.array_equal(gs, wsc)
