@@ -119,11 +119,23 @@ Stage1Config pick_config(bool stream, int B) {
     return B <= 16 ? Stage1Config{1, 4, 2} : Stage1Config{2, 4, 1};
 }
 
+// FS_SMALL_NB1=1: one batch block per workgroup for B <= 16 (tuning
+// experiments; by default two, the second one padding).
+bool small_nb1() {
+    static const bool on = [] {
+        const char* e = std::getenv("FS_SMALL_NB1");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
 // Resident-H shape for a batch, hidden size and variant (nw == 0: none
-// instantiated).  Above 16 rows two batch blocks per workgroup are preferred;
-// where no such shape holds the hidden size, one block per workgroup is used
-// with more batch groups.  FS_RES_CFG="nb,mpi,ks,nw" overrides the choice for
-// tuning experiments.
+// instantiated).  Two batch blocks per workgroup are preferred, also for 16
+// rows or fewer (the second block is padding: its MFMAs are free in this
+// HBM-bound loop, and the two-block shapes stream W faster, 198 against
+// 230 us at B = 8, d = 4096, V = 151936); where no such shape holds the
+// hidden size, one block per workgroup is used with more batch groups.
+// FS_RES_CFG="nb,mpi,ks,nw" overrides the choice for tuning experiments.
 ResidentConfig pick_resident(int B, int nks, int variant) {
     static const char* env = std::getenv("FS_RES_CFG");
     if (env) {
@@ -135,8 +147,9 @@ ResidentConfig pick_resident(int B, int nks, int variant) {
         }
         return ResidentConfig{0, 0, 0, 0, 0, 0};
     }
-    ResidentConfig c = resident_default(B <= 16 ? 1 : 2, nks, variant);
-    if (c.nw == 0 && B > 16) c = resident_default(1, nks, variant);
+    const int first = B <= 16 && small_nb1() ? 1 : 2;
+    ResidentConfig c = resident_default(first, nks, variant);
+    if (c.nw == 0) c = resident_default(3 - first, nks, variant);
     return c;
 }
 
