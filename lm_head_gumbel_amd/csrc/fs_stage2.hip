@@ -15,17 +15,19 @@
 namespace fs {
 
 constexpr int kRedThreads = 256;
+constexpr int kGrpThreads = 1024;   // grouped stage 2: a thread per tile up to 1024 tiles
 
-// Block-wide maximum of a packed key (256 threads); every thread gets it.
+// Block-wide maximum of a packed key (NT threads); every thread gets it.
+template <int NT = kRedThreads>
 __device__ uint64_t block_max_key(uint64_t k) {
-    __shared__ uint64_t part[kRedThreads / 64];
+    __shared__ uint64_t part[NT / 64];
     for (int m = 32; m >= 1; m >>= 1) k = key_max(k, shfl_xor_u64(k, m));
     const int wave = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) part[wave] = k;
     __syncthreads();
     uint64_t r = part[0];
-    for (int i = 1; i < kRedThreads / 64; ++i) r = key_max(r, part[i]);
+    for (int i = 1; i < NT / 64; ++i) r = key_max(r, part[i]);
     return r;
 }
 
@@ -60,7 +62,7 @@ __device__ __forceinline__ bool row_is_greedy(const float* temp, int b, uint32_t
     return !(T > 0.f);
 }
 
-__global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
+__global__ __launch_bounds__(kGrpThreads) void stage2_grouped_kernel(
     const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int G, int nmb,
     int tile_mb, const float* temp, uint32_t flags, NoiseSrc noise, float* tile_max,
     int32_t* tile_idx, float* tile_L, int32_t* out_idx) {
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
     const bool greedy = row_is_greedy(temp, b, flags);
     const RowKey rk = row_key(noise, b);
     uint64_t best = pack_key(-INFINITY, -1);
-    for (int t = threadIdx.x; t < T; t += kRedThreads) {
+    for (int t = threadIdx.x; t < T; t += kGrpThreads) {
         const int first = t * tile_mb;
         const int last = min(nmb, (t + 1) * tile_mb) - 1;
         const int wf = part_owner(first, nmb, G);
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kRedThreads) void stage2_grouped_kernel(
         }
     }
     if (out_idx) {
-        best = block_max_key(best);
+        best = block_max_key<kGrpThreads>(best);
         if (threadIdx.x == 0) out_idx[b] = key_index(best);
     }
 }
@@ -1035,7 +1037,7 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                                  uint32_t flags, const NoiseSrc& noise, float* tile_max,
                                  int32_t* tile_idx, float* tile_L, int32_t* out_idx,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kRedThreads), 0, stream, pm, pidx,
+    hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kGrpThreads), 0, stream, pm, pidx,
                        pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,
                        tile_L, out_idx);
     return hipGetLastError();
