@@ -44,7 +44,14 @@
  * Conventions
  *  - Ownership: the caller allocates every device buffer, including the
  *    workspace sized by fs_workspace_bytes.  The library allocates no device
- *    memory and keeps no state besides a per-device property cache.
+ *    memory and keeps no state besides a per-device property cache.  A
+ *    workspace needs no initialisation.  A flat workspace (FS_VARIANT_FLAT)
+ *    carries a small work-scheduling block from one fs_sample /
+ *    fs_sample_stage1 call to the next (its last 256 bytes): any content
+ *    there, a fresh buffer's included, gives correct results (an
+ *    unrecognised block makes that call schedule its work statically and
+ *    fs_sample then sets it up), but code other than these calls should not
+ *    write into a flat workspace between them, unless it zeroes it whole.
  *  - Asynchrony: every call enqueues work on `stream` (a hipStream_t; NULL is
  *    the default stream) and returns; outputs are valid once the stream has
  *    executed the work.  The host never reads device memory.
