@@ -377,7 +377,13 @@ size_t layout(int variant, const Plan& pl, int k, char* base, Workspace* w) {
         char* c = dense ? nullptr : take(n * 4);
         const size_t sb = stage2_topk_scratch_bytes(pl.G, L, pl.B, k, dense);
         char* d = sb ? take(sb) : nullptr;
-        if (w) { w->cx = (float*)a; w->cidx = (int32_t*)c; w->sel = d; }
+        char* e = take(sizeof(SchedState));
+        if (w) {
+            w->cx = (float*)a;
+            w->cidx = (int32_t*)c;
+            w->sel = d;
+            w->sched = (SchedState*)e;
+        }
     } else if (variant == FS_VARIANT_LOGITS) {
         char* a = pl.stream ? take(part_bytes(pl)) : nullptr;
         if (w) w->part = a;
@@ -456,13 +462,20 @@ fs_status sample_topk(const fs_params* p, const void* H, const void* W, const fl
     a.topk_dense = topk_dense(pl, k) ? 1 : 0;
     a.cx = w.cx;
     a.cidx = w.cidx;
+    // ticket order where the one-kernel stage 2 follows (it sets the block up);
+    // dense lists imply their ids by the strided order
+    const bool tickets = pl.kind == kResident && !a.topk_dense &&
+                         topk_small_path(pl.G, a.topk_len, k);
+    a.dyn_k0 = tickets ? dynamic_k0(pl) : 0;
+    a.sched = a.dyn_k0 > 0 ? w.sched : nullptr;
     hipError_t e = pl.kind == kResident ? launch_resident(kVarTopk, a, pl.grid_y, pl.rcfg, s)
                                         : launch_stage1(kVarTopk, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
     const int unit_rows = pl.kind == kResident ? pl.rcfg.mpi * kMBlock : kMBlock;
     const DenseIds dn{a.topk_dense, pl.v_offset, unit_rows, pl.G * unit_rows};
     return from_hip(launch_stage2_topk(w.cx, w.cidx, pl.G, a.topk_len, pl.B, k, dn, top_p, temp,
-                                       p->flags, noise_src(pl, p), out_idx, w.sel, s));
+                                       p->flags, noise_src(pl, p), out_idx, w.sel,
+                                       tickets ? w.sched : nullptr, s));
 }
 
 }  // namespace

@@ -170,13 +170,15 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
 // plain top-k; 0 < top_p < 1: top-p after top-k.  scratch: device memory of
 // stage2_topk_scratch_bytes(G, L, B, k, dense) bytes (256-byte aligned; may be null
 // when that is 0) for the lists of the intermediate selection levels.
-// Global ids of the rows a top-k workgroup keeps, in its store order: units of
-// unit_rows consecutive ids, unit_stride apart, the first at base.
+// Global ids of the rows a top-k workgroup keeps, in its store order: store
+// unit i (unit_rows rows, a power of two) is vocabulary unit tab[i], whose
+// rows are ids v_offset + tab[i] unit_rows + 0, 1, ...
 struct RowIds {
-    int base, unit_rows, unit_stride;
+    int v_offset, unit_rows;
+    const int* tab;
 };
-__host__ __device__ inline int row_id(const RowIds& m, int r) {
-    return m.base + (r / m.unit_rows) * m.unit_stride + r % m.unit_rows;
+__device__ inline int row_id(const RowIds& m, int r) {
+    return m.v_offset + m.tab[r / m.unit_rows] * m.unit_rows + r % m.unit_rows;
 }
 
 // Dense top-k lists (on != 0): entry r of list w has id row_id({v_offset +
@@ -185,10 +187,15 @@ struct DenseIds {
     int on, v_offset, unit_rows, unit_stride;
 };
 size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense);
+// Stage 2 of top-k runs in one kernel (stage2_topk_kernel): k <= 64, at most
+// 512 * 64 candidates per row, lists with ids.  sched (may be null; that
+// kernel only) is the unit scheduler block of the resident stage 1,
+// initialised by the kernel.
+bool topk_small_path(int G, int L, int k);
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,
                               DenseIds dn, float top_p, const float* temp, uint32_t flags,
                               const NoiseSrc& noise, int32_t* out_idx, void* scratch,
-                              hipStream_t stream);
+                              SchedState* sched, hipStream_t stream);
 
 hipError_t launch_merge_online(int B, int C, const int32_t* z, const float* L, const float* temp,
                                const NoiseSrc& noise, uint32_t flags,

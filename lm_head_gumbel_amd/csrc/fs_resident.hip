@@ -98,6 +98,7 @@ struct ResidentSmem {
 template <int NB, int NW, int HL>
 struct TopkRowsSmem {
     alignas(16) uint32_t u[16 * NB][TopkRows<NB, HL>::kStride];
+    int unit[TopkRows<NB, HL>::kRows / 16];   // vocabulary unit of each store unit
 };
 struct NoTopkRows {};
 
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits || VAR == kVarTopk;
     const int nunits = (a.nmb + MPI - 1) / MPI;   // strided: the host keeps G <= nunits
     bool dyn = false;
-    if constexpr (VAR == kVarFlat) {
+    if constexpr (VAR == kVarFlat || VAR == kVarTopk) {
         if (a.sched != nullptr) {   // uniform
             if (threadIdx.x == 0) {
                 const unsigned long long tag =
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     }
     const int bbase = y * 16 * NB;
     const int ks0 = wave * HT;
+    constexpr int kTopkRows = TopkRows<NB, HL>::kRows;   // top-k: rows the store holds
 
     // this wave's slice of H, resident for the whole kernel (rows past B reuse
     // row B - 1, their columns are discarded; k past d reads zeros): the first
@@ -285,7 +287,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         for (int j = 0; j < MPI; ++j)
 #pragma unroll
             for (int n = 0; n < NB; ++n) sm.red[buf][wave][j][n][lane] = acc[j][n];
-        const bool take = grabbing && more && gi + 3 >= a.dyn_k0;   // uniform
+        // (top-k: only while the row store has room for the unit of group i + 3)
+        const bool take = grabbing && more && gi + 3 >= a.dyn_k0 &&
+                          (VAR != kVarTopk || (gi + 4) * MPI * kMBlock <= kTopkRows);   // uniform
         if (threadIdx.x == 0) {
             if (held) {   // the previous group's ticket has long returned
                 const int u = a.dyn_k0 * a.G + (int)ticket;
@@ -343,6 +347,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // the next group writes the other buffer; this one is rewritten two
         // groups on, after every wave has passed the next group's barrier
         buf ^= 1;
+        if constexpr (VAR == kVarTopk)
+            if (threadIdx.x == 0) tk.unit[stored / MPI] = cur.g / MPI;
         stored += cur.nvm;
 
         if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             uc[q] = tk.u[cl];
             o[q] = ((size_t)(bbase + (ok ? cl : 0)) * a.G + w) * a.topk_len;
         }
-        const RowIds ids{a.v_offset + mb0 * kMBlock, MPI * kMBlock, a.G * MPI * kMBlock};
+        const RowIds ids{a.v_offset, MPI * kMBlock, tk.unit};
         if (nc > 0) {
             if (a.topk_dense)
                 topk_write_dense<C>(a, nc, uc, nr, o);

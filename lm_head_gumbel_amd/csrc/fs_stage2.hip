@@ -218,11 +218,17 @@ __device__ int32_t finish_topk(uint64_t key, int b, bool greedy, float top_p,
 template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void stage2_topk_kernel(
     const float* cx, const int32_t* cidx, int G, int L, int B, int k, float top_p,
-    const float* temp, uint32_t flags, NoiseSrc noise, int32_t* out_idx) {
+    const float* temp, uint32_t flags, NoiseSrc noise, int32_t* out_idx, SchedState* sched) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const bool greedy = row_is_greedy(temp, b, flags);
+    // stage 1 is done: mark the unit scheduler initialised for the next call
+    if (sched && b == 0 && threadIdx.x == 0) {
+        sched->word = (unsigned long long)kSchedTag32 << 32;
+        sched->exits = 0ull;
+        sched->tag = kSchedTag;
+    }
     __shared__ int red[2][kTopkWaves];
     __shared__ uint32_t wbound[kTopkWaves];
     __shared__ uint32_t g_u[kTopkGather];
@@ -1044,11 +1050,12 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
 }
 
 namespace {
+size_t align_256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
 bool topk_small_path(int G, int L, int k) {   // the dense form never takes it
     return k <= 64 && (int64_t)G * L <= (int64_t)kTopkThreads * 64;
 }
-size_t align_256(size_t x) { return (x + 255) / 256 * 256; }
-}  // namespace
 
 size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense) {
     const int64_t n = (int64_t)G * L;
@@ -1060,13 +1067,13 @@ size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense) {
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,
                               DenseIds dn, float top_p, const float* temp, uint32_t flags,
                               const NoiseSrc& noise, int32_t* out_idx, void* scratch,
-                              hipStream_t stream) {
+                              SchedState* sched, hipStream_t stream) {
     if (k < 1 || k > kMaxK || L < 1 || G < 1) return hipErrorInvalidValue;
     const bool dense = dn.on != 0;
 #define FS_TOPK2(PER_)                                                                       \
     if (!dense && k <= 64 && (int64_t)G * L <= (int64_t)kTopkThreads * PER_) {             \
         hipLaunchKernelGGL(stage2_topk_kernel<PER_>, dim3(B), dim3(kTopkThreads), 0, stream, \
-                           cx, cidx, G, L, B, k, top_p, temp, flags, noise, out_idx);        \
+                           cx, cidx, G, L, B, k, top_p, temp, flags, noise, out_idx, sched); \
         return hipGetLastError();                                                            \
     }
     FS_TOPK2(4)

@@ -10,7 +10,7 @@ import pytest
 import lm_head_gumbel_amd as fs
 from lm_head_gumbel_amd.inputs import hidden_bf16, weights_bf16
 from oracle import fs_oracle as O
-from gpu_util import (Inputs, TOL_GAP, check_index_rows, check_values, dev, host, log, run_flat,
+from gpu_util import (Inputs, TOL_CUT, TOL_GAP, check_index_rows, check_values, dev, host, log, run_flat,
                       run_grouped, run_logits, run_multinomial, run_topk, run_topp, torch,
                       workspace)
 
@@ -211,3 +211,47 @@ def test_flat_ticket_order_matches_fixed_order():
         wi, wsc = fresh(rep)
         log(f"replay {rep}: {np.count_nonzero(gi == wi)}/{B} equal to the fixed order")
         assert np.array_equal(gi, wi) and np.array_equal(gs, wsc)
+
+
+def test_topk_ticket_order_matches_fixed_order():
+    """The same for fs_sample_topk (k <= 64, where one stage-2 kernel follows
+    and sets the block up; its scheduler block is the last 256 bytes of the
+    top-k workspace): calls on a reused workspace, and top-p after top-k, equal
+    fresh-workspace calls bit for bit and the oracle."""
+    t = torch()
+    B, d, V, k = 32, 512, 40000, 40
+    Hb = hidden_bf16(B, d, seed=81)
+    Wb = weights_bf16(V, d, std=0.05, seed=82)
+    temp = np.random.default_rng(83).uniform(0.5, 1.3, B).astype(np.float32)
+    x_in = Inputs(Hb, Wb, temp)
+    l = O.logits_bf16(Hb, Wb)
+
+    def call(p, ws, top_p):
+        idx = t.full((B,), -7, dtype=t.int32, device="cuda")
+        if top_p < 1:
+            fs.check(fs.fs_sample_topk_topp(p, x_in.H, x_in.W, x_in.temp, None, k, top_p, idx, ws))
+        else:
+            fs.check(fs.fs_sample_topk(p, x_in.H, x_in.W, x_in.temp, None, k, idx, ws))
+        t.cuda.synchronize()
+        return host(idx).astype(np.int64)
+
+    p = x_in.params(seed=13, step=0)
+    n = fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, k)
+    ws = t.zeros(n, dtype=t.uint8, device="cuda")
+    for step in range(4):
+        for top_p in (1.0, 0.8):
+            p.step = step
+            got = call(p, ws, top_p)
+            assert sched_block(ws) == (SCHED_TAG, SCHED_TAG32 << 32), "scheduler block after a call"
+            want = call(p, t.zeros(n, dtype=t.uint8, device="cuda"), top_p)
+            log(f"step {step} top_p {top_p}: {np.count_nonzero(got == want)}/{B} equal to the fixed order")
+            assert np.array_equal(got, want)
+            r = O.run_call(l, temp, None, None, 13, step, 0, 128)
+            if top_p < 1:
+                oi, ogap, omarg, ocut = O.topk_topp_sample(r["x"], r["s"], k, top_p)
+                pin = (ogap > TOL_GAP) & (omarg > 1e-3) & (ocut > TOL_CUT)
+            else:
+                oi, ogap, omarg = O.topk_sample(r["x"], r["s"], k)
+                pin = (ogap > TOL_GAP) & (omarg > 1e-3)
+            assert pin.sum() >= B // 4
+            assert np.array_equal(got[pin], oi[pin])
