@@ -89,8 +89,8 @@ struct ResidentSmem {
     uint64_t fkey[NW][16];
     float fmx[NW][16];
     float fsm[NW][16];
-    int dyn;            // flat: units from the ticket counter
-    int next_unit[2];   // flat, ticket order: a unit taken by ticket (-1: none)
+    int dyn;            // flat and top-k: units from the ticket counter
+    int next_unit[2];   // ticket order: a unit taken by ticket (-1: none)
 };
 
 // Top-k: order images of the x of the workgroup's rows, one padded row of
@@ -160,7 +160,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // [mb0, mb1).  Strided: mb0 is the first block, mb1 one past the last
     // unit's blocks.
     //
-    // Flat with a scheduler block (one batch group): the first a.dyn_k0 >= 3
+    // Flat and top-k with a scheduler block (one batch group; top-k with lists
+    // that carry ids, its store unit table giving the ids): the first a.dyn_k0 >= 3
     // units of a workgroup are w, w + G, w + 2G, ... as in the strided order,
     // every later one comes from a ticket t (unit k0 G + t), so that the
     // workgroups that run faster take more of the last units and all finish
