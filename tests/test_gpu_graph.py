@@ -187,6 +187,18 @@ def test_flat_ticket_order_matches_fixed_order():
         r = O.run_call(l, temp, None, None, 11, step, 0, 128)
         check_index_rows(gi, r["flat_idx"], r["flat_gap"], r["s"], what=f"step {step}")
 
+    # a workspace full of arbitrary bytes (a fresh allocation's content):
+    # that call walks the fixed order and sets the block up
+    g = t.Generator(device="cuda")
+    g.manual_seed(5)
+    ws_r = t.randint(0, 256, (ws.numel(),), generator=g, device="cuda", dtype=t.int32).to(t.uint8)
+    p.step = 7
+    fs.check(fs.fs_sample(p, x_in.H, x_in.W, x_in.temp, None, idx, score, ws_r), "random ws")
+    t.cuda.synchronize()
+    wi, wsc = fresh(7)
+    assert np.array_equal(host(idx), wi) and np.array_equal(host(score), wsc)
+    assert sched_block(ws_r) == (SCHED_TAG, SCHED_TAG32 << 32)
+
     # graph replays with the device step advancing
     step_t = t.zeros(1, dtype=t.int32, device="cuda")
     pg = x_in.params(seed=11, step=0, step_ptr=step_t)
