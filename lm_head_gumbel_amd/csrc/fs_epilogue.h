@@ -36,17 +36,26 @@ __device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
     return c;
 }
 
+// The allow word of column c that holds rows row0..row0+3 (row0 % 4 == 0, so
+// one word holds all four): read only for a masked column and rows inside V;
+// all ones otherwise.  Issued ahead of its use, its wait does not hold the
+// loads issued after it.
+__device__ __forceinline__ uint32_t allow_word(const Stage1Args& a, const ColCtx& c, int row0,
+                                               bool blk_ok) {
+    return (c.allow_row && blk_ok && row0 < a.V) ? c.allow_row[row0 >> 5] : ~0u;
+}
+
 // Tempered, masked logits x of four consecutive rows row0..row0+3 (local W
 // rows) of one column: -inf past V, at or past n_valid, where the allow bit
-// is clear, and for NaN.
+// (of `word`, from allow_word) is clear, and for NaN.
 __device__ __forceinline__ void lane_x(const Stage1Args& a, const ColCtx& c, f32x4 v, int row0,
-                                       bool blk_ok, float (&x)[4]) {
+                                       bool blk_ok, uint32_t word, float (&x)[4]) {
     const int gid0 = a.v_offset + row0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = row0 + r;
         bool ok = blk_ok && c.ok && (i < a.V) && (gid0 + r < a.n_valid);
-        if (ok && c.allow_row) ok = (c.allow_row[i >> 5] >> (i & 31)) & 1u;
+        if (a.allow) ok = ok && ((word >> (i & 31)) & 1u);   // uniform
         const float xv = v[r] * c.inv_t;
         x[r] = (ok && xv == xv) ? xv : -INFINITY;
     }
@@ -54,10 +63,10 @@ __device__ __forceinline__ void lane_x(const Stage1Args& a, const ColCtx& c, f32
 
 // x as above and the noisy scores s = x + Gumbel (s = x for greedy columns).
 __device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c, f32x4 v,
-                                            int row0, bool blk_ok, float (&x)[4],
+                                            int row0, bool blk_ok, uint32_t word, float (&x)[4],
                                             float (&s)[4]) {
     const int gid0 = a.v_offset + row0;
-    lane_x(a, c, v, row0, blk_ok, x);
+    lane_x(a, c, v, row0, blk_ok, word, x);
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = x[r];
     if (!c.greedy && blk_ok && c.ok) {
@@ -69,6 +78,13 @@ __device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c
         s[2] += gumbel_from_word(rw.z);
         s[3] += gumbel_from_word(rw.w);
     }
+}
+
+// The same with the allow word read here.
+__device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c, f32x4 v,
+                                            int row0, bool blk_ok, float (&x)[4],
+                                            float (&s)[4]) {
+    lane_scores(a, c, v, row0, blk_ok, allow_word(a, c, row0, blk_ok), x, s);
 }
 
 // Folds four (x, s) pairs into a column's running winner and log-mass.

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                 }
             } else if constexpr (VAR == kVarTopk) {
                 float x[4];
-                lane_x(a, cc, v, row0, true, x);
+                lane_x(a, cc, v, row0, true, allow_word(a, cc, row0, true), x);
                 *reinterpret_cast<uint4*>(&tk.u[ncol * 16 + r16][(stored + j) * kMBlock + 4 * kg]) =
                     uint4{topk_order(x[0]), topk_order(x[1]), topk_order(x[2]), topk_order(x[3])};
             } else {

@@ -201,11 +201,14 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
             } else {
                 float x[4];
                 const int gid0 = a.v_offset + row0;
+                // one allow word holds the lane's four rows (row0 % 4 == 0)
+                const uint32_t word =
+                    (allow_row && blk_ok && row0 < a.V) ? allow_row[row0 >> 5] : ~0u;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = row0 + r;
                     bool ok = blk_ok && col_ok && (i < a.V) && (gid0 + r < a.n_valid);
-                    if (ok && allow_row) ok = (allow_row[i >> 5] >> (i & 31)) & 1u;
+                    if (a.allow) ok = ok && ((word >> (i & 31)) & 1u);   // uniform
                     const float xv = v[r] * inv_t;
                     x[r] = (ok && xv == xv) ? xv : -INFINITY;
                 }
