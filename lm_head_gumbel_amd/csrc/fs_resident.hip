@@ -102,6 +102,19 @@ struct TopkRowsSmem {
 };
 struct NoTopkRows {};
 
+// Grouped: the waves' column partials of each vocabulary tile that the
+// workgroup's range meets, kept here until the walk ends.  A record store
+// inside the walk would hold back the loads issued after it (its wait is
+// counted with theirs): 15 us of 240 at B = 32 with 128-row tiles.
+constexpr int kSegSlots = 16;
+template <int NW>
+struct SegSmem {
+    uint64_t key[kSegSlots][NW][16];
+    float mx[kSegSlots][NW][16];
+    float sm[kSegSlots][NW][16];
+};
+struct NoSeg {};
+
 // The last HL k-steps of each wave's H slice, when the registers cannot hold
 // the whole slice: per wave [HL][NB] fragments of 64 lanes (each lane reads
 // back only what it wrote).
@@ -131,6 +144,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     using TkSmem =
         typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW, HL>, NoTopkRows>::type;
     __shared__ TkSmem tk;
+    using SegPart = typename std::conditional<VAR == kVarGrouped, SegSmem<NW>, NoSeg>::type;
+    __shared__ SegPart seg;
 
     // Row range w and batch group y of this workgroup.  With xcd_pair the grid
     // is 1-D and the ny groups of a range get ids L, L + 8, L + 16, ...:
@@ -195,6 +210,11 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         mb0 = part_begin(w, a.nmb, a.G);
         mb1 = part_begin(w + 1, a.nmb, a.G);
     }
+    // grouped: the range meets tiles t0 .. t0 + nseg - 1; their records are
+    // stored after the walk when LDS holds them all
+    const int t0 = mb0 / a.tile_mb;
+    const int nseg = mb1 > mb0 ? (mb1 - 1) / a.tile_mb - t0 + 1 : 0;
+    const bool defer = VAR == kVarGrouped && nseg <= kSegSlots;
     const int bbase = y * 16 * NB;
     const int ks0 = wave * HT;
     constexpr int kTopkRows = TopkRows<NB, HL>::kRows;   // top-k: rows the store holds
@@ -356,25 +376,36 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             // flat: one record, after the workgroup's last group
             if (VAR == kVarFlat ? !more : cur.g + cur.nvm == cur.seg_end) {   // a segment ends here
                 column_reduce<VAR>(best, lse);
-                if (lane < 16) {
-                    sm.fkey[wave][lane] = best;
-                    sm.fmx[wave][lane] = lse.mx;
-                    sm.fsm[wave][lane] = lse.sm;
-                }
-                __syncthreads();
-                if (threadIdx.x < 16 * NB) {
-                    const int n = threadIdx.x >> 4;
-                    const ColCtx c = col_ctx(a, bbase + n * 16 + (threadIdx.x & 15));
-                    uint64_t k = pack_key(-INFINITY, -1);
-                    Lse l = lse_empty();
-                    for (int ww = n; ww < NW; ww += NB) {
-                        k = key_max(k, sm.fkey[ww][threadIdx.x & 15]);
-                        l = lse_merge(l, Lse{sm.fmx[ww][threadIdx.x & 15],
-                                             sm.fsm[ww][threadIdx.x & 15]});
+                if constexpr (VAR == kVarGrouped) {
+                    // (each segment has slots of its own: no barrier)
+                    if (defer && lane < 16) {
+                        const int sg = cur.t - t0;
+                        seg.key[sg][wave][lane] = best;
+                        seg.mx[sg][wave][lane] = lse.mx;
+                        seg.sm[sg][wave][lane] = lse.sm;
                     }
-                    put_record<VAR, false>(a, VAR == kVarGrouped ? w + cur.t : w, c, k, l);
                 }
-                __syncthreads();
+                if (VAR == kVarFlat || !defer) {   // uniform
+                    if (lane < 16) {
+                        sm.fkey[wave][lane] = best;
+                        sm.fmx[wave][lane] = lse.mx;
+                        sm.fsm[wave][lane] = lse.sm;
+                    }
+                    __syncthreads();
+                    if (threadIdx.x < 16 * NB) {
+                        const int n = threadIdx.x >> 4;
+                        const ColCtx c = col_ctx(a, bbase + n * 16 + (threadIdx.x & 15));
+                        uint64_t k = pack_key(-INFINITY, -1);
+                        Lse l = lse_empty();
+                        for (int ww = n; ww < NW; ww += NB) {
+                            k = key_max(k, sm.fkey[ww][threadIdx.x & 15]);
+                            l = lse_merge(l, Lse{sm.fmx[ww][threadIdx.x & 15],
+                                                 sm.fsm[ww][threadIdx.x & 15]});
+                        }
+                        put_record<VAR, false>(a, VAR == kVarGrouped ? w + cur.t : w, c, k, l);
+                    }
+                    __syncthreads();
+                }
                 best = pack_key(-INFINITY, -1);
                 lse = lse_empty();
             }
@@ -394,6 +425,26 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             __hip_atomic_store(&a.sched->word, (unsigned long long)kSchedTag32 << 32,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.sched->exits, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    if constexpr (VAR == kVarGrouped) {
+        if (defer) {   // uniform
+            // record (column c, tile t0 + sg) of the waves' partials; the
+            // tiles of one column go to neighbouring slots
+            __syncthreads();
+            for (int e = threadIdx.x; e < nseg * 16 * NB; e += 64 * NW) {
+                const int sg = e % nseg;
+                const int c = e / nseg;
+                const ColCtx cx = col_ctx(a, bbase + c);
+                uint64_t k = pack_key(-INFINITY, -1);
+                Lse l = lse_empty();
+                for (int ww = c >> 4; ww < NW; ww += NB) {
+                    k = key_max(k, seg.key[sg][ww][c & 15]);
+                    l = lse_merge(l, Lse{seg.mx[sg][ww][c & 15], seg.sm[sg][ww][c & 15]});
+                }
+                put_record<VAR, false>(a, w + t0 + sg, cx, k, l);
+            }
         }
     }
 
