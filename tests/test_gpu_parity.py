@@ -169,6 +169,9 @@ CASES = [
     (25, 1024, 2600, 64, 0, 32, "range", False),
     (20, 512, 1500, 256, 5, 0, "mixed", False),
     (2, 2048, 1111, 32, 1, 16, "range", True),
+    # d = 4096 with two batch blocks and an allow mask (the shape of the
+    # headline B = 32 call)
+    (20, 4096, 3000, 128, 5, 0, "mixed", True),
     # d = 5120 with two batch blocks: part of each wave's H slice lives in LDS
     (24, 5120, 2000, 128, 3, 16, "mixed", True),
     # fewer than four vocab blocks: the workgroup-cooperative kernel
