@@ -172,6 +172,9 @@ CASES = [
     # d = 4096 with two batch blocks and an allow mask (the shape of the
     # headline B = 32 call)
     (20, 4096, 3000, 128, 5, 0, "mixed", True),
+    # B > 64 grouped runs the resident kernel in three batch groups, paired
+    # on one XCD per row range
+    (72, 512, 2000, 64, 0, 0, "mixed", True),
     # d = 5120 with two batch blocks: part of each wave's H slice lives in LDS
     (24, 5120, 2000, 128, 3, 16, "mixed", True),
     # fewer than four vocab blocks: the workgroup-cooperative kernel
