@@ -38,8 +38,8 @@ __device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
 
 // The allow word of column c that holds rows row0..row0+3 (row0 % 4 == 0, so
 // one word holds all four): read only for a masked column and rows inside V;
-// all ones otherwise.  Issued ahead of its use, its wait does not hold the
-// loads issued after it.
+// all ones otherwise.  One read per fold instead of one per row: each wait
+// for it also waits for every load issued before it.
 __device__ __forceinline__ uint32_t allow_word(const Stage1Args& a, const ColCtx& c, int row0,
                                                bool blk_ok) {
     return (c.allow_row && blk_ok && row0 < a.V) ? c.allow_row[row0 >> 5] : ~0u;
