@@ -102,16 +102,18 @@ struct TopkRowsSmem {
 };
 struct NoTopkRows {};
 
-// Grouped: the waves' column partials of each vocabulary tile that the
-// workgroup's range meets, kept here until the walk ends.  A record store
-// inside the walk would hold back the loads issued after it (its wait is
-// counted with theirs): 15 us of 240 at B = 32 with 128-row tiles.
-constexpr int kSegSlots = 16;
-template <int NW>
+// Grouped: the column partials of the folding waves (waves 0 .. FW - 1,
+// FW = MPI NB, one (block, N-block) pair each per group) for each vocabulary
+// tile that the workgroup's range meets, kept here until the walk ends: 32 KiB,
+// 64 tiles when FW = 2.  A record store inside the walk would hold back the
+// loads issued after it (its wait is counted with theirs): 15 us of 240 at
+// B = 32 with 128-row tiles.
+template <int FW>
 struct SegSmem {
-    uint64_t key[kSegSlots][NW][16];
-    float mx[kSegSlots][NW][16];
-    float sm[kSegSlots][NW][16];
+    static constexpr int kSlots = 32768 / (FW * 16 * 16);
+    uint64_t key[kSlots][FW][16];
+    float mx[kSlots][FW][16];
+    float sm[kSlots][FW][16];
 };
 struct NoSeg {};
 
@@ -144,7 +146,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     using TkSmem =
         typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW, HL>, NoTopkRows>::type;
     __shared__ TkSmem tk;
-    using SegPart = typename std::conditional<VAR == kVarGrouped, SegSmem<NW>, NoSeg>::type;
+    static_assert(MPI * NB <= NW, "every (block, N-block) pair of a group has a wave");
+    constexpr int FW = MPI * NB;   // waves that fold
+    using SegPart = typename std::conditional<VAR == kVarGrouped, SegSmem<FW>, NoSeg>::type;
     __shared__ SegPart seg;
 
     // Row range w and batch group y of this workgroup.  With xcd_pair the grid
@@ -214,7 +218,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // stored after the walk when LDS holds them all
     const int t0 = mb0 / a.tile_mb;
     const int nseg = mb1 > mb0 ? (mb1 - 1) / a.tile_mb - t0 + 1 : 0;
-    const bool defer = VAR == kVarGrouped && nseg <= kSegSlots;
+    bool defer = false;
+    if constexpr (VAR == kVarGrouped) defer = nseg <= SegSmem<FW>::kSlots;
     const int bbase = y * 16 * NB;
     const int ks0 = wave * HT;
     constexpr int kTopkRows = TopkRows<NB, HL>::kRows;   // top-k: rows the store holds
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                 column_reduce<VAR>(best, lse);
                 if constexpr (VAR == kVarGrouped) {
                     // (each segment has slots of its own: no barrier)
-                    if (defer && lane < 16) {
+                    if (defer && lane < 16 && wave < FW) {
                         const int sg = cur.t - t0;
                         seg.key[sg][wave][lane] = best;
                         seg.mx[sg][wave][lane] = lse.mx;
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                 const ColCtx cx = col_ctx(a, bbase + c);
                 uint64_t k = pack_key(-INFINITY, -1);
                 Lse l = lse_empty();
-                for (int ww = c >> 4; ww < NW; ww += NB) {
+                for (int ww = c >> 4; ww < FW; ww += NB) {
                     k = key_max(k, seg.key[sg][ww][c & 15]);
                     l = lse_merge(l, Lse{seg.mx[sg][ww][c & 15], seg.sm[sg][ww][c & 15]});
                 }

@@ -187,11 +187,12 @@ CASES = [
     # 16-row vocabulary tiles (eight per range)
     (48, 256, 80000, 64, 7, 16, "mixed", True),
     (64, 128, 30000, 16, 0, 0, "range", False),
-    # resident grouped: ranges meeting eleven 16-row tiles (their records wait
-    # in LDS until the walk ends), and twenty (more than LDS keeps: each is
-    # stored when its tile ends)
+    # resident grouped: ranges meeting eleven and twenty 16-row tiles (their
+    # records wait in LDS until the walk ends), and 69 (more than LDS keeps:
+    # each is stored when its tile ends)
     (4, 1024, 45000, 16, 0, 0, "mixed", False),
     (3, 1024, 80000, 16, 9, 0, "range", True),
+    (2, 512, 280000, 16, 5, 0, "mixed", False),
 ]
 
 
