@@ -76,7 +76,8 @@ typedef enum {
     FS_OK = 0,
     FS_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad k, ...          */
     FS_ERR_UNSUPPORTED = 2,  /* valid request this build cannot serve (alignment,
-                                tile size, d % 8, k range, no gfx950 device)     */
+                                tile size, d % 8, k range, no gfx950 device,
+                                launch grids beyond HIP's limits)                */
     FS_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
     FS_ERR_HIP = 4           /* the HIP runtime reported an error               */
 } fs_status;

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfs.so")
-SOURCES = ["fs_api.hip", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip",
+SOURCES = ["fs_api.hip", "fs_plan.cpp", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip",
            "fs_wide_dma.hip", "fs_stage2.hip", "fs_probe.hip"]
 ARCH = "gfx950"
 
@@ -41,9 +41,13 @@ def compile_commands(objdir):
     """(source, object, command) per source file."""
     out = []
     for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + \
-            ["-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        if src.endswith(".cpp"):   # host-only C++ (no device code)
+            cmd = [hipcc(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-x", "c++",
+                   "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+        else:
+            cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, [])
+        cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
         out.append((src, obj, cmd))
     return out
 

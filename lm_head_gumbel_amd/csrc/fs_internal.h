@@ -5,15 +5,12 @@
 #include <stdint.h>
 
 #include "fs_device.h"
+#include "fs_plan.h"
 
 namespace fs {
 
-constexpr int kMBlock = 16;        // vocab rows per MFMA block (M of 16x16x32)
 constexpr int kThreads = 256;      // threads per stage-1 workgroup (4 waves)
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kFlagNoNoise = 1u;
-
-enum Stage1Variant { kVarFlat = 0, kVarGrouped = 1, kVarLogits = 2, kVarTopk = 3 };
 
 // Balanced split of `nmb` vocab blocks over `G` workgroups: workgroup w owns
 // blocks [begin(w), begin(w+1)).  Every workgroup owns at least one block
@@ -65,6 +62,7 @@ struct SchedState {
 };
 constexpr unsigned long long kSchedTag = 0x4c4d4847554d4231ull;
 constexpr unsigned int kSchedTag32 = 0x53434844u;
+static_assert(sizeof(SchedState) <= kSchedBytes, "scheduler block");
 
 struct Stage1Args {
     const uint16_t* H;      // [B, d] bf16
@@ -100,45 +98,23 @@ struct Stage1Args {
     int dyn_k0;
 };
 
-struct Stage1Config {
-    int nb;   // 16-wide batch blocks per workgroup
-    int mpi;  // vocab blocks per group
-    int ks;   // 32-element k-steps per pipeline stage
-};
-
 hipError_t launch_stage1(int variant, const Stage1Args& a, int grid_y, const Stage1Config& cfg,
                          hipStream_t stream);
-
-// Resident-H stage 1: nw waves split the hidden dimension, hk + hl k-steps
-// each (nks == nw * (hk + hl); hk of them held in registers, hl in LDS), mpi
-// blocks per group, ks k-steps per pipeline stage.
-struct ResidentConfig {
-    int nb, mpi, ks, nw, hk, hl;
-};
-bool resident_supported(const ResidentConfig& c, int variant);
-// Preferred instantiated shape for nb batch blocks, nks k-steps and a
-// variant (nw == 0: none).
-ResidentConfig resident_default(int nb, int nks, int variant);
-// Top-k: the most vocabulary rows one resident workgroup of shape c may own.
-int resident_topk_rows(const ResidentConfig& c);
 
 // Top-k row store of one resident workgroup: the most vocabulary rows it
 // may own (x of all its columns in LDS): 96 KiB of x, or 640 rows when part
 // of the H slice also lives in LDS (hl > 0).
 template <int NB, int HL>
 struct TopkRows {
-    static constexpr int kRows = HL > 0 ? 640 : 96 * 1024 / (16 * NB * 4);   // multiple of 128
+    static constexpr int kRows = topk_store_rows(NB, HL);   // multiple of 128
     static constexpr int kStride = kRows + 4;   // padded row of one column
 };
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
                            hipStream_t stream);
 
-// LDS-tiled stage 1 for large batches (flat and logits variants): nt batch
-// columns per workgroup (64 or 128); requires d % 64 == 0.
-// The LDS-tiled stage 1 (fs_wide.hip): flat and logits with nt = 64 or 128;
+// LDS-tiled stage 1 (fs_wide.hip): flat and logits with nt = 64 or 128;
 // grouped with nt = 64 when every workgroup range meets at most
-// kWideMaxTiles vocabulary tiles.
-constexpr int kWideMaxTiles = 16;
+// kWideMaxTiles vocabulary tiles; nt = 256 goes to launch_wide_dma.
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream);
 // The same contraction fed by direct-to-LDS loads (fs_wide_dma.hip): flat and
 // logits, nt = 256, d % 32 == 0.
@@ -186,12 +162,9 @@ __device__ inline int row_id(const RowIds& m, int r) {
 struct DenseIds {
     int on, v_offset, unit_rows, unit_stride;
 };
-size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense);
-// Stage 2 of top-k runs in one kernel (stage2_topk_kernel): k <= 64, at most
-// 512 * 64 candidates per row, lists with ids.  sched (may be null; that
-// kernel only) is the unit scheduler block of the resident stage 1,
-// initialised by the kernel.
-bool topk_small_path(int G, int L, int k);
+// Stage 2 of top-k runs in one kernel (stage2_topk_kernel) when
+// topk_small_path holds: sched (may be null; that kernel only) is the unit
+// scheduler block of the resident stage 1, initialised by the kernel.
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,
                               DenseIds dn, float top_p, const float* temp, uint32_t flags,
                               const NoiseSrc& noise, int32_t* out_idx, void* scratch,

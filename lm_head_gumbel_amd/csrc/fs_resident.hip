@@ -498,27 +498,13 @@ static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream
     }
 }
 
-// Instantiated shapes (nb, mpi, ks, nw, hk, hl), in order of preference for
-// a given nb and k-step count nw * (hk + hl).  Each fits 256 registers per
-// lane without spilling; hl > 0 keeps the last hl k-steps of each wave's H
-// slice in LDS (d = 5120 with two batch blocks; the 18 + 2 split leaves
-// room in LDS for the top-k row store).
-#define FS_RESIDENT_SHAPES(X) \
-    X(1, 2, 4, 8, 16, 0)      \
-    X(1, 4, 2, 8, 16, 0)      \
-    X(1, 2, 4, 4, 32, 0)      \
-    X(1, 2, 4, 8, 8, 0)       \
-    X(1, 2, 2, 8, 20, 0)      \
-    X(1, 2, 2, 8, 4, 0)       \
-    X(1, 2, 1, 8, 2, 0)       \
-    X(2, 1, 4, 8, 16, 0)      \
-    X(2, 1, 2, 8, 16, 0)      \
-    X(2, 2, 2, 8, 16, 0)      \
-    X(2, 1, 2, 8, 16, 4)      \
-    X(2, 1, 2, 8, 18, 2)      \
-    X(2, 2, 4, 8, 8, 0)       \
-    X(2, 2, 2, 8, 4, 0)       \
-    X(2, 2, 1, 8, 2, 0)
+// The shapes of FS_RESIDENT_SHAPES (fs_plan.h): their top-k column must say
+// whether the row store fits in LDS beside the shape's own areas.
+#define FS_RES_CHECK(NB_, MPI_, KS_, NW_, HK_, HL_, TK_)          \
+    static_assert(topk_fits<NB_, MPI_, NW_, HL_>() == (TK_ != 0), \
+                  "top-k column of FS_RESIDENT_SHAPES");
+FS_RESIDENT_SHAPES(FS_RES_CHECK)
+#undef FS_RES_CHECK
 
 #define FS_RES_MATCH(NB_, MPI_, KS_, NW_, HK_, HL_) \
     (c.nb == NB_ && c.mpi == MPI_ && c.ks == KS_ && c.nw == NW_ && c.hk == HK_ && c.hl == HL_)
@@ -526,36 +512,12 @@ static hipError_t launch_res(const Stage1Args& a, int grid_y, hipStream_t stream
 template <int VAR>
 static hipError_t launch_res_var(const Stage1Args& a, int grid_y, const ResidentConfig& c,
                                  hipStream_t stream) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)          \
+#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_, TK_)    \
     if (FS_RES_MATCH(NB_, MPI_, KS_, NW_, HK_, HL_)) \
         return launch_res<NB_, MPI_, KS_, NW_, HK_, HL_, VAR>(a, grid_y, stream);
     FS_RESIDENT_SHAPES(FS_RES)
 #undef FS_RES
     return hipErrorInvalidValue;
-}
-
-bool resident_supported(const ResidentConfig& c, int variant) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)          \
-    if (FS_RES_MATCH(NB_, MPI_, KS_, NW_, HK_, HL_)) \
-        return variant != kVarTopk || topk_fits<NB_, MPI_, NW_, HL_>();
-    FS_RESIDENT_SHAPES(FS_RES)
-#undef FS_RES
-    return false;
-}
-
-int resident_topk_rows(const ResidentConfig& c) {
-    if (c.nb == 1) return c.hl > 0 ? TopkRows<1, 1>::kRows : TopkRows<1, 0>::kRows;
-    return c.hl > 0 ? TopkRows<2, 1>::kRows : TopkRows<2, 0>::kRows;
-}
-
-ResidentConfig resident_default(int nb, int nks, int variant) {
-#define FS_RES(NB_, MPI_, KS_, NW_, HK_, HL_)                                          \
-    if (nb == NB_ && nks == NW_ * (HK_ + HL_) &&                                     \
-        (variant != kVarTopk || topk_fits<NB_, MPI_, NW_, HL_>()))                   \
-        return ResidentConfig{NB_, MPI_, KS_, NW_, HK_, HL_};
-    FS_RESIDENT_SHAPES(FS_RES)
-#undef FS_RES
-    return ResidentConfig{0, 0, 0, 0, 0, 0};
 }
 
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,

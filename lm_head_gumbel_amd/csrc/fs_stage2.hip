@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kGrpThreads) void stage2_grouped_kernel(
 // than 512 * 64 candidates, take the sliced selection below.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 512;
+static_assert(kTopkThreads == kTopkStage2Threads, "the host plan picks the one-kernel form");
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkGather = 512;   // gathered candidates, at most 8 per lane of one wave
 
@@ -450,6 +451,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxK = kSelThreads;   // the finish holds one selected entry per thread
 constexpr int kSelPer = 16;          // candidates per thread, in registers
 constexpr int kSliceCap = kSelThreads * kSelPer;   // candidates per workgroup
+static_assert(kSliceCap == kTopkSliceCap, "the host plan sizes the selection levels");
 constexpr int kBins = 2048;          // two per thread
 constexpr int kTieCap = 4096;
 
@@ -1047,21 +1049,6 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                        pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,
                        tile_L, out_idx);
     return hipGetLastError();
-}
-
-namespace {
-size_t align_256(size_t x) { return (x + 255) / 256 * 256; }
-}  // namespace
-
-bool topk_small_path(int G, int L, int k) {   // the dense form never takes it
-    return k <= 64 && (int64_t)G * L <= (int64_t)kTopkThreads * 64;
-}
-
-size_t stage2_topk_scratch_bytes(int G, int L, int B, int k, bool dense) {
-    const int64_t n = (int64_t)G * L;
-    if ((topk_small_path(G, L, k) && !dense) || n <= kSliceCap) return 0;
-    const int64_t S = (n + kSliceCap - 1) / kSliceCap;
-    return 4 * align_256((size_t)S * B * k * 4);   // lists of two levels: x and ids
 }
 
 hipError_t launch_stage2_topk(const float* cx, const int32_t* cidx, int G, int L, int B, int k,
