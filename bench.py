@@ -395,6 +395,7 @@ def hbm_probe(torch, fs, W):
 # The sources the headline stage-1 kernel (resident_kernel) and its launch
 # plan are built from.
 DIGEST_SOURCES = ("fs_api.hip", "fs_device.h", "fs_epilogue.h", "fs_internal.h", "fs_mfma.h",
+                  "fs_plan.cpp", "fs_plan.h",
                   "fs_resident.hip", "fs_topk.h")
 
 

@@ -39,6 +39,11 @@ What is computed (all in float64; every helper is a direct definition):
                 set's mass, then argmax s over the kept prefix     [FS-kr top-p; CAKE]
   multinomial   inverse CDF of softmax(x) at a stream-3 uniform    [FS-kr problem statement]
 
+Besides the results, the oracle reports how far each result is from changing
+(top-two gaps, membership, cut and decision margins, and the robustness of
+top-k and top-p picks to small logit errors): the parity tests compare an
+index only where that distance exceeds the stated tolerance.
+
 Every function taking `seed` also accepts one seed per batch row (a
 length-B sequence): row b then draws all its noise under key seed[b].
 
@@ -394,15 +399,105 @@ def topk_topp_sample(x, s, k, top_p, id0=0):
         keep = excl < top_p
         kept = S[keep]
         # the kept ones are a prefix: the first dropped element (if any) and
-        # the last kept one bound the cut
+        # the last kept one bound the cut; the first element has no mass
+        # before it and is kept for every top_p > 0, so it bounds nothing
         nk = kept.size
-        d_in = abs(top_p - excl[nk - 1])
+        d_in = abs(top_p - excl[nk - 1]) if nk > 1 else math.inf
         d_out = abs(excl[nk] - top_p) if nk < S.size else math.inf
         cut[b] = min(d_in, d_out)
         j, _ = first_argmax(s[b, kept])
         out[b] = id0 + int(kept[j])
         gap[b] = top_two_gap(s[b, kept])
     return out, gap, margin, cut
+
+
+def _topk_bounds(xb, k, tol_x):
+    """For one row of x: the ids ordered by x descending then id, and the ids
+    certainly in the top-k set and possibly in it when every x may be off by
+    up to tol_x / 2 (S- = x above x(k+1) + tol_x, S+ = x at least x(k) - tol_x;
+    every valid id when there are at most k)."""
+    valid = np.nonzero(np.isfinite(xb))[0]
+    order = valid[np.lexsort((valid, -xb[valid]))]
+    if order.size <= k:
+        return order, order, order
+    xk, xk1 = xb[order[k - 1]], xb[order[k]]
+    s_minus = valid[xb[valid] > xk1 + tol_x]
+    s_plus = valid[xb[valid] >= xk - tol_x]
+    return order, s_minus, s_plus
+
+
+def topk_pick_margin(x, s, k, tol_x):
+    """How robust the top-k sample of each row is when x (and with it s) may be
+    off by up to tol_x / 2 per id, as a GPU's FP32 logits are.
+
+    Every top-k set the perturbed x can give lies between S- and S+ (see
+    _topk_bounds), and the sample over any set between them is the same
+    exactly when the argmax of s over S+ lies in S-.  Then the returned value
+    is the top-two gap of s over S+ (the noise error the sample withstands);
+    otherwise 0.  With x(k) - x(k+1) > 2 tol_x, S- = S+ = the top-k set and
+    this is topk_sample's own gap.  Rows with no valid id give inf."""
+    x = np.asarray(x, np.float64)
+    s = np.asarray(s, np.float64)
+    out = np.full(x.shape[0], math.inf)
+    for b in range(x.shape[0]):
+        order, s_minus, s_plus = _topk_bounds(x[b], k, tol_x)
+        if order.size == 0:
+            continue
+        j, _ = first_argmax(s[b, s_plus])
+        w = s_plus[j]
+        out[b] = top_two_gap(s[b, s_plus]) if w in set(s_minus.tolist()) else 0.0
+    return out
+
+
+def topp_pick_margin(x, s, k, top_p, tol_x, tol_mass):
+    """How robust the top-p-after-top-k sample of each row is when x (and s)
+    may be off by up to tol_x / 2 per id and the exclusive masses by tol_mass.
+
+    top_p = 1 keeps the whole top-k set: the top-k question
+    (topk_pick_margin).  Otherwise, for every possible member j of the top-k
+    set (S+), the mass ranked before it and the set's total mass are bounded
+    over all admissible perturbations: weights scale by at most 1 +- rho
+    (rho = e^(tol_x/2) - 1); at least the certain members (S-) with x above
+    x_j + tol_x rank before j, at most every possible member with x at least
+    x_j - tol_x does; the total lies between the smallest and largest sums of
+    k possible members.  j is certainly kept when it is a certain member and
+    even its largest exclusive mass stays below top_p - tol_mass, possibly
+    kept when its smallest one is below top_p + tol_mass.  The sample is the
+    same for every admissible kept set exactly when the argmax of s over the
+    possibly kept ids is certainly kept; the value is then the top-two gap of
+    s over the possibly kept ids, otherwise 0."""
+    x = np.asarray(x, np.float64)
+    s = np.asarray(s, np.float64)
+    out = np.full(x.shape[0], math.inf)
+    if top_p >= 1:
+        return topk_pick_margin(x, s, k, tol_x)
+    rho = math.expm1(tol_x / 2)
+    for b in range(x.shape[0]):
+        order, s_minus, s_plus = _topk_bounds(x[b], k, tol_x)
+        if order.size == 0:
+            continue
+        cand = s_plus[np.lexsort((s_plus, -x[b, s_plus]))]   # by x descending, then id
+        xc = x[b, cand]
+        wc = np.exp(xc - xc[0])
+        sure = np.isin(cand, s_minus)
+        zone = np.sort(wc[~sure])
+        n_more = min(k, cand.size) - int(sure.sum())
+        z_sure = wc[sure].sum()
+        z_lo = (z_sure + (zone[:n_more].sum() if n_more > 0 else 0.0)) * (1 - rho)
+        z_hi = (z_sure + (zone[zone.size - n_more:].sum() if n_more > 0 else 0.0)) * (1 + rho)
+        csum_sure = np.concatenate([[0.0], np.cumsum(np.where(sure, wc, 0.0))])
+        csum_all = np.concatenate([[0.0], np.cumsum(wc)])
+        before_min = np.searchsorted(-xc, -(xc + tol_x), side="left")    # x_i > x_j + tol_x
+        before_max = np.searchsorted(-xc, -(xc - tol_x), side="right")   # x_i >= x_j - tol_x
+        p_min = csum_sure[before_min] * (1 - rho)
+        p_max = (csum_all[before_max] - wc) * (1 + rho)
+        certain = sure & (p_max / z_lo < top_p - tol_mass)
+        possible = p_min / z_hi < top_p + tol_mass
+        k_plus = np.sort(cand[possible])
+        k_minus = set(cand[certain].tolist())
+        j, _ = first_argmax(s[b, k_plus])
+        out[b] = top_two_gap(s[b, k_plus]) if int(k_plus[j]) in k_minus else 0.0
+    return out
 
 
 def multinomial(x, temp=None, seed=0, step=0, flags=0, id0=0):

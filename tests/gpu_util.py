@@ -8,6 +8,9 @@ import lm_head_gumbel_amd as fs
 
 TOL_GAP = 1e-2      # indices must agree when the oracle's top-two noisy scores differ by more
 TOL_VALUE = 2e-3    # per-tile max and log-mass, absolute
+TOL_X = 1e-3        # top-k / top-p picks: robust to logit errors up to TOL_X / 2 per id
+TOL_MASS = 1e-4     # top-p cut: exclusive masses this far from top_p
+MIN_PINNED = 0.9    # full-size tests: at least this fraction of rows compared index for index
 
 
 def log(msg):
@@ -157,6 +160,29 @@ def check_index_rows(got, want, gap, s_oracle, id0=0, tol=TOL_GAP, what="index")
         assert s_oracle[b, j] >= s_oracle[b, want[b] - id0] - tol, \
             f"{what}: row {b} picked {got[b]} which is not a near-maximiser"
     return int(pinned.sum())
+
+
+def assert_pinned(pin, what, min_frac=MIN_PINNED):
+    """Log and require the fraction of rows compared index for index: a
+    selection helper that wrongly marked rows as unpinned would otherwise
+    empty the comparison without failing it."""
+    pin = np.asarray(pin, bool)
+    n = int(pin.sum())
+    log(f"  {what}: {n}/{pin.size} rows pinned")
+    assert pin.size == 0 or n >= min_frac * pin.size, \
+        f"{what}: only {n}/{pin.size} rows pinned (< {min_frac:.0%})"
+    return n
+
+
+def check_grouped_unpinned(got, want, tile_idx, pinned, what="grouped"):
+    """Rows whose hierarchical draw is not pinned: -1 only where the oracle
+    row is empty, otherwise one of the row's own tile winners."""
+    for b in np.nonzero(~np.asarray(pinned, bool))[0]:
+        if want[b] < 0:
+            assert got[b] == -1, f"{what}: row {b} should be empty, got {got[b]}"
+        else:
+            assert got[b] >= 0 and got[b] in set(np.asarray(tile_idx[b]).tolist()), \
+                f"{what}: row {b} drew {got[b]}, not a tile winner of the row"
 
 
 def check_values(got, want, tol=TOL_VALUE, what="value"):

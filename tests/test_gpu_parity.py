@@ -15,7 +15,8 @@ from lm_head_gumbel_amd.inputs import (bf16_bits_to_f32, f32_to_bf16_bits, hidde
                                        normal_f32, tiny_reference, weights_bf16)
 from oracle import fs_oracle as O
 from oracle import philox as px
-from gpu_util import (Inputs, TOL_CUT, TOL_GAP, TOL_VALUE, check_index_rows, check_values, log,
+from gpu_util import (Inputs, TOL_CUT, TOL_GAP, TOL_VALUE, check_grouped_unpinned,
+                      check_index_rows, check_values, log,
                       run_flat, run_grouped, run_logits, run_merge, run_multinomial, run_topk,
                       run_topp, torch)
 from stats_util import chi_square_p, chi_square_rows_p, softmax
@@ -140,8 +141,7 @@ def compare_all(Hb, Wb, temp=None, n_valid=None, allow=None, tile_v=128, v_offse
                 pinned[b] = False
         bad = np.nonzero(pinned & (go != r["grp_idx"]))[0]
         assert bad.size == 0, f"grouped sample rows {bad}"
-        for b in np.nonzero(~pinned)[0]:
-            assert go[b] == -1 or go[b] in set(ti[b].tolist())
+        check_grouped_unpinned(go, r["grp_idx"], ti, pinned)
         # top-k
         for k in topk:
             check_topk(x_in, p, r, k, v_offset)
