@@ -148,6 +148,25 @@ fs_status fs_sample(const fs_params* p, const void* H, const void* W, const floa
                     const uint32_t* allow, int32_t* out_idx, float* out_score,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* fs_sample_noalloc -- fs_sample for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  It calls no allocator: its workspace is a scratch
+ * array the library holds in device memory for the life of the process, one
+ * of FS_NOALLOC_SCRATCH_BYTES per device (reserved when the library is
+ * loaded), so the caller passes only inputs and outputs.  Arguments and
+ * results are those of fs_sample without the workspace.  A call whose
+ * workspace would exceed the array (fs_workspace_bytes(p, FS_VARIANT_FLAT,
+ * 0) + 256 > FS_NOALLOC_SCRATCH_BYTES; e.g. B > 32 with a hidden size that
+ * only the streaming kernel serves) returns FS_ERR_WORKSPACE and enqueues
+ * nothing.  Every call on a device shares that device's array and it keeps
+ * the last call's contents (no call needs it cleared): calls that overlap on
+ * one device -- on two streams, or from two host threads without ordering
+ * -- race and give wrong results; the caller must order them. */
+#define FS_NOALLOC_SCRATCH_BYTES (8u << 20)
+fs_status fs_sample_noalloc(const fs_params* p, const void* H, const void* W, const float* temp,
+                            const uint32_t* allow, int32_t* out_idx, float* out_score,
+                            void* stream);
+
 /* fs_sample_stage1 -- the fused Stage-1 kernel of fs_sample alone: streams W,
  * computes the logits on chip and leaves the per-workgroup winners in `ws`
  * (layout internal to the library) without the Stage-2 reduction.  For timing

@@ -55,6 +55,8 @@ _SIGS = {
                                              ctypes.c_int32]),
     "fs_sample": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, _P, _P, _P,
                                  ctypes.c_size_t, _P]),
+    "fs_sample_noalloc": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, _P, _P,
+                                         _P]),
     "fs_sample_stage1": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
     "fs_sample_grouped": (ctypes.c_int, [ctypes.POINTER(fs_params), _P, _P, _P, _P, _P, _P, _P,
@@ -150,6 +152,14 @@ def fs_sample(p, H, W, temp, allow, out_idx, out_score=None, ws=None, ws_bytes=N
     w, n = _ws(ws, ws_bytes)
     return lib().fs_sample(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(temp), _ptr(allow),
                            _ptr(out_idx), _ptr(out_score), w, n, _stream(stream))
+
+
+def fs_sample_noalloc(p, H, W, temp, allow, out_idx, out_score=None, stream=None):
+    return lib().fs_sample_noalloc(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(temp), _ptr(allow),
+                                   _ptr(out_idx), _ptr(out_score), _stream(stream))
+
+
+FS_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def fs_sample_stage1(p, H, W, temp, allow, ws=None, ws_bytes=None, stream=None):

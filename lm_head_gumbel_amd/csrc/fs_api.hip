@@ -14,9 +14,19 @@ namespace {
 
 using namespace fs;
 
+// Scratch memory of fs_sample_noalloc: one array per device, held for the
+// life of the process.  In host code this name is a host-side stand-in, not
+// a device address: the address each device's copy has is taken once per
+// device with hipGetSymbolAddress (DeviceInfo::scratch) and only that is
+// used.  The first kSchedBytes hold the unit scheduler block at a fixed
+// place; the call's records follow.
+constexpr size_t kScratchBytes = (size_t)FS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 struct DeviceInfo {
     bool ok = false;      // a gfx950 device
     int cus = 0;
+    void* scratch = nullptr;   // this device's copy of `scratch` (null: not found)
 };
 
 std::mutex g_mu;
@@ -38,6 +48,13 @@ bool current_device(DeviceInfo& out) {
             info.cus = prop.multiProcessorCount;
         } else {
             (void)hipGetLastError();
+        }
+        if (info.ok) {   // with device `dev` current
+            void* ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr)
+                info.scratch = ptr;
+            else
+                (void)hipGetLastError();
         }
         g_dev[dev] = info;
         g_dev_init[dev] = true;
@@ -206,10 +223,13 @@ size_t fs_workspace_bytes(const fs_params* p, int variant, int32_t k) {
 // Shared front half of fs_sample and fs_sample_stage1: validation, plan,
 // workspace carve-up and the stage-1 launch.  `done` is set when nothing is
 // left to do (B == 0, or V == 0 after filling the outputs).
+// own_scratch: the workspace is the device's scratch array of
+// fs_sample_noalloc (ws and ws_bytes are ignored): its scheduler block sits
+// at a fixed place, the first kSchedBytes, and the records follow.
 static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, const float* temp,
                              const uint32_t* allow, int32_t* out_idx, float* out_score,
                              void* ws, size_t ws_bytes, hipStream_t s, bool need_out,
-                             Plan& pl, Workspace& w, bool& done) {
+                             bool own_scratch, Plan& pl, Workspace& w, bool& done) {
     done = true;
     fs_status st = check_params(p);
     if (st != FS_OK) return st;
@@ -218,13 +238,20 @@ static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, c
     if (p->V > 0 && (st = check_operands(p, H, W)) != FS_OK) return st;
     DeviceInfo dev;
     if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    if (own_scratch) {
+        if (!dev.scratch) return FS_ERR_HIP;
+        ws = dev.scratch;
+        ws_bytes = kScratchBytes;
+    }
     if (p->V == 0)
         return need_out ? from_hip(launch_fill_idx(out_idx, p->B, -1, out_score, s)) : FS_OK;
     make_plan(p, kVarFlat, dev.cus, pl);
     if (!pl.launchable) return FS_ERR_UNSUPPORTED;
     const WsLayout lay = layout(FS_VARIANT_FLAT, pl, 0);
-    if (!ws || ws_bytes < lay.total) return FS_ERR_WORKSPACE;
-    w = carve(static_cast<char*>(ws), lay);
+    const size_t head = own_scratch ? kSchedBytes : 0;
+    if (!ws || ws_bytes < head + lay.total) return FS_ERR_WORKSPACE;
+    w = carve(static_cast<char*>(ws) + head, lay);
+    if (own_scratch) w.sched = static_cast<SchedState*>(ws);
     Stage1Args a = stage1_args(pl, p, H, W, temp, allow);
     a.pm = w.pm;
     a.pidx = w.pidx;
@@ -248,7 +275,20 @@ fs_status fs_sample(const fs_params* p, const void* H, const void* W, const floa
     Workspace w;
     bool done;
     fs_status st = flat_stage1(p, H, W, temp, allow, out_idx, out_score, ws, ws_bytes, s, true,
-                               pl, w, done);
+                               false, pl, w, done);
+    if (st != FS_OK || done) return st;
+    return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.P, pl.B, out_idx, out_score, w.sched, s));
+}
+
+fs_status fs_sample_noalloc(const fs_params* p, const void* H, const void* W, const float* temp,
+                            const uint32_t* allow, int32_t* out_idx, float* out_score,
+                            void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Plan pl;
+    Workspace w;
+    bool done;
+    fs_status st = flat_stage1(p, H, W, temp, allow, out_idx, out_score, nullptr, 0, s, true,
+                               true, pl, w, done);
     if (st != FS_OK || done) return st;
     return from_hip(launch_stage2_flat(w.pm, w.pidx, pl.P, pl.B, out_idx, out_score, w.sched, s));
 }
@@ -259,7 +299,7 @@ fs_status fs_sample_stage1(const fs_params* p, const void* H, const void* W, con
     Workspace w;
     bool done;
     return flat_stage1(p, H, W, temp, allow, nullptr, nullptr, ws, ws_bytes,
-                       static_cast<hipStream_t>(stream), false, pl, w, done);
+                       static_cast<hipStream_t>(stream), false, false, pl, w, done);
 }
 
 fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
