@@ -41,25 +41,39 @@ def alg_bytes(B, d=D, v=V):
 
 
 class Timer:
-    """HIP events on the current (library launch) stream."""
+    """HIP events on the current (library launch) stream: one event before the
+    first call and one after every call, so each call's duration is the time
+    between its neighbouring events (back-to-back calls: the GPU time each
+    took, gaps included)."""
 
     def __init__(self, torch):
         self.t = torch
 
     def run(self, fn, n):
+        """Mean seconds per call, wall seconds, and the per-call seconds."""
         t = self.t
         s = t.cuda.current_stream()
-        e0 = t.cuda.Event(enable_timing=True)
-        e1 = t.cuda.Event(enable_timing=True)
+        ev = [t.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         t.cuda.synchronize()
         w0 = time.perf_counter()
-        e0.record(s)
+        ev[0].record(s)
         for i in range(n):
             fn(i)
-        e1.record(s)
+            ev[i + 1].record(s)
         t.cuda.synchronize()
         wall = time.perf_counter() - w0
-        return e0.elapsed_time(e1) / 1e3 / n, wall
+        per = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(n)]
+        return ev[0].elapsed_time(ev[n]) / 1e3 / n, wall, per
+
+
+def pct(per, q):
+    """q-th percentile of per-call seconds, in microseconds."""
+    import numpy as np
+    return float(np.percentile(np.asarray(per) * 1e6, q))
+
+
+def dist(per):
+    return {"p10_us": pct(per, 10), "p50_us": pct(per, 50), "p90_us": pct(per, 90)}
 
 
 def make_inputs(torch, B, d=D, v=V):
@@ -90,12 +104,13 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
 
     for i in range(warmup):
         call(i)
-    t_call, wall = timer.run(call, steps)
+    t_call, wall, per_call = timer.run(call, steps)
     for i in range(max(2, warmup // 2)):
         stage1(i)
-    t_k1, _ = timer.run(stage1, steps)
+    t_k1, _, per_k1 = timer.run(stage1, steps)
     res = {"B": B, "calls_per_s": 1.0 / t_call, "tokens_per_s": B / t_call,
-           "us_per_call": t_call * 1e6, "stage1_us": t_k1 * 1e6,
+           "us_per_call": t_call * 1e6, "call": dist(per_call),
+           "stage1_us": t_k1 * 1e6, "stage1": dist(per_k1),
            "hbm_GBps": alg_bytes(B) / t_k1 / 1e9,
            "hbm_frac": alg_bytes(B) / t_k1 / PEAK_HBM,
            "mfma_frac": 2.0 * B * D * V / t_k1 / PEAK_BF16,
@@ -114,7 +129,7 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
 
         for i in range(max(2, warmup // 2)):
             base(i)
-        t_base, _ = timer.run(base, max(10, steps // 4))
+        t_base = timer.run(base, max(10, steps // 4))[0]
         res["unfused_calls_per_s"] = 1.0 / t_base
         res["fused_speedup"] = t_base / t_call
         del logits
@@ -201,12 +216,15 @@ def bench_workloads(torch, fs, steps, W_head):
     def timed(fn):
         for i in range(3):
             fn(i)
-        return timer.run(fn, n)[0]
+        t, _, per = timer.run(fn, n)
+        return t, per
 
-    def line(name, wl, what, t, extra=None):
+    def line(name, wl, what, tp, extra=None):
+        t, per = tp
         r = {"workload": name, "B": wl.B, "d": wl.d, "V": wl.V, "what": what,
-             "calls_per_s": 1.0 / t, "us_per_call": t * 1e6,
+             "calls_per_s": 1.0 / t, "us_per_call": t * 1e6, "p50_us": pct(per, 50),
              "hbm_GBps": alg_bytes(wl.B, wl.d, wl.V) / t / 1e9,
+             "hbm_frac": alg_bytes(wl.B, wl.d, wl.V) / t / PEAK_HBM,
              "mfma_frac": 2.0 * wl.B * wl.d * wl.V / t / PEAK_BF16}
         if extra:
             r.update(extra)
@@ -237,6 +255,12 @@ def bench_workloads(torch, fs, steps, W_head):
             fs.check(fs.fs_sample(p, H, W, temp, None, idx, None, ws), name)
 
         line(name, wl, "flat fs_sample", timed(flat))
+
+        def flat_stage1(i):
+            p.step = i
+            fs.check(fs.fs_sample_stage1(p, H, W, temp, None, ws), name)
+
+        line(name, wl, "flat stage 1 alone (fs_sample_stage1)", timed(flat_stage1))
         if name == "mid_b64":
             T = fs.fs_num_tiles(p)
             tm = torch.empty((wl.B, T), dtype=torch.float32, device="cuda")
@@ -325,19 +349,28 @@ def bench_workloads(torch, fs, steps, W_head):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, H_all, W, B, seconds):
     """The CPU oracle (numpy float64: logits, Philox-Gumbel noise, argmax) on
-    the headline batch.  Whole calls are repeated (steps 0, 1, ...) until about
-    `seconds` of CPU time is spent; if one call is longer than that, a prefix
-    of the vocabulary is timed and scaled to the full call."""
+    the headline batch, timed twice: with every BLAS thread the host offers
+    and with one.  Whole calls are repeated (steps 0, 1, ...) until about
+    `seconds` of CPU time is spent in each mode; if one call is longer than
+    that, a prefix of the vocabulary is timed and scaled to the full call."""
     import numpy as np
     from oracle import fs_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
     Hb = H_all[:B].view(torch.int16).cpu().numpy().view(np.uint16)
+    W_host = W.view(torch.int16).cpu().numpy().view(np.uint16)
 
     def call(Wb, step):
         l = O.logits_bf16(Hb, Wb)
@@ -345,31 +378,34 @@ def cpu_baseline(torch, H_all, W, B, seconds):
         s = O.scores(x, None, SEED, step, 0, 0)
         return O.sample_flat(s)[0]
 
-    Wsmall = W[:4096].view(torch.int16).cpu().numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    call(Wsmall, 0)
-    est = (time.perf_counter() - t0) * V / 4096          # seconds per full call, estimated
-    if est <= seconds:
-        Wb = W.view(torch.int16).cpu().numpy().view(np.uint16)
-        n, t0 = 0, time.perf_counter()
-        while n == 0 or time.perf_counter() - t0 < seconds:
-            call(Wb, n)
-            n += 1
-        t = time.perf_counter() - t0
-        per_call = t / n
-        sample = (f"{n} full oracle calls (float64 logits + Philox-Gumbel + argmax), B={B}, "
-                  f"d={D}, V={V}, steps 0..{n - 1}: {t:.1f} s")
-    else:
-        nv = int(min(V, max(4096, 4096 * seconds / est * V / 4096)) // 16 * 16)
-        Wb = W[:nv].view(torch.int16).cpu().numpy().view(np.uint16)
+    def timed():
         t0 = time.perf_counter()
-        call(Wb, 0)
+        call(W_host[:4096], 0)
+        est = (time.perf_counter() - t0) * V / 4096          # seconds per full call, estimated
+        if est <= seconds:
+            n, t0 = 0, time.perf_counter()
+            while n == 0 or time.perf_counter() - t0 < seconds:
+                call(W_host, n)
+                n += 1
+            t = time.perf_counter() - t0
+            return t / n, (f"{n} full oracle calls (float64 logits + Philox-Gumbel + argmax), "
+                           f"B={B}, d={D}, V={V}, steps 0..{n - 1}: {t:.1f} s")
+        nv = int(min(V, max(4096, 4096 * seconds / est * V / 4096)) // 16 * 16)
+        t0 = time.perf_counter()
+        call(W_host[:nv], 0)
         t = time.perf_counter() - t0
-        per_call = t * V / nv
-        sample = (f"one oracle call over the first {nv} of {V} ids (B={B}, d={D}): {t:.1f} s, "
-                  f"scaled by {V}/{nv}")
-    return {"value": 1.0 / per_call, "unit": "calls/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds_per_call": per_call}
+        return t * V / nv, (f"one oracle call over the first {nv} of {V} ids (B={B}, d={D}): "
+                            f"{t:.1f} s, scaled by {V}/{nv}")
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    per_all, sample_all = timed()
+    with threadpool_limits(limits=1):
+        per_one, sample_one = timed()
+    return {"value": 1.0 / per_all, "unit": "calls/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample_all, "seconds_per_call": per_all,
+            "single_thread": {"value": 1.0 / per_one, "unit": "calls/s", "cores": 1,
+                              "sample": sample_one, "seconds_per_call": per_one},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def hbm_probe(torch, fs, W):
@@ -380,13 +416,13 @@ def hbm_probe(torch, fs, W):
     timer = Timer(torch)
     for i in range(3):
         fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256), "read probe")
-    t_read, _ = timer.run(lambda i: fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256)), 20)
+    t_read = timer.run(lambda i: fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256)), 20)[0]
     n = 1 << 30
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
     for i in range(3):
         fs.check(fs.fs_debug_copy(b, a, n, 1024), "copy")
-    t_copy, _ = timer.run(lambda i: fs.check(fs.fs_debug_copy(b, a, n, 1024)), 10)
+    t_copy = timer.run(lambda i: fs.check(fs.fs_debug_copy(b, a, n, 1024)), 10)[0]
     del a, b
     return {"read_GBps": nbytes / t_read / 1e9, "copy_GBps": 2 * n / t_copy / 1e9,
             "read_grid": 256, "copy_grid": 1024, "copy_bytes": n}
@@ -464,6 +500,13 @@ def main():
     log(f"generating inputs d={D} V={V} (W {2 * V * D / 1e9:.2f} GB bf16)")
     H_all, W = make_inputs(torch, bmax)
 
+    # the HBM ceilings first: a measurement of its own, and the device's clocks
+    # have settled by the time the headline is timed
+    probe = None
+    if not args.no_probe:
+        probe = hbm_probe(torch, fs, W)
+        log(json.dumps(probe))
+
     log(f"headline B={args.batch}: {args.warmup} warmup + {args.steps} timed calls")
     head = bench_batch(torch, fs, H_all, W, args.batch, args.steps, args.warmup,
                        unfused=True, variants=not args.no_variants)
@@ -482,11 +525,6 @@ def main():
         log("other workloads and shard shapes")
         workloads = bench_workloads(torch, fs, args.steps, W)
 
-    probe = None
-    if not args.no_probe:
-        probe = hbm_probe(torch, fs, W)
-        log(json.dumps(probe))
-
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -502,6 +540,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["us_per_call"] / 1e3,
+        "per_call_us": head["call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -515,7 +554,7 @@ def main():
                      "frac": alg_bytes(args.batch) / t_k1 / PEAK_HBM,
                      "traffic": stored_traffic(args.batch),
                      "kernel": "fs::resident_kernel (flat stage 1)",
-                     "kernel_us": head["stage1_us"],
+                     "kernel_us": head["stage1_us"], "kernel_per_launch_us": head["stage1"],
                      "bytes_per_launch": alg_bytes(args.batch),
                      "frac_of_read_probe": (alg_bytes(args.batch) / t_k1 / 1e9 / probe["read_GBps"]
                                             if probe else None)},
