@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfs.so")
 SOURCES = ["fs_api.hip", "fs_plan.cpp", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip",
-           "fs_wide_dma.hip", "fs_stage2.hip", "fs_probe.hip"]
+           "fs_wide_dma.hip", "fs_rows.hip", "fs_stage2.hip", "fs_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -27,6 +27,13 @@ def hipcc():
 # rewriting of atomics (it would read the ticket back at once, waiting for
 # every load in flight; the kernel uses it only after the contraction).
 EXTRA_FLAGS = {"fs_resident.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
+# Sources whose kernels issue untracked loads from inline assembly and count
+# their waits by hand: the build also emits their assembly and proves that the
+# compiler touches no register of such a load before a wait retires it
+# (isa_check.py); a failure stops the build.
+ISA_CHECKED = ["fs_rows.hip"]
 
 
 def common_flags():
@@ -67,14 +74,29 @@ def build(verbose=False):
                 print(" ".join(cmd), flush=True)
             return src, subprocess.run(cmd, capture_output=True, text=True)
 
-        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        asm_jobs = []
+        for src in ISA_CHECKED:
+            out = os.path.join(objdir, os.path.splitext(src)[0] + ".s")
+            cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + \
+                ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+            asm_jobs.append((src + " (assembly)", out, cmd))
+
+        workers = max(1, min(len(jobs) + len(asm_jobs), os.cpu_count() or 1, 8))
         with ThreadPoolExecutor(workers) as ex:
-            results = list(ex.map(run, jobs))
+            results = list(ex.map(run, jobs + asm_jobs))
         failed = [(src, r) for src, r in results if r.returncode != 0]
         for src, r in failed:
             sys.stderr.write(f"--- {src}\n" + r.stdout + r.stderr)
         if failed:
             raise RuntimeError("hipcc failed building libfs.so: " + ", ".join(s for s, _ in failed))
+        from . import isa_check
+        for src, out, _ in asm_jobs:
+            with open(out) as f:
+                errors = isa_check.check_text(f.read(), require_untracked=True)
+            if errors:
+                sys.stderr.write("\n".join(errors[:20]) + "\n")
+                raise RuntimeError("%s: %d register(s) of untracked loads touched in flight"
+                                   % (src, len(errors)))
         link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + \
             [obj for _, obj, _ in jobs]
         if verbose:

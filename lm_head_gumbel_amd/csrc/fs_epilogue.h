@@ -36,6 +36,46 @@ __device__ __forceinline__ ColCtx col_ctx(const Stage1Args& a, int col) {
     return c;
 }
 
+// Column contexts of N consecutive columns kept in LDS.  The LDS-tiled
+// kernels rebuild a column's context in every tile's epilogue (held in
+// registers through the contraction they would spill); reading the
+// temperatures, per-row seeds and the device step from global memory there
+// would leave loads whose completion the compiler cannot track across the
+// contraction loop, and it then drains every load in flight (a full vmcnt
+// wait) once per chunk.  Filled once per workgroup before the loop.
+template <int N>
+struct ColCtxSmem {
+    float inv_t[N];
+    uint32_t k0[N], k1[N], step[N];
+    uint32_t flags[N];   // bit 0: column < B, bit 1: greedy
+};
+
+template <int N>
+__device__ __forceinline__ void col_ctx_store(ColCtxSmem<N>& s, const Stage1Args& a, int col0) {
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        const ColCtx c = col_ctx(a, col0 + i);
+        s.inv_t[i] = c.inv_t;
+        s.k0[i] = c.key.k0;
+        s.k1[i] = c.key.k1;
+        s.step[i] = c.key.step;
+        s.flags[i] = (c.ok ? 1u : 0u) | (c.greedy ? 2u : 0u);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ ColCtx col_ctx_load(const ColCtxSmem<N>& s, const Stage1Args& a,
+                                               int col0, int i) {
+    ColCtx c;
+    c.col = col0 + i;
+    const uint32_t f = s.flags[i];
+    c.ok = (f & 1u) != 0;
+    c.greedy = (f & 2u) != 0;
+    c.inv_t = s.inv_t[i];
+    c.allow_row = (a.allow && c.ok) ? a.allow + (size_t)c.col * ((a.V + 31) >> 5) : nullptr;
+    c.key = RowKey{s.k0[i], s.k1[i], s.step[i]};
+    return c;
+}
+
 // The allow word of column c that holds rows row0..row0+3 (row0 % 4 == 0, so
 // one word holds all four): read only for a masked column and rows inside V;
 // all ones otherwise.  One read per fold instead of one per row: each wait

@@ -121,6 +121,10 @@ hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hip
 hipError_t launch_wide_dma(int variant, const Stage1Args& a, int nt, int grid_y,
                            hipStream_t stream);
 
+// Row-streaming stage 1 for large batches (fs_rows.hip): flat and logits,
+// nt = 64, 128 or 256 batch columns per workgroup, d % (64 rows_kcs(nt)) == 0.
+hipError_t launch_rows(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream);
+
 // Streaming stage 1 (flat, grouped or logits) over a.G workgroups of four
 // worker waves; `part` holds grid_y * 4 * a.G * 2 * nb KiB of partial sums.
 // with_fixup also launches the kernel finishing the split blocks.

@@ -114,13 +114,13 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
             pl.kind = kResident;
         else if (pl.nmb >= 4)
             pl.kind = kStream;
-        // large batches: the LDS-tiled kernel shares each W tile among all columns
-        // (chunks of d: 128 deep for 64 columns, 64 deep for 128)
+        // large batches: W rows streamed into registers against all the
+        // workgroup's columns (up to 256), H in chunks through LDS
+        const int nt = p->B <= 64 ? 64 : p->B <= 128 ? 128 : 256;
         if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
-            p->d % (p->B <= 64 ? 128 : 64) == 0 &&
-            wide_offsets_fit(pl, std::max(1, std::min(pl.nmb, cus)))) {
-            pl.kind = kWide;
-            pl.nt = p->B <= 64 ? 64 : p->B <= 128 ? 128 : 256;
+            p->d % (64 * rows_kcs(nt)) == 0) {
+            pl.kind = kRows;
+            pl.nt = nt;
         }
         // grouped records up to 64 columns: one workgroup per CU, each range
         // meeting at most kWideMaxTiles vocabulary tiles (its slots live in LDS)
@@ -138,7 +138,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     pl.cfg = pick_config(pl.stream, p->B);
 
     // 2. batch groups
-    const int cols = pl.kind == kWide       ? pl.nt
+    const int cols = (pl.kind == kWide || pl.kind == kRows) ? pl.nt
                      : pl.kind == kResident ? 16 * pl.rcfg.nb
                                             : 16 * pl.cfg.nb;
     pl.grid_y = ceil_div(p->B, cols);
@@ -174,7 +174,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         }
     }
     pl.xcd_pair = 0;
-    if ((pl.kind == kResident || pl.kind == kWide) && pl.grid_y > 1) {
+    if ((pl.kind == kResident || pl.kind == kWide || pl.kind == kRows) && pl.grid_y > 1) {
         // all batch groups of a row range resident at once, on one XCD
         int g = (cus / pl.grid_y) / 8 * 8;
         if (g < min_g) g = (min_g + 7) / 8 * 8;

@@ -33,8 +33,18 @@ enum Stage1Variant { kVarFlat = 0, kVarGrouped = 1, kVarLogits = 2, kVarTopk = 3
 // Stage-1 kernel families: resident (H slice in registers; the default for
 // the common shapes), stream (independent worker waves, H reloaded per stage),
 // coop (workgroup-cooperative, H reloaded per stage; top-k and the shapes the
-// others do not cover) and wide (LDS-tiled, large batches).
-enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2, kWide = 3 };
+// others do not cover), rows (large batches: W rows streamed into registers,
+// H chunks through LDS; flat and logits) and wide (LDS-tiled; grouped records
+// for 32 < B <= 64).
+enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2, kWide = 3, kRows = 4 };
+
+// The row-streaming large-batch kernel (fs_rows.hip): H chunks of KCS k-steps
+// per batch-column tile of 64, 128 or 256 columns, taken in pairs; d must be a
+// multiple of 64 KCS.
+constexpr int kRowsKcs64 = 8;
+constexpr int kRowsKcs128 = 4;
+constexpr int kRowsKcs256 = 4;
+constexpr int rows_kcs(int nt) { return nt == 64 ? kRowsKcs64 : nt == 128 ? kRowsKcs128 : kRowsKcs256; }
 
 struct Stage1Config {
     int nb;   // 16-wide batch blocks per workgroup
@@ -94,7 +104,7 @@ struct Plan {
     int P;         // record slots per row
     Stage1Config cfg;
     ResidentConfig rcfg;
-    int nt;        // kWide: batch columns per workgroup
+    int nt;        // kWide, kRows: batch columns per workgroup
     int grid_y;
     int xcd_pair;
     uint32_t k0, k1;

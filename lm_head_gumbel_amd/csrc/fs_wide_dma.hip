@@ -49,6 +49,7 @@ template <int NT>
 struct WideDmaSmem {
     alignas(1024) char buf[WideDmaGeom<NT>::kStages][WideDmaGeom<NT>::kStageBytes];
     uint64_t fkey[2][NT];
+    ColCtxSmem<NT> cols;
 };
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
@@ -166,6 +167,10 @@ __global__ __launch_bounds__(kDThreads) void wide_dma_kernel(Stage1Args a) {
         }
     };
 
+    // the contexts of the workgroup's columns, read back in every epilogue
+    col_ctx_store(sm.cols, a, bbase);
+    __syncthreads();
+
     // per-lane column winners of this wave (one per B fragment)
     uint64_t best[NF];
 #pragma unroll
@@ -222,35 +227,46 @@ __global__ __launch_bounds__(kDThreads) void wide_dma_kernel(Stage1Args a) {
 
         if (c + 1 == nchunks) {
             // the tile is complete: fold its logits into the column winners
-            // (the column contexts are rebuilt per tile from a few cached
-            // loads: registers held through the contraction would spill)
+            // (the column contexts are rebuilt per tile from LDS: registers
+            // held through the contraction would spill)
             ColCtx cxs[NF];
             static_for<NF>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
-                cxs[n] = col_ctx(a, bbase + wn * (NT / WN) + n * 16 + r16);
+                cxs[n] = col_ctx_load(sm.cols, a, bbase, wn * (NT / WN) + n * 16 + r16);
             });
-            static_for<MF>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                if (j < nvalid) {   // uniform
-                    const int row0 = (blk0 + j) * kMBlock + 4 * kg;
-                    static_for<NF>([&](auto nc) {
-                        constexpr int n = decltype(nc)::value;
-                        const ColCtx& cx = cxs[n];
-                        if constexpr (VAR == kVarLogits) {
-                            if (cx.ok) {
-                                float* dst = a.logits + (size_t)cx.col * a.V;
+            // MASKED: the allow words are read here.  Without a mask (a
+            // uniform branch) the epilogue issues no memory load at all, so
+            // nothing makes the loads of the next chunks wait.
+            auto fold_tile = [&](auto masked) {
+                static_for<MF>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if (j < nvalid) {   // uniform
+                        const int row0 = (blk0 + j) * kMBlock + 4 * kg;
+                        static_for<NF>([&](auto nc) {
+                            constexpr int n = decltype(nc)::value;
+                            const ColCtx& cx = cxs[n];
+                            if constexpr (VAR == kVarLogits) {
+                                if (cx.ok) {
+                                    float* dst = a.logits + (size_t)cx.col * a.V;
 #pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    if (row0 + r < a.V) dst[row0 + r] = acc[j][n][r];
+                                    for (int r = 0; r < 4; ++r)
+                                        if (row0 + r < a.V) dst[row0 + r] = acc[j][n][r];
+                                }
+                            } else {
+                                const uint32_t word =
+                                    decltype(masked)::value ? allow_word(a, cx, row0, true) : ~0u;
+                                float x[4], sc[4];
+                                lane_scores(a, cx, acc[j][n], row0, true, word, x, sc);
+                                fold<kVarFlat>(best[n], unused, x, sc, a.v_offset + row0);
                             }
-                        } else {
-                            float x[4], sc[4];
-                            lane_scores(a, cx, acc[j][n], row0, true, x, sc);
-                            fold<kVarFlat>(best[n], unused, x, sc, a.v_offset + row0);
-                        }
-                    });
-                }
-            });
+                        });
+                    }
+                });
+            };
+            if (a.allow != nullptr)
+                fold_tile(std::true_type{});
+            else
+                fold_tile(std::false_type{});
 #pragma unroll
             for (int j = 0; j < MF; ++j)
 #pragma unroll

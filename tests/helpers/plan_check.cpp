@@ -81,18 +81,24 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
         CHECK(pl.xcd_pair ? (int64_t)pl.G * pl.grid_y <= kMaxGridX
                           : pl.G <= kMaxGridX && pl.grid_y <= kMaxGridY,
               "grid %d x %d", pl.G, pl.grid_y);
-        CHECK(pl.kind >= kCoop && pl.kind <= kWide, "kind %d", pl.kind);
+        CHECK(pl.kind >= kCoop && pl.kind <= kRows, "kind %d", pl.kind);
         CHECK(pl.stream == (pl.kind == kStream), "stream flag");
-        const int cols = pl.kind == kWide ? pl.nt : pl.kind == kResident ? 16 * pl.rcfg.nb
-                                                                         : 16 * pl.cfg.nb;
+        const int cols = (pl.kind == kWide || pl.kind == kRows) ? pl.nt
+                         : pl.kind == kResident                  ? 16 * pl.rcfg.nb
+                                                                 : 16 * pl.cfg.nb;
         CHECK(cols >= 16 && (int64_t)pl.grid_y * cols >= B && (int64_t)(pl.grid_y - 1) * cols < B,
               "grid_y %d cols %d B %d", pl.grid_y, cols, B);
         if (pl.kind == kResident) {
             CHECK(pl.rcfg.nw > 0 && resident_supported(pl.rcfg, var), "resident shape");
             CHECK(pl.rcfg.nw * (pl.rcfg.hk + pl.rcfg.hl) == cdiv(d, 32), "resident k-steps");
         }
-        if (pl.kind == kWide) {
+        if (pl.kind == kRows) {
+            CHECK(var == kVarFlat || var == kVarLogits, "rows variant");
+            CHECK(d % (64 * rows_kcs(pl.nt)) == 0, "rows d %d nt %d", d, pl.nt);
+        }
+        if (pl.kind == kWide || pl.kind == kRows)
             CHECK(pl.nt == 64 || pl.nt == 128 || pl.nt == 256, "nt %d", pl.nt);
+        if (pl.kind == kWide) {   // 32-bit element offsets (the rows kernel forms 64-bit ones)
             CHECK((int64_t)B * d < INT32_MAX, "wide H offsets B %d d %d", B, d);
             CHECK((cdiv(pl.nmb, pl.G) * kMBlock + 256) * d < INT32_MAX, "wide W offsets");
             CHECK(var != kVarGrouped || pl.nt == 64, "wide grouped nt");
@@ -203,6 +209,14 @@ int main() {
     check_case(32, 5120, 152064, 0, 256, 256, "topk_b32");
     check_case(4, 256, 4096, 0, 512, 256, "tiny_b4");
     check_case(32, 4096, 18992, 132944, 0, 256, "shard8_b32");
+    // parity cases meant for the row-streaming kernel
+    check_case(33, 512, 3001, 16, 64, 256, "rows_b33");
+    check_case(40, 4096, 3000, 0, 128, 256, "rows_b40");
+    check_case(100, 256, 3001, 0, 64, 256, "rows_b100");
+    check_case(128, 512, 70000, 32, 2048, 256, "rows_b128");
+    check_case(150, 256, 2000, 0, 128, 256, "rows_b150");
+    check_case(256, 256, 70000, 0, 4096, 256, "rows_b256");
+    check_case(300, 256, 5000, 0, 64, 256, "rows_b300");
 
     // a grid of shapes, extremes included
     const int Bs[] = {1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,

@@ -217,8 +217,8 @@ def test_compute_lean_sampled_rows(B):
 @pytest.mark.parametrize("B", [128, 256])
 def test_headline_vocab_large_batches(B):
     """B = 128 and 256 at the headline shape d=4096, V=151936 (the benchmark
-    sweep's largest batches): the LDS-tiled kernels with a partial last tile
-    in every workgroup range."""
+    sweep's largest batches): the row-streaming kernel at 128 and 256 columns
+    per workgroup, with a partial last tile in every workgroup range."""
     log(f"headline vocabulary B={B} d={D_HEAD} V={V_HEAD}")
     Hb = hidden_bf16(B, D_HEAD)
     Wb = weights(V_HEAD, D_HEAD)

@@ -49,13 +49,25 @@ def test_plans_and_layouts_under_sanitizers(plan_check):
             kv = dict(x.split("=") for x in f[2:])
             plans[(f[1], int(kv["var"]))] = kv
     # the headline call: the register-resident kernel, one workgroup per CU,
-    # last units by ticket; the largest batch: the 256-column LDS-tiled kernel
+    # last units by ticket; the largest batch: the 256-column row-streaming kernel
     h = plans[("headline_b32", 0)]
     assert (h["kind"], h["G"], h["grid_y"], h["rcfg"]) == ("2", "256", "1", "2,1,4,8,16,0")
     assert int(h["dyn_k0"]) == 9496 // 256 - 2
     assert plans[("headline_b32", 1)]["dyn_k0"] == "0"        # grouped keeps its ranges
-    assert plans[("sweep_b256", 0)]["kind"] == "3" and plans[("sweep_b256", 0)]["nt"] == "256"
+    assert plans[("sweep_b256", 0)]["kind"] == "4" and plans[("sweep_b256", 0)]["nt"] == "256"
     assert plans[("sweep_b128", 0)]["nt"] == "128"
     assert plans[("mid_b64", 1)]["kind"] == "3"               # grouped B = 64 on the LDS kernel
     assert plans[("topk_b32", 3)]["rcfg"] == "2,1,2,8,18,2"   # d = 5120: H partly in LDS
     assert plans[("tiny_b4", 0)]["kind"] == "1"                # d = 256: the streaming kernel
+    # the parity cases of the row-streaming kernel reach it, flat and logits,
+    # at each column width, with several tiles per range and two column groups
+    for name, nt, gy in [("rows_b33", 64, 1), ("rows_b40", 64, 1), ("rows_b100", 128, 1),
+                         ("rows_b128", 128, 1), ("rows_b150", 256, 1), ("rows_b256", 256, 1),
+                         ("rows_b300", 256, 2)]:
+        for var in (0, 2):   # flat, logits
+            pl = plans[(name, var)]
+            assert (pl["kind"], pl["nt"], pl["grid_y"]) == ("4", str(nt), str(gy)), (name, pl)
+    assert plans[("rows_b300", 0)]["xcd"] == "1"
+    # ranges of 17 blocks: two 256-row tiles
+    for name in ("rows_b128", "rows_b256"):
+        assert 70000 // 16 // int(plans[(name, 0)]["G"]) >= 17
