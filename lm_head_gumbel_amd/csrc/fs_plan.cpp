@@ -116,7 +116,9 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
             pl.kind = kStream;
         // large batches: W rows streamed into registers against all the
         // workgroup's columns (up to 256), H in chunks through LDS
-        const int nt = p->B <= 64 ? 64 : p->B <= 128 ? 128 : 256;
+        const int nt = p->B <= kRows64.nt    ? kRows64.nt
+                       : p->B <= kRows128.nt ? kRows128.nt
+                                             : kRows256.nt;
         if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
             p->d % (64 * rows_kcs(nt)) == 0) {
             pl.kind = kRows;

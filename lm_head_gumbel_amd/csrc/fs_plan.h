@@ -38,13 +38,22 @@ enum Stage1Variant { kVarFlat = 0, kVarGrouped = 1, kVarLogits = 2, kVarTopk = 3
 // for 32 < B <= 64).
 enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2, kWide = 3, kRows = 4 };
 
-// The row-streaming large-batch kernel (fs_rows.hip): H chunks of KCS k-steps
-// per batch-column tile of 64, 128 or 256 columns, taken in pairs; d must be a
-// multiple of 64 KCS.
-constexpr int kRowsKcs64 = 8;
-constexpr int kRowsKcs128 = 4;
-constexpr int kRowsKcs256 = 4;
-constexpr int rows_kcs(int nt) { return nt == 64 ? kRowsKcs64 : nt == 128 ? kRowsKcs128 : kRowsKcs256; }
+// The row-streaming large-batch kernel (fs_rows.hip): workgroups of 64, 128
+// or 256 batch columns (more columns: several column groups), H chunks of KCS
+// k-steps taken in pairs (d a multiple of 64 KCS).
+struct RowsShape {
+    int nt;    // batch columns per workgroup
+    int kra;   // 16-row blocks per wave and tile (tiles of 128 kra rows)
+    int kcs;   // k-steps of 32 per H chunk
+    int pf;    // k-steps of W in flight per wave (at most)
+    int gq;    // k-steps of W loaded at a time (runs of 64 gq bytes per row)
+};
+constexpr RowsShape kRows64 = {64, 2, 8, 8, 4};
+constexpr RowsShape kRows128 = {128, 2, 8, 8, 4};
+constexpr RowsShape kRows256 = {256, 2, 4, 4, 2};
+constexpr int rows_kcs(int nt) {
+    return nt == kRows64.nt ? kRows64.kcs : nt == kRows128.nt ? kRows128.kcs : kRows256.kcs;
+}
 
 struct Stage1Config {
     int nb;   // 16-wide batch blocks per workgroup

@@ -41,8 +41,6 @@ namespace fs {
 namespace {
 
 constexpr int kRWaves = 8;
-constexpr int kRA = 2;                       // 16-row blocks per wave and tile
-constexpr int kRMT = kRWaves * kRA * 16;     // 256 rows per tile
 
 template <int N>
 __device__ __forceinline__ void rows_wait_vmcnt() {
@@ -50,10 +48,30 @@ __device__ __forceinline__ void rows_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// tile row of A-operand row `ar` (0..15) of block j of wave `wave`
+// tile row of A-operand row `ar` (0..15) of block j of wave `wave`: block j
+// covers tile rows 128 j .. 128 j + 127 across the waves
 __device__ __forceinline__ int rows_tile_row(int wave, int j, int ar) {
     return ((j * 4 + (ar >> 2)) * kRWaves + wave) * 4 + (ar & 3);
 }
+
+// The W ring is refilled in groups of GQ k-steps: after k-step kk with
+// kk % GQ == GQ - 1, the loads of k-steps kk + PF - GQ + 1 .. kk + PF go out
+// back to back, so that each row is read in runs of 64 GQ bytes (whole
+// 128-byte lines leave the L1 cache as one request, and DRAM pages see runs
+// instead of single lines).  The load of k-step kk thus went out at the end of
+// k-step e = (kk | (GQ - 1)) - PF, and the wait before k-step kk lets these
+// loads stay in flight: the later members of its group and the later groups
+// ((PF - 1 - kk % GQ) JN loads), and the H part loads issued since, at the
+// k-steps of this chunk from e + 1 on that are multiples of KP (parts of the
+// previous chunk are not counted: a wait for fewer younger loads than there
+// are waits longer, never shorter).
+constexpr int rows_h_issues(int kk, int PF, int KP, int GQ) {
+    int n = 0;
+    for (int q = (kk | (GQ - 1)) - PF + 1 < 0 ? 0 : (kk | (GQ - 1)) - PF + 1; q <= kk; ++q)
+        n += q % KP == 0;
+    return n;
+}
+constexpr int rows_w_younger(int kk, int PF, int JN, int GQ) { return (PF - 1 - kk % GQ) * JN; }
 
 template <typename F, int... I>
 __device__ __forceinline__ void rows_static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -92,13 +110,21 @@ __device__ __forceinline__ bf16x8 load_untracked(const uint16_t* p) {
 
 }  // namespace
 
-template <int RB, int KCS, int VAR>
+// RB 16-column blocks per workgroup, KRA 16-row blocks per wave and tile,
+// chunks of KCS k-steps, a W ring of PF k-steps refilled GQ at a time.  LEAN: the flat epilogue for
+// calls with one Philox key and no allow mask (a kernel of its own: beside
+// the general epilogue it would not fit in registers).
+template <int RB, int KRA, int KCS, int PF, int GQ, int VAR, bool LEAN>
 __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     static_assert(VAR == kVarFlat || VAR == kVarLogits, "variant");
+    static_assert(!LEAN || VAR == kVarFlat, "lean epilogue: flat only");
+    static_assert(KRA >= 1 && KRA <= 4 && KCS % PF == 0 && (GQ & (GQ - 1)) == 0 && PF % GQ == 0 &&
+                      PF >= 2 * GQ,
+                  "shape");
     using Geo = RowsGeom<RB, KCS>;
     constexpr int NT = Geo::kNT;
     constexpr int HL = Geo::kHL;
-    constexpr int PF = KCS;   // W ring depth: one chunk of k-steps
+    constexpr int kRMT = kRWaves * KRA * 16;   // rows per tile
     __shared__ RowsSmem<RB, KCS> sm;
 
     // row range w and column group y (see resident_kernel for the XCD pairing)
@@ -122,6 +148,11 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     const int row_end = min(part_begin(w + 1, a.nmb, a.G) * kMBlock, a.V);
     const int nks = a.d / 32;
     const int nch = nks / KCS;                                   // chunks per tile
+    // Each row range walks d from its own starting chunk (and wraps): rows of
+    // W lie d elements apart, a power of two at the usual sizes, so ranges
+    // that all read the same offset at once would load a few HBM channels
+    // and leave the rest idle.  The sum over d does not depend on the order.
+    const int rot = w % nch;
     const int ntiles = (row_end - row0 + kRMT - 1) / kRMT;       // >= 1 (G <= nmb)
     const int nsteps = ntiles * nks;
 
@@ -149,19 +180,19 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     const int hk = (hr / NT) * 32 + (((lane & 3) ^ ((hcol >> 2) & 3)) << 3);
     // A chunk's H goes through registers in HP parts of HLP loads: part p is
     // loaded at k-step p KP of the previous chunk and written to LDS KP
-    // k-steps later (RB = 16 takes two parts: a whole chunk in registers
-    // would not fit beside its accumulators and the W ring).
-    constexpr int HP = RB == 16 ? 2 : 1;
+    // k-steps later (two parts where a whole chunk in registers would not
+    // fit beside the accumulators and the W ring).
+    constexpr int HP = RB * KRA >= 32 ? 2 : 1;
     constexpr int HLP = HL / HP;
     constexpr int KP = KCS / HP;
-    static_assert(HL % HP == 0 && KCS % HP == 0, "H parts");
+    static_assert(HL % HP == 0 && KCS % HP == 0 && (KCS / HP) % GQ == 0, "H parts");
     bf16x8 hreg[HLP];
     auto load_h = [&](int cg, int part) __attribute__((always_inline)) {   // chunk cg % nch of its tile
         // (the addresses are formed here, per part, from an opaque column:
         // hoisted out of the loop they would take 2 HL registers)
         int c0 = bbase + hcol;
         asm volatile("" : "+v"(c0));
-        const int k = hk + (cg % nch) * KCS * 32;
+        const int k = hk + ((cg + rot) % nch) * KCS * 32;
 #pragma unroll
         for (int ii = 0; ii < HLP; ++ii) {
             const int i = part * HLP + ii;
@@ -177,17 +208,20 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     };
     // W fragments of global k-step g (tile g / nks): rows past the range re-read
     // its last row (their results are discarded)
-    const int trow0 = rows_tile_row(wave, 0, r16);
-    const int trow1 = rows_tile_row(wave, 1, r16);
     int ld_tile = 0, ld_ks = 0;   // the k-step the next W load is for (advanced by one per load)
-    bf16x8 wr[PF][kRA];
-    auto load_w = [&](bf16x8 (&dst)[kRA]) __attribute__((always_inline)) {
+    bf16x8 wr[PF][KRA];
+    // (jn: blocks loaded, KRA, or 1 in a short last tile whose other blocks
+    // hold no rows: a load whose result is never read must not be issued,
+    // the compiler would reuse its registers while it is in flight)
+    auto load_w = [&](bf16x8 (&dst)[KRA], auto jn) __attribute__((always_inline)) {
         const int base = row0 + ld_tile * kRMT;
-        const int rA = min(base + trow0, row_end - 1);
-        const int rB = min(base + trow1, row_end - 1);
-        const int k = ld_ks * 32 + kg * 8;
-        dst[0] = load_untracked(a.W + (size_t)rA * a.d + k);
-        dst[1] = load_untracked(a.W + (size_t)rB * a.d + k);
+        const int ks = ld_ks + rot * KCS;
+        const int k = (ks < nks ? ks : ks - nks) * 32 + kg * 8;
+#pragma unroll
+        for (int j = 0; j < decltype(jn)::value; ++j) {
+            const int r = min(base + rows_tile_row(wave, j, r16), row_end - 1);
+            dst[j] = load_untracked(a.W + (size_t)r * a.d + k);
+        }
         if (ld_tile * nks + ld_ks + 1 < nsteps) {   // clamp at the last k-step
             if (++ld_ks == nks) {
                 ld_ks = 0;
@@ -196,9 +230,9 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
         }
     };
 
-    f32x4 acc[kRA][RB];
+    f32x4 acc[KRA][RB];
 #pragma unroll
-    for (int j = 0; j < kRA; ++j)
+    for (int j = 0; j < KRA; ++j)
 #pragma unroll
         for (int n = 0; n < RB; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -211,12 +245,20 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
         store_h(sm.hs0, part);
     }
 #pragma unroll
-    for (int p = 0; p < PF; ++p) load_w(wr[p]);
+    for (int p = 0; p < PF; ++p) load_w(wr[p], std::integral_constant<int, KRA>{});
 
     const int nchunks = ntiles * nch;   // even: the host requires nch even
     // one chunk: read from stage `st`, the next chunk goes to `other`
-    // (the chunk that ends a tile is always the second of a pair: nch is even)
-    auto chunk = [&](int cg, const char* st, char* other, auto second) __attribute__((always_inline)) {
+    // (the chunk that ends a tile is always the second of a pair: nch is
+    // even).  A tile with at most 128 rows left in the range (`half`) has
+    // rows in block j = 0 only (rows_tile_row): the other blocks' loads,
+    // MFMAs and noise are skipped.  Such a tile comes last and runs in a loop
+    // of its own, entered with no load in flight, where every k-step issues
+    // one W load per wave: the waits count JN loads per k-step.
+    auto chunk = [&](int cg, const char* st, char* other, auto second, auto half)
+                     __attribute__((always_inline)) {
+        constexpr int JN = decltype(half)::value ? 1 : KRA;   // blocks with rows
+        const auto jn = std::integral_constant<int, JN>{};
         // every wave's part of chunk cg is in `st` (written at the end of the
         // previous chunk), and every wave is past its reads of `other`
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
@@ -227,17 +269,17 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
             constexpr int kk = decltype(kc)::value;
             if constexpr (kk % KP == 0) {
                 if constexpr (kk > 0) {
-                    // H part kk / KP - 1 has landed once only the KP kRA W
+                    // H part kk / KP - 1 has landed once only the KP JN W
                     // refills since are younger
-                    rows_wait_vmcnt<KP * kRA>();
+                    rows_wait_vmcnt<KP * JN>();
                     __builtin_amdgcn_sched_barrier(0);
                     store_h(other, kk / KP - 1);
                 }
                 load_h(cnext, kk / KP);
             }
             // W k-step cg KCS + kk has landed once only the ring's other
-            // (PF - 1) kRA loads and the H parts loaded so far are younger
-            rows_wait_vmcnt<(PF - 1) * kRA + (kk / KP + 1) * HLP>();
+            // (PF - 1) JN loads and the H parts issued since are younger
+            rows_wait_vmcnt<rows_w_younger(kk, PF, JN, GQ) + rows_h_issues(kk, PF, KP, GQ) * HLP>();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = 0; n < RB; ++n) {
@@ -245,9 +287,9 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                 const bf16x8 bf = *reinterpret_cast<const bf16x8*>(
                     st + (kk * NT + col) * 64 + ((kg ^ ((col >> 2) & 3)) << 4));
 #pragma unroll
-                for (int j = 0; j < kRA; ++j)
-                    acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[kk][j], bf, acc[j][n], 0,
-                                                                        0, 0);
+                for (int j = 0; j < JN; ++j)
+                    acc[j][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[kk % PF][j], bf,
+                                                                        acc[j][n], 0, 0, 0);
             }
             // issue order: each fragment's read two fragments ahead of its
             // MFMAs (the compiler would read all RB fragments first, 4 RB
@@ -255,14 +297,18 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
             for (int n = 0; n < RB - 2; ++n) {
-                __builtin_amdgcn_sched_group_barrier(0x008, kRA, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, JN, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRA, 0);
-            load_w(wr[kk]);   // the k-step PF ahead
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * JN, 0);
+            if constexpr (kk % GQ == GQ - 1) {   // k-steps kk + PF - GQ + 1 .. kk + PF
+                rows_static_for<GQ>([&](auto qc) __attribute__((always_inline)) {
+                    load_w(wr[(kk - GQ + 1 + decltype(qc)::value) % PF], jn);
+                });
+            }
         });
         // the last H part of chunk cg + 1 into `other`
-        rows_wait_vmcnt<KP * kRA>();
+        rows_wait_vmcnt<KP * JN>();
         __builtin_amdgcn_sched_barrier(0);
         store_h(other, HP - 1);
 
@@ -282,7 +328,7 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                     const ColCtx cx = col_ctx_load(sm.cols, a, bbase, n * 16 + r16 + fresh);
                     uint64_t best = pack_key(-INFINITY, -1);
                     Lse unused = lse_empty();
-                    rows_static_for<kRA>([&](auto jc) {
+                    rows_static_for<JN>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
                         const int rowg = tbase + rows_tile_row(wave, j, 4 * kg);   // 4 consecutive rows
                         const bool ok = rowg < row_end;
@@ -317,6 +363,11 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
             // and rows at or past `lim` never take.  Temperature and noise as
             // in lane_scores; greedy columns take no noise.
             auto fold_lean = [&]() __attribute__((always_inline)) {
+                // the key and step, opaque per tile: the twenty round keys are
+                // then formed on the scalar unit here instead of being kept
+                // through the loop
+                uint32_t k0 = ukey0, k1 = ukey1, st = ustep;
+                asm volatile("" : "+s"(k0), "+s"(k1), "+s"(st));
                 rows_static_for<RB>([&](auto nc) {
                     constexpr int n = decltype(nc)::value;
                     const int c = n * 16 + r16 + fresh;
@@ -324,16 +375,16 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                     const bool noisy = (sm.cols.flags[c] & 3u) == 1u;   // inside B, not greedy
                     float bs = -INFINITY;
                     int bi = -1;
-                    rows_static_for<kRA>([&](auto jc) {
+                    rows_static_for<JN>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
                         const int rowg = tbase + rows_tile_row(wave, j, 4 * kg);
                         const int gid0 = a.v_offset + rowg;
                         float g[4] = {0.f, 0.f, 0.f, 0.f};
                         if (noisy) {
                             const uint4 rw = philox4x32_10(
-                                make_uint4((uint32_t)gid0 >> 2, (uint32_t)(bbase + c), ustep,
+                                make_uint4((uint32_t)gid0 >> 2, (uint32_t)(bbase + c), st,
                                            kStreamToken),
-                                ukey0, ukey1);
+                                k0, k1);
                             g[0] = gumbel_from_word(rw.x);
                             g[1] = gumbel_from_word(rw.y);
                             g[2] = gumbel_from_word(rw.z);
@@ -354,6 +405,9 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                         uint64_t& slot = sm.key[wave][n * 16 + lane];
                         slot = key_max(slot, best);
                     }
+                    // one column block at a time: interleaved, their noise
+                    // chains would not fit beside the accumulators
+                    __builtin_amdgcn_sched_barrier(0);
                 });
             };
             if constexpr (VAR == kVarLogits) {
@@ -361,20 +415,33 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                 // the loop's counted waits assume loads only: stores may
                 // complete out of order with them, so none stays in flight
                 rows_wait_vmcnt<0>();
-            } else if (a.allow != nullptr || a.noise.seeds != nullptr) {
-                fold_tile(std::true_type{});   // the general epilogue (tests allow only if given)
-            } else {
+            } else if constexpr (LEAN) {
                 fold_lean();
+            } else {
+                fold_tile(std::true_type{});   // the general epilogue (tests allow only if given)
             }
 #pragma unroll
-            for (int j = 0; j < kRA; ++j)
+            for (int j = 0; j < JN; ++j)
 #pragma unroll
                 for (int n = 0; n < RB; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
-    for (int cg = 0; cg < nchunks; cg += 2) {
-        chunk(cg, sm.hs0, sm.hs1, std::false_type{});
-        chunk(cg + 1, sm.hs1, sm.hs0, std::true_type{});
+    // only a range's last tile can be short: the full tiles first, then a
+    // half tile in a loop of its own
+    const bool tail_half = KRA > 1 && row_end - (row0 + (ntiles - 1) * kRMT) <= 128;
+    const int nfull = (tail_half ? ntiles - 1 : ntiles) * nch;
+    int cg = 0;
+    for (; cg < nfull; cg += 2) {
+        chunk(cg, sm.hs0, sm.hs1, std::false_type{}, std::false_type{});
+        chunk(cg + 1, sm.hs1, sm.hs0, std::true_type{}, std::false_type{});
+    }
+    // nothing stays in flight from one loop into the other: the compiler
+    // may place the ring in other registers there
+    rows_wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    for (; cg < nchunks; cg += 2) {
+        chunk(cg, sm.hs0, sm.hs1, std::false_type{}, std::true_type{});
+        chunk(cg + 1, sm.hs1, sm.hs0, std::true_type{}, std::true_type{});
     }
     // the trailing loads (refills past the end) land before the wave goes on
     rows_wait_vmcnt<0>();
@@ -391,18 +458,25 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     }
 }
 
-template <int RB, int KCS, int VAR>
+template <int RB, const RowsShape& S, int VAR>
 static hipError_t launch_rows_shape(const Stage1Args& a, int grid_y, hipStream_t stream) {
+    static_assert(S.nt == 16 * RB, "shape");
     const dim3 grid = a.xcd_pair ? dim3(a.G * grid_y) : dim3(a.G, grid_y);
-    hipLaunchKernelGGL((rows_kernel<RB, KCS, VAR>), grid, dim3(64 * kRWaves), 0, stream, a);
+    const dim3 block(64 * kRWaves);
+    if (VAR == kVarFlat && a.allow == nullptr && a.noise.seeds == nullptr)
+        hipLaunchKernelGGL((rows_kernel<RB, S.kra, S.kcs, S.pf, S.gq, VAR, VAR == kVarFlat>), grid,
+                           block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((rows_kernel<RB, S.kra, S.kcs, S.pf, S.gq, VAR, false>), grid, block, 0,
+                           stream, a);
     return hipGetLastError();
 }
 
 template <int VAR>
 static hipError_t launch_rows_var(const Stage1Args& a, int nt, int grid_y, hipStream_t stream) {
-    if (nt == 64) return launch_rows_shape<4, kRowsKcs64, VAR>(a, grid_y, stream);
-    if (nt == 128) return launch_rows_shape<8, kRowsKcs128, VAR>(a, grid_y, stream);
-    if (nt == 256) return launch_rows_shape<16, kRowsKcs256, VAR>(a, grid_y, stream);
+    if (nt == kRows64.nt) return launch_rows_shape<4, kRows64, VAR>(a, grid_y, stream);
+    if (nt == kRows128.nt) return launch_rows_shape<8, kRows128, VAR>(a, grid_y, stream);
+    if (nt == kRows256.nt) return launch_rows_shape<16, kRows256, VAR>(a, grid_y, stream);
     return hipErrorInvalidValue;
 }
 

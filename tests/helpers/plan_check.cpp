@@ -212,8 +212,9 @@ int main() {
     // parity cases meant for the row-streaming kernel
     check_case(33, 512, 3001, 16, 64, 256, "rows_b33");
     check_case(40, 4096, 3000, 0, 128, 256, "rows_b40");
-    check_case(100, 256, 3001, 0, 64, 256, "rows_b100");
+    check_case(100, 512, 3001, 0, 64, 256, "rows_b100");
     check_case(128, 512, 70000, 32, 2048, 256, "rows_b128");
+    check_case(100, 512, 102400, 0, 4096, 256, "rows_b100_tail144");
     check_case(150, 256, 2000, 0, 128, 256, "rows_b150");
     check_case(256, 256, 70000, 0, 4096, 256, "rows_b256");
     check_case(300, 256, 5000, 0, 64, 256, "rows_b300");

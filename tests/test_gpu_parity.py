@@ -179,14 +179,15 @@ CASES = [
     (24, 5120, 2000, 128, 3, 16, "mixed", True),
     # fewer than four vocab blocks: the workgroup-cooperative kernel
     (5, 64, 40, 16, 3, 0, "one", False),
-    # B > 32 flat and logits with d % 512 == 0 (up to 64 columns) or d % 256
-    # == 0 (above): the row-streaming kernel at 64, 128 and 256 columns per
-    # workgroup; ragged ranges, ranges of two 256-row tiles, and two
-    # column groups paired on one XCD
+    # B > 32 flat and logits with d % 512 == 0 (64 or 128 columns per
+    # workgroup) or d % 256 == 0 (256): the row-streaming kernel; ragged
+    # ranges, short last tiles (at most 128 rows skip block 1, more run
+    # whole), and two column groups paired on one XCD
     (33, 512, 3001, 64, 7, 16, "mixed", True),
     (40, 4096, 3000, 128, 5, 0, "mixed", True),
-    (100, 256, 3001, 64, 5, 0, "mixed", True),
+    (100, 512, 3001, 64, 5, 0, "mixed", True),
     (128, 512, 70000, 2048, 0, 32, "range", False),
+    (100, 512, 102400, 4096, 0, 0, "range", False),   # ranges of 400 rows
     (150, 256, 2000, 128, 5, 0, "mixed", True),
     (256, 256, 70000, 4096, 3, 0, "mixed", True),
     (300, 256, 5000, 64, 0, 0, "range", False),

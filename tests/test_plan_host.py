@@ -54,7 +54,8 @@ def test_plans_and_layouts_under_sanitizers(plan_check):
     assert (h["kind"], h["G"], h["grid_y"], h["rcfg"]) == ("2", "256", "1", "2,1,4,8,16,0")
     assert int(h["dyn_k0"]) == 9496 // 256 - 2
     assert plans[("headline_b32", 1)]["dyn_k0"] == "0"        # grouped keeps its ranges
-    assert plans[("sweep_b256", 0)]["kind"] == "4" and plans[("sweep_b256", 0)]["nt"] == "256"
+    sw = plans[("sweep_b256", 0)]   # one group of 256 columns, a workgroup per CU
+    assert (sw["kind"], sw["nt"], sw["grid_y"], sw["G"]) == ("4", "256", "1", "256")
     assert plans[("sweep_b128", 0)]["nt"] == "128"
     assert plans[("mid_b64", 1)]["kind"] == "3"               # grouped B = 64 on the LDS kernel
     assert plans[("topk_b32", 3)]["rcfg"] == "2,1,2,8,18,2"   # d = 5120: H partly in LDS
@@ -68,6 +69,9 @@ def test_plans_and_layouts_under_sanitizers(plan_check):
             pl = plans[(name, var)]
             assert (pl["kind"], pl["nt"], pl["grid_y"]) == ("4", str(nt), str(gy)), (name, pl)
     assert plans[("rows_b300", 0)]["xcd"] == "1"
-    # ranges of 17 blocks: two 256-row tiles
-    for name in ("rows_b128", "rows_b256"):
-        assert 70000 // 16 // int(plans[(name, 0)]["G"]) >= 17
+    # ranges of 17 or 18 blocks (272 or 288 rows: a 256-row tile and a short
+    # one) and of 25 blocks (400 rows: the last tile of 144 rows runs whole)
+    assert plans[("rows_b128", 0)]["G"] == "256"
+    assert plans[("rows_b256", 0)]["G"] == "256"
+    pl = plans[("rows_b100_tail144", 0)]
+    assert (pl["kind"], pl["nt"], pl["G"]) == ("4", "128", "256")
