@@ -41,29 +41,39 @@ def alg_bytes(B, d=D, v=V):
 
 
 class Timer:
-    """HIP events on the current (library launch) stream: one event before the
-    first call and one after every call, so each call's duration is the time
-    between its neighbouring events (back-to-back calls: the GPU time each
-    took, gaps included)."""
+    """HIP events on the current (library launch) stream.  The mean per call
+    comes from n back-to-back calls between two events (the timed region);
+    the per-call distribution from a second pass of n calls with an event
+    after each call (an event costs the stream about 3 us, so recording one
+    per call would inflate the mean)."""
 
     def __init__(self, torch):
         self.t = torch
 
     def run(self, fn, n):
-        """Mean seconds per call, wall seconds, and the per-call seconds."""
+        """Mean seconds per call, wall seconds of the timed region, and the
+        per-call seconds of the second pass."""
         t = self.t
         s = t.cuda.current_stream()
-        ev = [t.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
         t.cuda.synchronize()
         w0 = time.perf_counter()
+        e0.record(s)
+        for i in range(n):
+            fn(i)
+        e1.record(s)
+        t.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        mean = e0.elapsed_time(e1) / 1e3 / n
+        ev = [t.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         ev[0].record(s)
         for i in range(n):
             fn(i)
             ev[i + 1].record(s)
         t.cuda.synchronize()
-        wall = time.perf_counter() - w0
         per = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(n)]
-        return ev[0].elapsed_time(ev[n]) / 1e3 / n, wall, per
+        return mean, wall, per
 
 
 def pct(per, q):

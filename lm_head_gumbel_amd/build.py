@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfs.so")
 SOURCES = ["fs_api.hip", "fs_plan.cpp", "fs_stage1.hip", "fs_stream.hip", "fs_resident.hip", "fs_wide.hip",
-           "fs_wide_dma.hip", "fs_rows.hip", "fs_stage2.hip", "fs_probe.hip"]
+           "fs_rows.hip", "fs_stage2.hip", "fs_probe.hip"]
 ARCH = "gfx950"
 
 

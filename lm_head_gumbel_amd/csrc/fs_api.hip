@@ -259,7 +259,6 @@ static fs_status flat_stage1(const fs_params* p, const void* H, const void* W, c
     a.sched = a.dyn_k0 > 0 ? w.sched : nullptr;
     const hipError_t e =
         pl.kind == kRows       ? launch_rows(kVarFlat, a, pl.nt, pl.grid_y, s)
-        : pl.kind == kWide     ? launch_wide(kVarFlat, a, pl.nt, pl.grid_y, s)
         : pl.kind == kResident ? launch_resident(kVarFlat, a, pl.grid_y, pl.rcfg, s)
         : pl.stream          ? launch_stream(kVarFlat, a, pl.grid_y, pl.cfg, w.part, need_out, s)
                              : launch_stage1(kVarFlat, a, pl.grid_y, pl.cfg, s);
@@ -394,9 +393,6 @@ fs_status fs_logits(const fs_params* p, const void* H, const void* W, float* log
     a.logits = logits;
     if (pl.kind == kRows)
         return from_hip(launch_rows(kVarLogits, a, pl.nt, pl.grid_y,
-                                    static_cast<hipStream_t>(stream)));
-    if (pl.kind == kWide)
-        return from_hip(launch_wide(kVarLogits, a, pl.nt, pl.grid_y,
                                     static_cast<hipStream_t>(stream)));
     if (pl.kind == kResident)
         return from_hip(launch_resident(kVarLogits, a, pl.grid_y, pl.rcfg,

@@ -112,14 +112,9 @@ struct TopkRows {
 hipError_t launch_resident(int variant, const Stage1Args& a, int grid_y, const ResidentConfig& c,
                            hipStream_t stream);
 
-// LDS-tiled stage 1 (fs_wide.hip): flat and logits with nt = 64 or 128;
-// grouped with nt = 64 when every workgroup range meets at most
-// kWideMaxTiles vocabulary tiles; nt = 256 goes to launch_wide_dma.
+// LDS-tiled grouped stage 1 (fs_wide.hip): nt = 64, when every workgroup
+// range meets at most kWideMaxTiles vocabulary tiles.
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream);
-// The same contraction fed by direct-to-LDS loads (fs_wide_dma.hip): flat and
-// logits, nt = 256, d % 32 == 0.
-hipError_t launch_wide_dma(int variant, const Stage1Args& a, int nt, int grid_y,
-                           hipStream_t stream);
 
 // Row-streaming stage 1 for large batches (fs_rows.hip): flat and logits,
 // nt = 64, 128 or 256 batch columns per workgroup, d % (64 rows_kcs(nt)) == 0.

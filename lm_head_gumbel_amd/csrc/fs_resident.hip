@@ -184,11 +184,13 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // units of a workgroup are w, w + G, w + 2G, ... as in the strided order,
     // every later one comes from a ticket t (unit k0 G + t), so that the
     // workgroups that run faster take more of the last units and all finish
-    // close together.  The ticket taken in group i (after the group's last
-    // load, so that no load waits for it) is read in group i + 1 and names
-    // the unit of group i + 3.  Tickets are handed out in order, so a
-    // workgroup that has one past the end takes no more; the last workgroup
-    // to finish resets the counts.
+    // close together.  The ticket taken at the start of group i (before the
+    // group's own loads: the previous group's prefetch, which the group waits
+    // for first, does not wait for it) is read at the end of group i and
+    // names the unit of group i + 2, whose rows group i + 1 prefetches: a
+    // workgroup is committed at most two units ahead when the tickets run
+    // out.  Tickets are handed out in order, so a workgroup that has one past
+    // the end takes no more; the last workgroup to finish resets the counts.
     constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits || VAR == kVarTopk;
     const int nunits = (a.nmb + MPI - 1) / MPI;   // strided: the host keeps G <= nunits
     bool dyn = false;
@@ -269,7 +271,6 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     int gi = 0;                 // group index
     int dyn_next = (w + a.G) * MPI;
     bool grabbing = dyn;        // no ticket past the end seen yet (uniform)
-    bool held = false;          // a ticket taken in the previous group (uniform)
     unsigned int ticket = 0;    // (thread 0)
     while (true) {
         // (strided: only a workgroup's last unit can be short, so the group
@@ -280,6 +281,13 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // (cache hits, never used), keeping every load unconditional
         const Group nxt = more ? group_at<MPI>(gnext, mb1, a.tile_mb) : cur;
         group_rows<MPI>(wnext, a.W, nxt, r16, a.V, a.d);
+        // the ticket for the unit of group i + 2 (top-k: only while the row
+        // store has room for it)
+        const bool take = grabbing && more && gi + 2 >= a.dyn_k0 &&
+                          (VAR != kVarTopk || (gi + 3) * MPI * kMBlock <= kTopkRows);   // uniform
+        if (take && threadIdx.x == 0)
+            ticket = (unsigned int)__hip_atomic_fetch_add(&a.sched->word, 1ull, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
 
         f32x4 acc[MPI][NB];
 #pragma unroll
@@ -313,31 +321,21 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         for (int j = 0; j < MPI; ++j)
 #pragma unroll
             for (int n = 0; n < NB; ++n) sm.red[buf][wave][j][n][lane] = acc[j][n];
-        // (top-k: only while the row store has room for the unit of group i + 3)
-        const bool take = grabbing && more && gi + 3 >= a.dyn_k0 &&
-                          (VAR != kVarTopk || (gi + 4) * MPI * kMBlock <= kTopkRows);   // uniform
-        if (threadIdx.x == 0) {
-            if (held) {   // the previous group's ticket has long returned
-                const int u = a.dyn_k0 * a.G + (int)ticket;
-                sm.next_unit[buf] = u < nunits ? u : -1;
-            }
-            if (take)
-                ticket = (unsigned int)__hip_atomic_fetch_add(&a.sched->word, 1ull,
-                                                              __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT);
+        if (take && threadIdx.x == 0) {   // this group's ticket, back by now
+            const int u = a.dyn_k0 * a.G + (int)ticket;
+            sm.next_unit[buf] = u < nunits ? u : -1;
         }
         __syncthreads();
         if (dyn) {   // the unit of group i + 2
             if (gi + 2 < a.dyn_k0) {
                 dyn_next = (w + (gi + 2) * a.G) * MPI;
-            } else if (held) {
+            } else if (take) {
                 const int u = sm.next_unit[buf];
                 if (u < 0) grabbing = false;
                 dyn_next = u >= 0 ? u * MPI : mb1;
             } else {
                 dyn_next = mb1;
             }
-            held = take;
         }
         ++gi;
 

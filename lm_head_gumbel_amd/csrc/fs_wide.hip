@@ -1,6 +1,10 @@
-// Stage 1 for large batches (gfx950): an LDS-tiled bf16 GEMM with the
+// Grouped stage 1 for 32 < B <= 64 (gfx950): an LDS-tiled bf16 GEMM with the
 // sampling epilogue fused in ("FlashSampling: Fast and Memory-Efficient Exact
-// Sampling", Abstract; FlashSampling explainer on aitrends.kr, Stage 1).
+// Sampling", Abstract; FlashSampling explainer on aitrends.kr, Stage 1 and the
+// Group-Gumbel-Max paragraph).  Flat and logits calls at these batch sizes
+// take the row-streaming kernel (fs_rows.hip); the kernel below keeps its
+// general shape (NT = 64 or 128) but only the grouped 64-column variant is
+// built.
 //
 // A workgroup (8 waves) owns a balanced range of 16-row vocabulary blocks and
 // walks it in tiles of MT rows (128 for NT = 64 batch columns, 256 for 128).
@@ -375,18 +379,7 @@ static hipError_t launch_wide_nt(const Stage1Args& a, int grid_y, hipStream_t st
 }
 
 hipError_t launch_wide(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream) {
-    if (nt == 256) return launch_wide_dma(variant, a, nt, grid_y, stream);
-    if (variant == kVarGrouped) {
-        if (nt == 64) return launch_wide_nt<64, kVarGrouped>(a, grid_y, stream);
-        return hipErrorInvalidValue;
-    }
-    if (variant == kVarFlat) {
-        if (nt == 64) return launch_wide_nt<64, kVarFlat>(a, grid_y, stream);
-        if (nt == 128) return launch_wide_nt<128, kVarFlat>(a, grid_y, stream);
-    } else if (variant == kVarLogits) {
-        if (nt == 64) return launch_wide_nt<64, kVarLogits>(a, grid_y, stream);
-        if (nt == 128) return launch_wide_nt<128, kVarLogits>(a, grid_y, stream);
-    }
+    if (variant == kVarGrouped && nt == 64) return launch_wide_nt<64, kVarGrouped>(a, grid_y, stream);
     return hipErrorInvalidValue;
 }
 

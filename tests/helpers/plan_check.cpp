@@ -98,6 +98,7 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
         }
         if (pl.kind == kWide || pl.kind == kRows)
             CHECK(pl.nt == 64 || pl.nt == 128 || pl.nt == 256, "nt %d", pl.nt);
+        if (pl.kind == kWide) CHECK(var == kVarGrouped && pl.nt == 64, "wide: grouped, 64 columns");
         if (pl.kind == kWide) {   // 32-bit element offsets (the rows kernel forms 64-bit ones)
             CHECK((int64_t)B * d < INT32_MAX, "wide H offsets B %d d %d", B, d);
             CHECK((cdiv(pl.nmb, pl.G) * kMBlock + 256) * d < INT32_MAX, "wide W offsets");
