@@ -74,6 +74,7 @@ struct Workspace {
     float* ms = nullptr;
     uint64_t* mkey = nullptr;
     void* part = nullptr;   // streaming stage 1: parked partial sums of split blocks
+    unsigned long long* gsel = nullptr;   // grouped block records: stage 2's sample pairs
     SchedState* sched = nullptr;   // flat: unit scheduler block (kept from call to call)
     void* sel = nullptr;    // top-k: lists of the intermediate selection levels
 };
@@ -91,6 +92,7 @@ Workspace carve(char* base, const WsLayout& l) {
     w.ms = static_cast<float*>(at(l.ms));
     w.mkey = static_cast<uint64_t*>(at(l.mkey));
     w.part = at(l.part);
+    w.gsel = static_cast<unsigned long long*>(at(l.gsel));
     w.sched = static_cast<SchedState*>(at(l.sched));
     return w;
 }
@@ -325,6 +327,11 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     a.pm = w.pm;
     a.pidx = w.pidx;
     a.pL = w.pL;
+    // unit records: the ticket order like flat once stage 2 has set up the
+    // scheduler block
+    a.dyn_k0 = dynamic_k0(pl);
+    a.sched = a.dyn_k0 > 0 ? w.sched : nullptr;
+    a.gsel = w.gsel;
     hipError_t e =
         pl.kind == kWide       ? launch_wide(kVarGrouped, a, pl.nt, pl.grid_y, s)
         : pl.kind == kResident ? launch_resident(kVarGrouped, a, pl.grid_y, pl.rcfg, s)
@@ -332,13 +339,15 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
                                : launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);
     if (e != hipSuccess) return FS_ERR_HIP;
     // record slot (worker w, tile t) is w + t; the streaming kernel's workers
-    // own ranges of (block, quarter) units, the cooperative kernel's of blocks
+    // own ranges of (block, quarter) units, the cooperative kernel's of blocks;
+    // with unit records the slot is the block
     const int workers = pl.stream ? 4 * pl.G : pl.G;
     const int units = pl.stream ? 4 * pl.nmb : pl.nmb;
     const int tile_units = pl.stream ? 4 * pl.tile_mb : pl.tile_mb;
     return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.P, pl.B, pl.T, workers, units,
                                           tile_units, temp, p->flags, noise_src(pl, p), tile_max,
-                                          tile_idx, tile_logmass, out_idx, s));
+                                          tile_idx, tile_logmass, out_idx, w.gsel,
+                                          a.dyn_k0 > 0 ? w.sched : nullptr, s));
 }
 
 

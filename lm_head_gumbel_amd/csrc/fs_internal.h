@@ -81,11 +81,14 @@ struct Stage1Args {
     int ny;                 // resident kernel: batch groups sharing one row range
     int xcd_pair;           // resident kernel: 1-D grid, groups of a range on one XCD
     // partial records [B][P] (P slots per row: the workers for flat, workers
-    // + T - 1 for grouped, where (worker w, tile t) is slot w + t)
+    // + T - 1 for grouped, where (worker w, tile t) is slot w + t; the
+    // resident kernel's grouped records: one per 16-row block, slot = block)
     int P;
     float* pm;
     int32_t* pidx;
     float* pL;
+    // resident grouped: stage 2's per-row [key, count] pairs, cleared here
+    unsigned long long* gsel;
     // top-k candidates [B][G][topk_len] (row-major: a row's lists are one
     // contiguous run): tempered logit and id
     float* cx;
@@ -131,12 +134,15 @@ hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B
                               int32_t* out_idx, float* out_score, SchedState* sched,
                               hipStream_t stream);
 
+// Grouped records: tile t's are the slots w + t of the G ranges of nmb units
+// that meet it, or with gsel (block records, slot = block: nmb blocks, tiles
+// of tile_mb) its blocks; gsel is the per-row [key, count] pair of the
+// sample, cleared by stage 1.  sched as for flat.
 hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
-                                 int B,
-                                 int T, int G, int nmb, int tile_mb, const float* temp,
-                                 uint32_t flags, const NoiseSrc& noise,
-                                 float* tile_max, int32_t* tile_idx, float* tile_L,
-                                 int32_t* out_idx, hipStream_t stream);
+                                 int B, int T, int G, int nmb, int tile_mb, const float* temp,
+                                 uint32_t flags, const NoiseSrc& noise, float* tile_max,
+                                 int32_t* tile_idx, float* tile_L, int32_t* out_idx,
+                                 unsigned long long* gsel, SchedState* sched, hipStream_t stream);
 
 // Candidates [B][G][L] (L entries per list); 1 <= k <= 1024.  With dn.on
 // the lists are dense: list w holds the x of every row workgroup w kept, in

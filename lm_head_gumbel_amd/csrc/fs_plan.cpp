@@ -138,6 +138,9 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     }
     pl.stream = pl.kind == kStream;
     pl.cfg = pick_config(pl.stream, p->B);
+    // grouped on the resident kernel: a record per 16-row block, so that its
+    // walk takes the strided (and ticket) order like flat
+    pl.unit_rec = variant == kVarGrouped && pl.kind == kResident;
 
     // 2. batch groups
     const int cols = (pl.kind == kWide || pl.kind == kRows) ? pl.nt
@@ -157,7 +160,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     }
     // resident flat, logits and top-k stride units of mpi blocks over the
     // workgroups: at most one workgroup per unit
-    const bool strided = pl.kind == kResident && variant != kVarGrouped;
+    const bool strided = pl.kind == kResident;   // (grouped too: block records)
     const int nunits = strided ? ceil_div(pl.nmb, pl.rcfg.mpi) : pl.nmb;
     const int max_g = nunits;
     if (pl.G > max_g) {
@@ -186,7 +189,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
             pl.xcd_pair = 1;
         }
     }
-    pl.P = workers + (variant == kVarGrouped ? pl.T - 1 : 0);
+    pl.P = pl.unit_rec ? pl.nmb : workers + (variant == kVarGrouped ? pl.T - 1 : 0);
     pl.k0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
     pl.k1 = (uint32_t)(p->seed >> 32);
 
@@ -194,8 +197,9 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     // stage-2 kernels of grouped and flat take one workgroup per batch row
     // along x, top-k's selection levels (slices, B)
     const int64_t gx = pl.xcd_pair ? (int64_t)pl.G * pl.grid_y : pl.G;
+    // (top-k and grouped block records: stage 2 takes the rows along y)
     pl.launchable = gx <= kMaxGridX && (pl.xcd_pair || pl.grid_y <= kMaxGridY) &&
-                    (variant != kVarTopk || pl.B <= kMaxGridY);
+                    ((variant != kVarTopk && !pl.unit_rec) || pl.B <= kMaxGridY);
 }
 
 size_t part_bytes(const Plan& pl) {
@@ -210,7 +214,7 @@ int dynamic_k0(const Plan& pl) {
     // ticket 11 us slower).  One batch group and at least three units per
     // workgroup.
     constexpr int kDepth = 2;
-    if (pl.variant != kVarFlat && pl.variant != kVarTopk) return 0;
+    if (pl.variant != kVarFlat && pl.variant != kVarTopk && !pl.unit_rec) return 0;
     if (pl.kind != kResident || pl.grid_y != 1 || pl.xcd_pair) return 0;
     const int nunits = ceil_div(pl.nmb, std::max(1, pl.rcfg.mpi));
     const int per = nunits / pl.G;   // units every workgroup has in the strided order
@@ -257,7 +261,8 @@ WsLayout layout(int ws_variant, const Plan& pl, int k) {
         w.pidx = take(P * B * 4);
         if (ws_variant == FS_VARIANT_GROUPED) w.pL = take(P * B * 4);
         if (pl.stream) w.part = take(part_bytes(pl));
-        if (ws_variant == FS_VARIANT_FLAT) w.sched = take(kSchedBytes);
+        if (ws_variant == FS_VARIANT_GROUPED && pl.unit_rec) w.gsel = take(B * 16);
+        w.sched = take(kSchedBytes);
     } else if (ws_variant == FS_VARIANT_TOPK) {
         const int L = topk_len(pl, k);
         const bool dense = topk_dense(pl, k);

@@ -116,6 +116,10 @@ struct Plan {
     int nt;        // kWide, kRows: batch columns per workgroup
     int grid_y;
     int xcd_pair;
+    // resident grouped: one record per 16-row block (slot = block index, the
+    // blocks of a tile merged in stage 2) instead of one per (range, tile):
+    // the walk then takes the strided and ticket order of flat
+    bool unit_rec;
     uint32_t k0, k1;
     bool launchable;   // the grids fit HIP's limits (else FS_ERR_UNSUPPORTED)
 };
@@ -134,7 +138,8 @@ struct WsLayout {
     size_t sel = kAbsent;                            // top-k selection levels
     size_t mm = kAbsent, ms = kAbsent, mkey = kAbsent;   // multinomial chunk sums
     size_t part = kAbsent;                           // streaming partial sums
-    size_t sched = kAbsent;                          // flat/top-k unit scheduler
+    size_t gsel = kAbsent;                           // grouped block records: [B][2] sample pairs
+    size_t sched = kAbsent;                          // flat/grouped/top-k unit scheduler (last)
     size_t total = 0;
 };
 

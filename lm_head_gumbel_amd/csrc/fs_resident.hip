@@ -102,20 +102,20 @@ struct TopkRowsSmem {
 };
 struct NoTopkRows {};
 
-// Grouped: the column partials of the folding waves (waves 0 .. FW - 1,
-// FW = MPI NB, one (block, N-block) pair each per group) for each vocabulary
-// tile that the workgroup's range meets, kept here until the walk ends: 32 KiB,
-// 64 tiles when FW = 2.  A record store inside the walk would hold back the
-// loads issued after it (its wait is counted with theirs): 15 us of 240 at
-// B = 32 with 128-row tiles.
-template <int FW>
-struct SegSmem {
-    static constexpr int kSlots = 32768 / (FW * 16 * 16);
-    uint64_t key[kSlots][FW][16];
-    float mx[kSlots][FW][16];
-    float sm[kSlots][FW][16];
+// Grouped: the records (winner key and log-mass per column) of the 16-row
+// blocks the workgroup has walked, kept here and written out when the store
+// is full and after the walk.  A record store inside the walk would hold back
+// the loads issued after it (its wait is counted with theirs): 15 us of 240
+// at B = 32.
+template <int NB>
+struct BlockRecSmem {
+    static constexpr int kSlots = 64;
+    uint64_t key[kSlots][16 * NB];
+    float mx[kSlots][16 * NB];
+    float sm[kSlots][16 * NB];
+    int blk[kSlots];   // block of each slot
 };
-struct NoSeg {};
+struct NoRec {};
 
 // The last HL k-steps of each wave's H slice, when the registers cannot hold
 // the whole slice: per wave [HL][NB] fragments of 64 lanes (each lane reads
@@ -147,9 +147,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         typename std::conditional<VAR == kVarTopk, TopkRowsSmem<NB, NW, HL>, NoTopkRows>::type;
     __shared__ TkSmem tk;
     static_assert(MPI * NB <= NW, "every (block, N-block) pair of a group has a wave");
-    constexpr int FW = MPI * NB;   // waves that fold
-    using SegPart = typename std::conditional<VAR == kVarGrouped, SegSmem<FW>, NoSeg>::type;
-    __shared__ SegPart seg;
+    using RecPart = typename std::conditional<VAR == kVarGrouped, BlockRecSmem<NB>, NoRec>::type;
+    __shared__ RecPart rec;
 
     // Row range w and batch group y of this workgroup.  With xcd_pair the grid
     // is 1-D and the ny groups of a range get ids L, L + 8, L + 16, ...:
@@ -169,17 +168,16 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15;
     const int kg = lane >> 4;
-    // Flat, logits and top-k walk units of MPI blocks strided by G (unit w,
-    // w + G, w + 2G, ...): at any moment the workgroups read neighbouring
-    // parts of W, which streams HBM better than one contiguous range per
-    // workgroup (6.10 against 5.78 TB/s at B = 32, d = 4096, V = 151936).  Any
-    // partition gives the same flat sample (the noise is keyed by the global
-    // id) and the same top-k set (the row store maps back to global ids).
-    // Grouped records (one per workgroup and tile) need a contiguous range
-    // [mb0, mb1).  Strided: mb0 is the first block, mb1 one past the last
-    // unit's blocks.
+    // Every variant walks units of MPI blocks strided by G (unit w, w + G,
+    // w + 2G, ...): at any moment the workgroups read neighbouring parts of W,
+    // which streams HBM better than one contiguous range per workgroup (6.10
+    // against 5.78 TB/s at B = 32, d = 4096, V = 151936).  Any partition gives
+    // the same flat sample (the noise is keyed by the global id), the same
+    // top-k set (the row store maps back to global ids) and the same grouped
+    // records (one per 16-row block, its slot the block).  mb0 is the first
+    // block, mb1 one past the last unit's blocks.
     //
-    // Flat and top-k with a scheduler block (one batch group; top-k with lists
+    // Flat, grouped and top-k with a scheduler block (one batch group; top-k with lists
     // that carry ids, its store unit table giving the ids): the first a.dyn_k0 >= 3
     // units of a workgroup are w, w + G, w + 2G, ... as in the strided order,
     // every later one comes from a ticket t (unit k0 G + t), so that the
@@ -191,10 +189,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     // workgroup is committed at most two units ahead when the tickets run
     // out.  Tickets are handed out in order, so a workgroup that has one past
     // the end takes no more; the last workgroup to finish resets the counts.
-    constexpr bool kStrided = VAR == kVarFlat || VAR == kVarLogits || VAR == kVarTopk;
     const int nunits = (a.nmb + MPI - 1) / MPI;   // strided: the host keeps G <= nunits
     bool dyn = false;
-    if constexpr (VAR == kVarFlat || VAR == kVarTopk) {
+    if constexpr (VAR == kVarFlat || VAR == kVarTopk || VAR == kVarGrouped) {
         if (a.sched != nullptr) {   // uniform
             if (threadIdx.x == 0) {
                 const unsigned long long tag =
@@ -208,20 +205,11 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         }
     }
     int mb0, mb1;
-    if constexpr (kStrided) {
+    {
         const int last = w + a.G * ((nunits - 1 - w) / a.G);
         mb0 = w * MPI;
         mb1 = dyn ? a.nmb : min(last * MPI + MPI, a.nmb);
-    } else {
-        mb0 = part_begin(w, a.nmb, a.G);
-        mb1 = part_begin(w + 1, a.nmb, a.G);
     }
-    // grouped: the range meets tiles t0 .. t0 + nseg - 1; their records are
-    // stored after the walk when LDS holds them all
-    const int t0 = mb0 / a.tile_mb;
-    const int nseg = mb1 > mb0 ? (mb1 - 1) / a.tile_mb - t0 + 1 : 0;
-    bool defer = false;
-    if constexpr (VAR == kVarGrouped) defer = nseg <= SegSmem<FW>::kSlots;
     const int bbase = y * 16 * NB;
     const int ks0 = wave * HT;
     constexpr int kTopkRows = TopkRows<NB, HL>::kRows;   // top-k: rows the store holds
@@ -259,7 +247,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     WStage<MPI, KS> sa, sb;
     const uint16_t* wrow[MPI];
     const uint16_t* wnext[MPI];
-    Group cur = group_at<MPI>(mb0, mb1, a.tile_mb);
+    // (groups never end at a tile: records are per block)
+    constexpr int kNoSeg = INT32_MAX / 2;
+    Group cur = group_at<MPI>(mb0, mb1, kNoSeg);
     group_rows<MPI>(wrow, a.W, cur, r16, a.V, a.d);
     load_w<MPI, KS>(sa, wrow, 0, ks0, kg, a.d);
 
@@ -267,19 +257,19 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     Lse lse = lse_empty();
     int buf = 0;
     int stored = 0;   // top-k: blocks in the row store (the workgroup's blocks in walk order)
+    int nrec = 0;     // grouped: block records in the store
     // ticket order: first block of the next group's unit (mb1: none)
     int gi = 0;                 // group index
     int dyn_next = (w + a.G) * MPI;
     bool grabbing = dyn;        // no ticket past the end seen yet (uniform)
     unsigned int ticket = 0;    // (thread 0)
     while (true) {
-        // (strided: only a workgroup's last unit can be short, so the group
-        // and its record segment end together there)
-        const int gnext = dyn ? dyn_next : kStrided ? cur.g + a.G * MPI : cur.g + cur.nvm;
+        // (only a workgroup's last unit can be short)
+        const int gnext = dyn ? dyn_next : cur.g + a.G * MPI;
         const bool more = gnext < mb1;
         // after the last group the prefetch re-reads this group's first stage
         // (cache hits, never used), keeping every load unconditional
-        const Group nxt = more ? group_at<MPI>(gnext, mb1, a.tile_mb) : cur;
+        const Group nxt = more ? group_at<MPI>(gnext, mb1, kNoSeg) : cur;
         group_rows<MPI>(wnext, a.W, nxt, r16, a.V, a.d);
         // the ticket for the unit of group i + 2 (top-k: only while the row
         // store has room for it)
@@ -365,7 +355,22 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             } else {
                 float x[4], s[4];
                 lane_scores(a, cc, v, row0, true, x, s);
-                fold<VAR>(best, lse, x, s, a.v_offset + row0);
+                if constexpr (VAR == kVarGrouped) {
+                    // the block's record for these 16 columns: this wave alone
+                    // holds them (no barrier), into the store's next slot
+                    uint64_t kb = pack_key(-INFINITY, -1);
+                    Lse lb = lse_empty();
+                    fold<VAR>(kb, lb, x, s, a.v_offset + row0);
+                    column_reduce<VAR>(kb, lb);
+                    if (lane < 16) {
+                        rec.key[nrec + j][n * 16 + lane] = kb;
+                        rec.mx[nrec + j][n * 16 + lane] = lb.mx;
+                        rec.sm[nrec + j][n * 16 + lane] = lb.sm;
+                    }
+                    if (n == 0 && lane == 0) rec.blk[nrec + j] = cur.g + j;
+                } else {
+                    fold<VAR>(best, lse, x, s, a.v_offset + row0);
+                }
             }
         }
         // the next group writes the other buffer; this one is rewritten two
@@ -375,42 +380,46 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             if (threadIdx.x == 0) tk.unit[stored / MPI] = cur.g / MPI;
         stored += cur.nvm;
 
-        if constexpr (VAR == kVarFlat || VAR == kVarGrouped) {
+        if constexpr (VAR == kVarFlat) {
             // flat: one record, after the workgroup's last group
-            if (VAR == kVarFlat ? !more : cur.g + cur.nvm == cur.seg_end) {   // a segment ends here
+            if (!more) {
                 column_reduce<VAR>(best, lse);
-                if constexpr (VAR == kVarGrouped) {
-                    // (each segment has slots of its own: no barrier)
-                    if (defer && lane < 16 && wave < FW) {
-                        const int sg = cur.t - t0;
-                        seg.key[sg][wave][lane] = best;
-                        seg.mx[sg][wave][lane] = lse.mx;
-                        seg.sm[sg][wave][lane] = lse.sm;
-                    }
+                if (lane < 16) {
+                    sm.fkey[wave][lane] = best;
+                    sm.fmx[wave][lane] = lse.mx;
+                    sm.fsm[wave][lane] = lse.sm;
                 }
-                if (VAR == kVarFlat || !defer) {   // uniform
-                    if (lane < 16) {
-                        sm.fkey[wave][lane] = best;
-                        sm.fmx[wave][lane] = lse.mx;
-                        sm.fsm[wave][lane] = lse.sm;
+                __syncthreads();
+                if (threadIdx.x < 16 * NB) {
+                    const int n = threadIdx.x >> 4;
+                    const ColCtx c = col_ctx(a, bbase + n * 16 + (threadIdx.x & 15));
+                    uint64_t k = pack_key(-INFINITY, -1);
+                    Lse l = lse_empty();
+                    for (int ww = n; ww < NW; ww += NB) {
+                        k = key_max(k, sm.fkey[ww][threadIdx.x & 15]);
+                        l = lse_merge(l, Lse{sm.fmx[ww][threadIdx.x & 15],
+                                             sm.fsm[ww][threadIdx.x & 15]});
                     }
-                    __syncthreads();
-                    if (threadIdx.x < 16 * NB) {
-                        const int n = threadIdx.x >> 4;
-                        const ColCtx c = col_ctx(a, bbase + n * 16 + (threadIdx.x & 15));
-                        uint64_t k = pack_key(-INFINITY, -1);
-                        Lse l = lse_empty();
-                        for (int ww = n; ww < NW; ww += NB) {
-                            k = key_max(k, sm.fkey[ww][threadIdx.x & 15]);
-                            l = lse_merge(l, Lse{sm.fmx[ww][threadIdx.x & 15],
-                                                 sm.fsm[ww][threadIdx.x & 15]});
-                        }
-                        put_record<VAR, false>(a, VAR == kVarGrouped ? w + cur.t : w, c, k, l);
-                    }
-                    __syncthreads();
+                    put_record<VAR, false>(a, w, c, k, l);
                 }
-                best = pack_key(-INFINITY, -1);
-                lse = lse_empty();
+                __syncthreads();
+            }
+        }
+        if constexpr (VAR == kVarGrouped) {
+            // the block records go out when the store is full and after the
+            // walk (every wave is past its slot writes at the first barrier)
+            nrec += cur.nvm;
+            if (!more || nrec + MPI > BlockRecSmem<NB>::kSlots) {   // uniform
+                __syncthreads();
+                for (int e = threadIdx.x; e < nrec * 16 * NB; e += 64 * NW) {
+                    const int sl = e / (16 * NB);
+                    const int c = e % (16 * NB);
+                    const ColCtx cx = col_ctx(a, bbase + c);
+                    put_record<VAR, false>(a, rec.blk[sl], cx, rec.key[sl][c],
+                                           Lse{rec.mx[sl][c], rec.sm[sl][c]});
+                }
+                __syncthreads();
+                nrec = 0;
             }
         }
 
@@ -418,6 +427,12 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         cur = nxt;
 #pragma unroll
         for (int j = 0; j < MPI; ++j) wrow[j] = wnext[j];
+    }
+    if constexpr (VAR == kVarGrouped) {
+        // stage 2's per-row [key, count] pairs start cleared (after the walk:
+        // no store is pending during it)
+        if (a.gsel && blockIdx.x == 0 && blockIdx.y == 0)
+            for (int b = threadIdx.x; b < 2 * a.B; b += blockDim.x) a.gsel[b] = 0ull;
     }
     if (dyn && threadIdx.x == 0) {
         // every ticket of this workgroup has returned (each was read back);
@@ -428,26 +443,6 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             __hip_atomic_store(&a.sched->word, (unsigned long long)kSchedTag32 << 32,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.sched->exits, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-
-    if constexpr (VAR == kVarGrouped) {
-        if (defer) {   // uniform
-            // record (column c, tile t0 + sg) of the waves' partials; the
-            // tiles of one column go to neighbouring slots
-            __syncthreads();
-            for (int e = threadIdx.x; e < nseg * 16 * NB; e += 64 * NW) {
-                const int sg = e % nseg;
-                const int c = e / nseg;
-                const ColCtx cx = col_ctx(a, bbase + c);
-                uint64_t k = pack_key(-INFINITY, -1);
-                Lse l = lse_empty();
-                for (int ww = c >> 4; ww < FW; ww += NB) {
-                    k = key_max(k, seg.key[sg][ww][c & 15]);
-                    l = lse_merge(l, Lse{seg.mx[sg][ww][c & 15], seg.sm[sg][ww][c & 15]});
-                }
-                put_record<VAR, false>(a, w + t0 + sg, cx, k, l);
-            }
         }
     }
 

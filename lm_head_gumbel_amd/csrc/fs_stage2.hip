@@ -62,53 +62,138 @@ __device__ __forceinline__ bool row_is_greedy(const float* temp, int b, uint32_t
     return !(T > 0.f);
 }
 
+// One tile of a grouped row: merges its record slots s0 .. s1 into the
+// tile's winner key k (largest score) and log-mass L (greedy rows: the
+// largest tempered logit).
+struct TileRec {
+    uint64_t k;
+    float L;
+};
+__device__ __forceinline__ TileRec grouped_merge(const float* pm, const int32_t* pidx,
+                                                 const float* pL, int P, int b, int s0, int s1,
+                                                 bool greedy) {
+    uint64_t k = pack_key(-INFINITY, -1);
+    Lse l = lse_empty();
+    // eight records at a time: their loads go out together
+    for (int s8 = s0; s8 <= s1; s8 += 8) {
+        float m8[8], L8[8];
+        int32_t i8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const size_t o = (size_t)b * P + (s8 + q);
+            const bool in = s8 + q <= s1;
+            i8[q] = in ? pidx[o] : -1;
+            m8[q] = in ? pm[o] : -INFINITY;
+            L8[q] = in ? pL[o] : -INFINITY;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (i8[q] >= 0) k = key_max(k, pack_key(m8[q], i8[q]));
+            if (greedy)
+                l.mx = fmaxf(l.mx, L8[q]);
+            else
+                l = lse_merge(l, Lse{L8[q], 1.f});
+        }
+    }
+    return TileRec{k, greedy ? l.mx : lse_value(l)};
+}
+
+__device__ __forceinline__ void store_tile(const TileRec& r, int b, int T, int t, float* tile_max,
+                                           int32_t* tile_idx, float* tile_L) {
+    const int32_t id = key_index(r.k);
+    const size_t ot = (size_t)b * T + t;
+    tile_max[ot] = id >= 0 ? key_score(r.k) : -INFINITY;
+    tile_idx[ot] = id;
+    tile_L[ot] = r.L;
+}
+
+// The tile's noisy group score as a key (the group noise is keyed by the
+// tile; -inf for an empty tile).
+__device__ __forceinline__ uint64_t group_key(const TileRec& r, int b, int t, bool greedy,
+                                              const RowKey& rk) {
+    const int32_t id = key_index(r.k);
+    const float L = r.L;
+    if (id < 0 || !(L > -INFINITY)) return pack_key(-INFINITY, -1);
+    float sc = L;
+    if (!greedy) {
+        const uint4 rw = philox4x32_10(make_uint4((uint32_t)t >> 2, (uint32_t)b, rk.step,
+                                                  kStreamGroup),
+                                       rk.k0, rk.k1);
+        const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
+        sc += gumbel_from_word(words[t & 3]);
+    }
+    // tiles hold ascending id ranges, so the lowest id also means the lowest tile
+    return pack_key(sc, id);
+}
+
+__device__ __forceinline__ void mark_scheduler(SchedState* sched) {
+    // stage 1 is done: mark the unit scheduler initialised for the next call
+    sched->word = (unsigned long long)kSchedTag32 << 32;
+    sched->exits = 0ull;
+    sched->tag = kSchedTag;
+}
+
+// Records per (range, tile): one workgroup per row, slots w + t of the G
+// ranges w of nmb units that meet tile t.
 __global__ __launch_bounds__(kGrpThreads) void stage2_grouped_kernel(
     const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int G, int nmb,
     int tile_mb, const float* temp, uint32_t flags, NoiseSrc noise, float* tile_max,
-    int32_t* tile_idx, float* tile_L, int32_t* out_idx) {
+    int32_t* tile_idx, float* tile_L, int32_t* out_idx, SchedState* sched) {
     const int b = blockIdx.x;
+    if (sched && b == 0 && threadIdx.x == 0) mark_scheduler(sched);
     const bool greedy = row_is_greedy(temp, b, flags);
     const RowKey rk = row_key(noise, b);
     uint64_t best = pack_key(-INFINITY, -1);
     for (int t = threadIdx.x; t < T; t += kGrpThreads) {
         const int first = t * tile_mb;
         const int last = min(nmb, (t + 1) * tile_mb) - 1;
-        const int wf = part_owner(first, nmb, G);
-        const int wl = part_owner(last, nmb, G);
-        uint64_t k = pack_key(-INFINITY, -1);
-        Lse l = lse_empty();
-        for (int w = wf; w <= wl; ++w) {   // partial record (w, t) lives in slot w + t
-            const size_t o = (size_t)b * P + (w + t);
-            const int32_t id = pidx[o];
-            if (id >= 0) k = key_max(k, pack_key(pm[o], id));
-            const float Lp = pL[o];
-            if (greedy)
-                l.mx = fmaxf(l.mx, Lp);
-            else
-                l = lse_merge(l, Lse{Lp, 1.f});
-        }
-        const int32_t id = key_index(k);
-        const float L = greedy ? l.mx : lse_value(l);
-        const size_t ot = (size_t)b * T + t;
-        tile_max[ot] = id >= 0 ? key_score(k) : -INFINITY;
-        tile_idx[ot] = id;
-        tile_L[ot] = L;
-        if (out_idx && id >= 0 && L > -INFINITY) {
-            float sc = L;
-            if (!greedy) {
-                const uint4 rw = philox4x32_10(
-                    make_uint4((uint32_t)t >> 2, (uint32_t)b, rk.step, kStreamGroup), rk.k0, rk.k1);
-                const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
-                sc += gumbel_from_word(words[t & 3]);
-            }
-            // tiles hold ascending id ranges, so the lowest id also means the lowest tile
-            best = key_max(best, pack_key(sc, id));
-        }
+        const TileRec r = grouped_merge(pm, pidx, pL, P, b, part_owner(first, nmb, G) + t,
+                                        part_owner(last, nmb, G) + t, greedy);
+        store_tile(r, b, T, t, tile_max, tile_idx, tile_L);
+        best = key_max(best, group_key(r, b, t, greedy, rk));
     }
     if (out_idx) {
         best = block_max_key<kGrpThreads>(best);
         if (threadIdx.x == 0) out_idx[b] = key_index(best);
     }
+}
+
+// Records per 16-row block (slot = block): a workgroup per (row, chunk of
+// kGrpBlkThreads tiles).  The chunks' group-sample keys meet in the row's
+// [key, count] pair of gsel (cleared by stage 1): an atomic maximum, and the
+// chunk that counts last writes the sample.
+constexpr int kGrpBlkThreads = 256;
+__global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
+    const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int nmb,
+    int tile_mb, const float* temp, uint32_t flags, NoiseSrc noise, float* tile_max,
+    int32_t* tile_idx, float* tile_L, int32_t* out_idx, unsigned long long* gsel,
+    SchedState* sched) {
+    const int b = blockIdx.y;
+    if (sched && b == 0 && blockIdx.x == 0 && threadIdx.x == 0) mark_scheduler(sched);
+    const bool greedy = row_is_greedy(temp, b, flags);
+    const RowKey rk = row_key(noise, b);
+    const int t = blockIdx.x * kGrpBlkThreads + threadIdx.x;
+    TileRec r{pack_key(-INFINITY, -1), -INFINITY};
+    if (t < T) r = grouped_merge(pm, pidx, pL, P, b, t * tile_mb, min(nmb, (t + 1) * tile_mb) - 1,
+                                 greedy);
+    // the sample first, the tile outputs after: the release of the count then
+    // has no tile store of this workgroup to wait for
+    if (out_idx) {   // uniform
+        uint64_t best = t < T ? group_key(r, b, t, greedy, rk) : pack_key(-INFINITY, -1);
+        best = block_max_key<kGrpBlkThreads>(best);
+        if (threadIdx.x == 0) {
+            __hip_atomic_fetch_max(&gsel[2 * b], (unsigned long long)best, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned long long n = __hip_atomic_fetch_add(
+                &gsel[2 * b + 1], 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            if (n == gridDim.x - 1) {   // every chunk of the row is in
+                const unsigned long long k =
+                    __hip_atomic_load(&gsel[2 * b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                out_idx[b] = key_index(k);
+            }
+        }
+    }
+    if (t < T) store_tile(r, b, T, t, tile_max, tile_idx, tile_L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1044,10 +1129,18 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                                  int B, int T, int G, int nmb, int tile_mb, const float* temp,
                                  uint32_t flags, const NoiseSrc& noise, float* tile_max,
                                  int32_t* tile_idx, float* tile_L, int32_t* out_idx,
-                                 hipStream_t stream) {
-    hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kGrpThreads), 0, stream, pm, pidx,
-                       pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,
-                       tile_L, out_idx);
+                                 unsigned long long* gsel, SchedState* sched, hipStream_t stream) {
+    if (gsel) {
+        const int chunks = (T + kGrpBlkThreads - 1) / kGrpBlkThreads;
+        if (chunks > kMaxGridX || B > kMaxGridY) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(stage2_grouped_blocks_kernel, dim3(chunks, B), dim3(kGrpBlkThreads), 0,
+                           stream, pm, pidx, pL, P, B, T, nmb, tile_mb, temp, flags, noise,
+                           tile_max, tile_idx, tile_L, out_idx, gsel, sched);
+    } else {
+        hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kGrpThreads), 0, stream, pm, pidx,
+                           pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,
+                           tile_L, out_idx, sched);
+    }
     return hipGetLastError();
 }
 

@@ -105,15 +105,17 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
             CHECK(var != kVarGrouped || pl.nt == 64, "wide grouped nt");
         }
         if (pl.kind == kStream) CHECK(pl.G <= std::max(1, pl.nmb / 4), "stream G");
-        const bool strided = pl.kind == kResident && var != kVarGrouped;
+        CHECK(pl.unit_rec == (var == kVarGrouped && pl.kind == kResident), "block records");
+        const bool strided = pl.kind == kResident && (var != kVarGrouped || pl.unit_rec);
         const int64_t nunits = strided ? cdiv(pl.nmb, pl.rcfg.mpi) : pl.nmb;
         CHECK(pl.G <= nunits, "G %d > units %lld", pl.G, (long long)nunits);
         if (pl.xcd_pair) CHECK(pl.G % 8 == 0 && pl.grid_y > 1, "xcd pairing");
         const int workers = pl.kind == kStream ? 4 * pl.G : pl.G;
-        CHECK(pl.P == workers + (var == kVarGrouped ? pl.T - 1 : 0), "P %d", pl.P);
+        CHECK(pl.P == (pl.unit_rec ? pl.nmb : workers + (var == kVarGrouped ? pl.T - 1 : 0)),
+              "P %d", pl.P);
         const int dk = dynamic_k0(pl);
         if (dk > 0) {
-            CHECK(var == kVarFlat || var == kVarTopk, "tickets");
+            CHECK(var == kVarFlat || var == kVarTopk || pl.unit_rec, "tickets");
             CHECK(dk >= 3 && (int64_t)dk * pl.G <= nunits, "dyn_k0 %d G %d units %lld", dk, pl.G,
                   (long long)nunits);
         }
@@ -123,10 +125,13 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
             const WsLayout l = layout(wv, pl, 0);
             CHECK(l.pm != kAbsent && l.pidx != kAbsent, "records");
             CHECK((var == kVarGrouped) == (l.pL != kAbsent), "log-mass records");
-            CHECK((var == kVarFlat) == (l.sched != kAbsent), "scheduler block");
+            CHECK(l.sched != kAbsent, "scheduler block");
             CHECK(pl.stream == (l.part != kAbsent), "partial sums");
+            CHECK((var == kVarGrouped && pl.unit_rec) == (l.gsel != kAbsent), "sample pairs");
+            CHECK(l.sched + kSchedBytes == l.total, "scheduler block last");
             check_layout(l, {{l.pm, P * b * 4}, {l.pidx, P * b * 4}, {l.pL, P * b * 4},
-                             {l.part, pl.stream ? part_bytes(pl) : 0}, {l.sched, kSchedBytes}},
+                             {l.part, pl.stream ? part_bytes(pl) : 0}, {l.gsel, b * 16},
+                             {l.sched, kSchedBytes}},
                          "records");
             // the multinomial baseline plans with the flat variant
             if (var == kVarFlat) {
@@ -166,9 +171,10 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
         }
         if (name) {
             std::printf("plan %s var=%d kind=%d G=%d grid_y=%d P=%d nt=%d xcd=%d rcfg=%d,%d,%d,%d,%d,%d "
-                        "dyn_k0=%d\n",
+                        "dyn_k0=%d unit_rec=%d\n",
                         name, var, pl.kind, pl.G, pl.grid_y, pl.P, pl.nt, pl.xcd_pair, pl.rcfg.nb,
-                        pl.rcfg.mpi, pl.rcfg.ks, pl.rcfg.nw, pl.rcfg.hk, pl.rcfg.hl, dk);
+                        pl.rcfg.mpi, pl.rcfg.ks, pl.rcfg.nw, pl.rcfg.hk, pl.rcfg.hl, dk,
+                        pl.unit_rec ? 1 : 0);
         }
     }
 }

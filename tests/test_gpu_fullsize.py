@@ -118,6 +118,60 @@ def test_headline_call_on_a_reused_workspace():
             check_flat(gi, gs.astype(np.float64), x, s, rows, what=f"headline step {step}")
 
 
+def test_headline_grouped_on_a_reused_workspace():
+    """Grouped records at the benchmark's shape (B=32, d=4096, V=151936,
+    tiles of 128 ids): a record per 16-row unit, taken in the strided order
+    and, from the second call on a workspace, the last units by ticket.  Every
+    call's tile records and sample equal, bit for bit, those of the same call
+    on a zeroed workspace, and agree with the oracle."""
+    t = torch()
+    B = 32
+    Hb = hidden_bf16(B, D_HEAD)
+    Wb = weights(V_HEAD, D_HEAD)
+    x_in = Inputs(Hb, Wb)
+    rows = np.arange(B)
+    p = x_in.params(seed=PHILOX_SEED)
+    n = fs.fs_workspace_bytes(p, fs.FS_VARIANT_GROUPED)
+    T = fs.fs_num_tiles(p)
+    ws = t.zeros(n, dtype=t.uint8, device="cuda")
+
+    def call(wsx):
+        m = t.empty((B, T), dtype=t.float32, device="cuda")
+        ti = t.empty((B, T), dtype=t.int32, device="cuda")
+        L = t.empty((B, T), dtype=t.float32, device="cuda")
+        out = t.empty(B, dtype=t.int32, device="cuda")
+        fs.check(fs.fs_sample_grouped(p, x_in.H, x_in.W, None, None, m, ti, L, out, wsx),
+                 "fs_sample_grouped")
+        t.cuda.synchronize()
+        return [host(m), host(ti), host(L), host(out)]
+
+    for step in range(3):
+        p.step = step
+        tagged = sched_tagged(ws)
+        assert tagged == (step > 0), f"step {step}: scheduler block tagged {tagged}"
+        log(f"grouped headline step {step}: {'ticket' if tagged else 'strided'} order")
+        got = call(ws)
+        want = call(t.zeros(n, dtype=t.uint8, device="cuda"))
+        for g, w in zip(got, want):
+            assert np.array_equal(g.view(np.uint32), w.view(np.uint32))
+        assert sched_tagged(ws)
+        if step in (0, 2):
+            m, ti, L, go = (got[0].astype(np.float64), got[1].astype(np.int64),
+                            got[2].astype(np.float64), got[3].astype(np.int64))
+            _, x, s = oracle_rows(Hb, Wb, rows, None, None, PHILOX_SEED, step)
+            om, oidx, oL, ogap = O.tile_records(x, s, 128)
+            check_values(m, om, what="tile max")
+            check_values(L, oL, what="tile log-mass")
+            pinned = ogap > TOL_GAP
+            assert np.array_equal(ti[pinned], oidx[pinned])
+            assert_pinned(pinned.ravel(), "tiles")
+            gidx, ggap, gt = O.sample_grouped(oidx, oL, None, PHILOX_SEED, step)
+            pin = (ggap > TOL_GAP) & np.array([gt[b] < 0 or ogap[b, gt[b]] > TOL_GAP for b in rows])
+            assert np.array_equal(go[pin], gidx[pin])
+            assert_pinned(pin, "grouped")
+            check_grouped_unpinned(go, gidx, ti, pin)
+
+
 @pytest.mark.parametrize("B", [1, 8, 32])
 def test_small_model_flat_and_grouped(B):
     wl = WORKLOADS[f"small_b{B}"]

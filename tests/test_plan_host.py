@@ -53,7 +53,11 @@ def test_plans_and_layouts_under_sanitizers(plan_check):
     h = plans[("headline_b32", 0)]
     assert (h["kind"], h["G"], h["grid_y"], h["rcfg"]) == ("2", "256", "1", "2,1,4,8,16,0")
     assert int(h["dyn_k0"]) == 9496 // 256 - 2
-    assert plans[("headline_b32", 1)]["dyn_k0"] == "0"        # grouped keeps its ranges
+    # grouped on the resident kernel: a record per 16-row unit, strided and
+    # ticket order like flat
+    g = plans[("headline_b32", 1)]
+    assert (g["unit_rec"], g["P"], g["dyn_k0"]) == ("1", "9496", h["dyn_k0"])
+    assert plans[("mid_b64", 1)]["unit_rec"] == "0"            # the LDS-tiled kernel's ranges
     sw = plans[("sweep_b256", 0)]   # one group of 256 columns, a workgroup per CU
     assert (sw["kind"], sw["nt"], sw["grid_y"], sw["G"]) == ("4", "256", "1", "256")
     assert plans[("sweep_b128", 0)]["nt"] == "128"
