@@ -12,6 +12,8 @@
 #include "fs_internal.h"
 #include "fs_topk.h"
 
+#include <algorithm>
+
 namespace fs {
 
 constexpr int kRedThreads = 256;
@@ -158,42 +160,192 @@ __global__ __launch_bounds__(kGrpThreads) void stage2_grouped_kernel(
     }
 }
 
-// Records per 16-row block (slot = block): a workgroup per (row, chunk of
-// kGrpBlkThreads tiles).  The chunks' group-sample keys meet in the row's
-// [key, count] pair of gsel (cleared by stage 1): an atomic maximum, and the
-// chunk that counts last writes the sample.
+// A tile's running winner key and log-sum-exp state (value mx + log sm).
+// Both merges are symmetric bit for bit, so the two lanes of a shuffle pair
+// hold the same state afterwards.
+struct TileAcc {
+    uint64_t k;
+    Lse l;
+};
+
+__device__ __forceinline__ TileAcc tile_acc_merge(TileAcc a, TileAcc b) {
+    return TileAcc{key_max(a.k, b.k), lse_merge(a.l, b.l)};
+}
+
+__device__ __forceinline__ TileAcc shfl_xor_acc(TileAcc a, int m) {
+    return TileAcc{shfl_xor_u64(a.k, m), Lse{__shfl_xor(a.l.mx, m, 64), __shfl_xor(a.l.sm, m, 64)}};
+}
+
+// One block record as a tile state (ok: the slot belongs to the tile).  A
+// greedy row's log-mass is its maximum (the state's mx), so one merge serves
+// both kinds of row.
+__device__ __forceinline__ TileAcc block_acc(bool ok, int32_t id, float m, float L) {
+    return TileAcc{ok && id >= 0 ? pack_key(m, id) : pack_key(-INFINITY, -1),
+                   ok && L > -INFINITY ? Lse{L, 1.f} : lse_empty()};
+}
+
+// Records per 16-row block (slot = block).  Tile t goes to rpt = 2^rpt_log2
+// consecutive threads (rpt: the power of two at or above tile_mb, at most
+// kGrpBlkThreads), thread j of them merging blocks t tile_mb + j len .. + len
+// - 1 (len = 1 unless a tile has more blocks than a workgroup has threads);
+// a pass covers kGrpBlkThreads / rpt tiles, so consecutive threads read
+// consecutive records.  Workgroup (c, b) takes passes c ppw .. c ppw + ppw - 1
+// of row b and loads the records of up to kGrpBlkBatch of them together; each
+// pass's runs then meet in an xor tree (shuffles inside a wave, the tile's
+// waves in order through LDS), the same merge order on every call.
+// Afterwards every thread of a tile's group holds the tile, and the passes
+// are dealt out so that a thread finishes (log-mass, outputs, group noise) at
+// most ceil(kGrpBlkBatch / rpt) tiles.  The row's sample is the largest
+// group key over its tiles (Group-Gumbel-Max): with several workgroups per
+// row their keys meet in the row's [key, count] pair of gsel (cleared by
+// stage 1), an atomic maximum, and the workgroup that counts last writes it.
 constexpr int kGrpBlkThreads = 256;
+constexpr int kGrpBlkBatch = 8;
+
+template <bool ONE>   // len == 1
 __global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
     const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int nmb,
-    int tile_mb, const float* temp, uint32_t flags, NoiseSrc noise, float* tile_max,
-    int32_t* tile_idx, float* tile_L, int32_t* out_idx, unsigned long long* gsel,
-    SchedState* sched) {
+    int tile_mb, int rpt_log2, int ppw, const float* temp, uint32_t flags, NoiseSrc noise,
+    float* tile_max, int32_t* tile_idx, float* tile_L, int32_t* out_idx,
+    unsigned long long* gsel, SchedState* sched) {
+    __shared__ uint64_t wk[kGrpBlkBatch][kGrpBlkThreads / 64];
+    __shared__ Lse wl[kGrpBlkBatch][kGrpBlkThreads / 64];
     const int b = blockIdx.y;
     if (sched && b == 0 && blockIdx.x == 0 && threadIdx.x == 0) mark_scheduler(sched);
     const bool greedy = row_is_greedy(temp, b, flags);
     const RowKey rk = row_key(noise, b);
-    const int t = blockIdx.x * kGrpBlkThreads + threadIdx.x;
-    TileRec r{pack_key(-INFINITY, -1), -INFINITY};
-    if (t < T) r = grouped_merge(pm, pidx, pL, P, b, t * tile_mb, min(nmb, (t + 1) * tile_mb) - 1,
-                                 greedy);
-    // the sample first, the tile outputs after: the release of the count then
-    // has no tile store of this workgroup to wait for
-    if (out_idx) {   // uniform
-        uint64_t best = t < T ? group_key(r, b, t, greedy, rk) : pack_key(-INFINITY, -1);
-        best = block_max_key<kGrpBlkThreads>(best);
-        if (threadIdx.x == 0) {
-            __hip_atomic_fetch_max(&gsel[2 * b], (unsigned long long)best, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            const unsigned long long n = __hip_atomic_fetch_add(
-                &gsel[2 * b + 1], 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            if (n == gridDim.x - 1) {   // every chunk of the row is in
-                const unsigned long long k =
-                    __hip_atomic_load(&gsel[2 * b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-                out_idx[b] = key_index(k);
+    const int rpt = 1 << rpt_log2;
+    const int run = threadIdx.x & (rpt - 1);
+    const int grp = threadIdx.x >> rpt_log2;
+    const int len = (tile_mb + rpt - 1) >> rpt_log2;   // blocks per run
+    const int tpp = kGrpBlkThreads >> rpt_log2;        // tiles per pass
+    const int npass = min((T + tpp - 1) / tpp, ((int)blockIdx.x + 1) * ppw);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const size_t rb = (size_t)b * P;
+    uint64_t best = pack_key(-INFINITY, -1);
+    for (int p0 = blockIdx.x * ppw; p0 < npass; p0 += kGrpBlkBatch) {   // uniform
+        TileAcc r[kGrpBlkBatch];
+        if constexpr (ONE) {
+            // one record per pass, loaded unconditionally at a clamped slot:
+            // every load of the batch goes out before the first is used
+            int32_t id[kGrpBlkBatch];
+            float m[kGrpBlkBatch], L[kGrpBlkBatch];
+            bool ok[kGrpBlkBatch];
+#pragma unroll
+            for (int q = 0; q < kGrpBlkBatch; ++q) {
+                const int t = (p0 + q) * tpp + grp;
+                const int s = t * tile_mb + run;
+                ok[q] = p0 + q < npass && t < T && run < tile_mb && s < nmb;
+                const size_t o = rb + (size_t)min(s, nmb - 1);
+                id[q] = pidx[o];
+                m[q] = pm[o];
+                L[q] = pL[o];
+            }
+#pragma unroll
+            for (int q = 0; q < kGrpBlkBatch; ++q) r[q] = block_acc(ok[q], id[q], m[q], L[q]);
+        } else {
+            // runs of len blocks, eight records at a time
+#pragma unroll
+            for (int q = 0; q < kGrpBlkBatch; ++q) {
+                const int t = (p0 + q) * tpp + grp;
+                const int s0 = t * tile_mb + run * len;
+                const int s1 = p0 + q < npass && t < T ? min(min(s0 + len, (t + 1) * tile_mb), nmb)
+                                                       : s0;   // end
+                TileAcc a = block_acc(false, -1, 0.f, 0.f);
+                for (int s8 = s0; s8 < s1; s8 += 8) {
+                    int32_t id[8];
+                    float m[8], L[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const size_t o = rb + (size_t)min(s8 + j, s1 - 1);
+                        id[j] = pidx[o];
+                        m[j] = pm[o];
+                        L[j] = pL[o];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        a = tile_acc_merge(a, block_acc(s8 + j < s1, id[j], m[j], L[j]));
+                }
+                r[q] = a;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kGrpBlkBatch; ++q)
+            for (int mm = 1; mm < rpt && mm < 64; mm <<= 1)
+                r[q] = tile_acc_merge(r[q], shfl_xor_acc(r[q], mm));
+        if (rpt > 64) {   // uniform: a tile spans rpt / 64 waves
+            __syncthreads();   // the previous batch is done with wk, wl
+            if (lane == 0) {
+#pragma unroll
+                for (int q = 0; q < kGrpBlkBatch; ++q) {
+                    wk[q][wave] = r[q].k;
+                    wl[q][wave] = r[q].l;
+                }
+            }
+            __syncthreads();
+            const int w0 = wave & ~((rpt >> 6) - 1);
+#pragma unroll
+            for (int q = 0; q < kGrpBlkBatch; ++q) {
+                r[q] = TileAcc{wk[q][w0], wl[q][w0]};
+                for (int ww = w0 + 1; ww < w0 + (rpt >> 6); ++ww)
+                    r[q] = tile_acc_merge(r[q], TileAcc{wk[q][ww], wl[q][ww]});
+            }
+        }
+        // thread `run` of a group finishes passes q = run, run + rpt, ...
+        for (int q0 = 0; q0 < kGrpBlkBatch; q0 += rpt) {   // uniform
+            const int qs = q0 + run;
+            // a = r[qs], as selects on the bits (an opaque mask per pass keeps
+            // the compiler from turning the chain into an indexed array in
+            // scratch memory)
+            uint64_t ak = 0ull;
+            uint32_t amx = 0u, asm_ = 0u;
+#pragma unroll
+            for (int q = 0; q < kGrpBlkBatch; ++q) {
+                uint32_t mk = qs == q ? ~0u : 0u;
+                asm volatile("" : "+v"(mk));
+                const uint64_t mk64 = ((uint64_t)mk << 32) | mk;
+                ak |= r[q].k & mk64;
+                amx |= __float_as_uint(r[q].l.mx) & mk;
+                asm_ |= __float_as_uint(r[q].l.sm) & mk;
+            }
+            const TileAcc a{ak, Lse{__uint_as_float(amx), __uint_as_float(asm_)}};
+            const int t = (p0 + qs) * tpp + grp;
+            if (qs < kGrpBlkBatch && p0 + qs < npass && t < T) {
+                const TileRec tr{a.k, greedy ? a.l.mx : lse_value(a.l)};
+                store_tile(tr, b, T, t, tile_max, tile_idx, tile_L);
+                best = key_max(best, group_key(tr, b, t, greedy, rk));
             }
         }
     }
-    if (t < T) store_tile(r, b, T, t, tile_max, tile_idx, tile_L);
+    if (out_idx) {   // uniform
+        best = block_max_key<kGrpBlkThreads>(best);
+        if (threadIdx.x == 0) {
+            if (gridDim.x == 1) {
+                out_idx[b] = key_index(best);
+            } else {
+                // Relaxed device-scope atomics, each waited for before the
+                // next is issued: this workgroup's maximum has been performed
+                // before its count, so the workgroup that counts last finds
+                // every maximum in.  (Release and acquire at device scope
+                // would write back and invalidate the whole L2 of the XCD.)
+                unsigned long long old = __hip_atomic_fetch_max(
+                    &gsel[2 * b], (unsigned long long)best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                asm volatile("" : "+v"(old));   // the maximum has returned
+                const unsigned long long n = __hip_atomic_fetch_add(
+                    &gsel[2 * b + 1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (n == gridDim.x - 1) {   // every workgroup of the row is in
+                    // read back as an atomic where the others were performed
+                    // (an opaque operand keeps it from becoming a plain load)
+                    unsigned long long zero = 0ull;
+                    asm volatile("" : "+v"(zero));
+                    const unsigned long long k = __hip_atomic_fetch_max(
+                        &gsel[2 * b], zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    out_idx[b] = key_index(key_max(k, old));
+                }
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1131,11 +1283,28 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
                                  int32_t* tile_idx, float* tile_L, int32_t* out_idx,
                                  unsigned long long* gsel, SchedState* sched, hipStream_t stream) {
     if (gsel) {
-        const int chunks = (T + kGrpBlkThreads - 1) / kGrpBlkThreads;
+        // rpt: the power of two at or above tile_mb, at most kGrpBlkThreads
+        int lg = 0;
+        while ((1 << lg) < tile_mb && (2 << lg) <= kGrpBlkThreads) ++lg;
+        const int tpp = kGrpBlkThreads >> lg;
+        const int passes = (T + tpp - 1) / tpp;
+        // workgroups per row: at least two per compute unit over all rows,
+        // at most one batch of passes each
+        const int want = std::max(1, std::min(passes, (2 * 256 + B - 1) / B));
+        int ppw = std::max((passes + want - 1) / want, 1);
+        ppw = std::min(ppw, kGrpBlkBatch);
+        const int chunks = (passes + ppw - 1) / ppw;
         if (chunks > kMaxGridX || B > kMaxGridY) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(stage2_grouped_blocks_kernel, dim3(chunks, B), dim3(kGrpBlkThreads), 0,
-                           stream, pm, pidx, pL, P, B, T, nmb, tile_mb, temp, flags, noise,
-                           tile_max, tile_idx, tile_L, out_idx, gsel, sched);
+        if ((1 << lg) >= tile_mb)
+            hipLaunchKernelGGL(stage2_grouped_blocks_kernel<true>, dim3(chunks, B),
+                               dim3(kGrpBlkThreads), 0, stream, pm, pidx, pL, P, B, T, nmb, tile_mb,
+                               lg, ppw, temp, flags, noise, tile_max, tile_idx, tile_L, out_idx,
+                               gsel, sched);
+        else
+            hipLaunchKernelGGL(stage2_grouped_blocks_kernel<false>, dim3(chunks, B),
+                               dim3(kGrpBlkThreads), 0, stream, pm, pidx, pL, P, B, T, nmb, tile_mb,
+                               lg, ppw, temp, flags, noise, tile_max, tile_idx, tile_L, out_idx,
+                               gsel, sched);
     } else {
         hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kGrpThreads), 0, stream, pm, pidx,
                            pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,

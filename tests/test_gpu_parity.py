@@ -198,12 +198,17 @@ CASES = [
     # 16-row vocabulary tiles (eight per range)
     (48, 256, 80000, 64, 7, 16, "mixed", True),
     (64, 128, 30000, 16, 0, 0, "range", False),
-    # resident grouped: ranges meeting eleven and twenty 16-row tiles (their
-    # records wait in LDS until the walk ends), and 69 (more than LDS keeps:
-    # each is stored when its tile ends)
+    # resident grouped (a record per 16-row block): 16-row tiles, with more
+    # blocks per workgroup than its LDS store holds at once (stored in parts)
     (4, 1024, 45000, 16, 0, 0, "mixed", False),
     (3, 1024, 80000, 16, 9, 0, "range", True),
     (2, 512, 280000, 16, 5, 0, "mixed", False),
+    # resident grouped, few large tiles: stage 2 splits a tile into runs of
+    # blocks merged in a tree inside one wave (20 tiles, 32 runs each), across
+    # two waves (5 tiles, 128 runs) and across all sixteen (one tile)
+    (5, 2048, 20000, 1024, 3, 0, "mixed", True),
+    (6, 1024, 40000, 8192, 5, 16, "range", False),
+    (3, 512, 30000, 40000, 0, 0, "mixed", True),
 ]
 
 
