@@ -434,8 +434,21 @@ def hbm_probe(torch, fs, W):
         fs.check(fs.fs_debug_copy(b, a, n, 1024), "copy")
     t_copy = timer.run(lambda i: fs.check(fs.fs_debug_copy(b, a, n, 1024)), 10)[0]
     del a, b
+    # L2 -> compute unit rate: every workgroup reads the same 2 MiB (the H of
+    # B = 256, d = 4096; it fits one XCD's L2) four times
+    l2b, reps = 2 << 20, 4
+    l2 = {}
+    for grid in (256, 512):
+        sink2 = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        for i in range(3):
+            fs.check(fs.fs_debug_shared_read_probe(W, l2b, reps, sink2, grid), "L2 probe")
+        t_l2 = timer.run(lambda i: fs.check(
+            fs.fs_debug_shared_read_probe(W, l2b, reps, sink2, grid)), 20)[0]
+        l2[f"grid{grid}_GBps"] = grid * reps * l2b / t_l2 / 1e9
     return {"read_GBps": nbytes / t_read / 1e9, "copy_GBps": 2 * n / t_copy / 1e9,
-            "read_grid": 256, "copy_grid": 1024, "copy_bytes": n}
+            "read_grid": 256, "copy_grid": 1024, "copy_bytes": n,
+            "l2_shared_read": dict(l2, bytes=l2b, reps=reps,
+                                   per_cu_bytes_per_clk_at_2_4GHz=max(l2.values()) * 1e9 / 256 / 2.4e9)}
 
 
 # The sources the headline stage-1 kernel (resident_kernel) and its launch

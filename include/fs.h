@@ -272,6 +272,16 @@ fs_status fs_debug_noise(uint64_t seed, uint32_t step, uint32_t stream_id, int32
 fs_status fs_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
                               void* stream);
 
+/* fs_debug_shared_read_probe -- every one of `grid` workgroups of 256
+ * threads reads all `bytes` (a positive multiple of 32768) at `src` (16-byte
+ * aligned) `reps` (>= 1) times with 16-byte loads, each workgroup starting at
+ * its own offset, folding the data into sink (device uint32 [grid * 256]).
+ * With a buffer that fits one XCD's L2 cache this measures the rate at which
+ * the compute units take data from L2 (grid * reps * bytes bytes in all): the
+ * ceiling of a stage 1 that re-reads its H tiles from L2. */
+fs_status fs_debug_shared_read_probe(const void* src, size_t bytes, int32_t reps, uint32_t* sink,
+                                     int32_t grid, void* stream);
+
 /* fs_debug_copy -- plain device copy of `bytes` (a multiple of 16; both
  * pointers 16-byte aligned, no overlap) from `grid` workgroups of 256 threads:
  * a kernel of known traffic for calibrating hardware byte counters. */

@@ -462,6 +462,17 @@ fs_status fs_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, int
     return from_hip(launch_read_probe(src, bytes, sink, grid, static_cast<hipStream_t>(stream)));
 }
 
+fs_status fs_debug_shared_read_probe(const void* src, size_t bytes, int32_t reps, uint32_t* sink,
+                                     int32_t grid, void* stream) {
+    if (!src || !sink || grid < 1 || reps < 1 || bytes == 0 || bytes % 32768 != 0)
+        return FS_ERR_INVALID_ARG;
+    if (!aligned16(src)) return FS_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    return from_hip(launch_shared_read_probe(src, bytes, reps, sink, grid,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 fs_status fs_debug_copy(void* dst, const void* src, size_t bytes, int32_t grid, void* stream) {
     if (!src || !dst || grid < 1 || bytes % 16 != 0) return FS_ERR_INVALID_ARG;
     if (!aligned16(src) || !aligned16(dst)) return FS_ERR_UNSUPPORTED;

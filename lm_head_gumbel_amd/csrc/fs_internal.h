@@ -194,5 +194,8 @@ hipError_t launch_debug_noise(uint32_t k0, uint32_t k1, uint32_t step, uint32_t 
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
                              hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t stream);
+// bytes a multiple of 32 KiB
+hipError_t launch_shared_read_probe(const void* src, size_t bytes, int reps, uint32_t* sink,
+                                   int grid, hipStream_t stream);
 
 }  // namespace fs

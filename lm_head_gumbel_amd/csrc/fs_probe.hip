@@ -31,6 +31,30 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* src, size_
     sink[tid] = acc;
 }
 
+// Every workgroup reads all n16 words `reps` times, each starting at its own
+// offset (n16 a multiple of 256 UNROLL): with a buffer that fits one XCD's
+// L2 this is the rate at which the compute units take data from L2.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void shared_read_kernel(const u32x4* src, size_t n16, int reps,
+                                                          uint32_t* sink) {
+    constexpr size_t kStep = 256 * UNROLL;
+    const size_t start = ((size_t)blockIdx.x * kStep) % n16;
+    uint32_t acc = 0;
+    for (int r = 0; r < reps; ++r) {
+        for (size_t i = 0; i < n16; i += kStep) {
+            size_t base = i + start;
+            base = base >= n16 ? base - n16 : base;
+            u32x4 v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                v[u] = *(const global_u32x4*)(src + base + u * 256 + threadIdx.x);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
+    }
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* dst, const u32x4* src, size_t n16) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
@@ -41,6 +65,13 @@ hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int 
                              hipStream_t stream) {
     hipLaunchKernelGGL(read_probe_kernel<8>, dim3(grid), dim3(256), 0, stream,
                        static_cast<const u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_read_probe(const void* src, size_t bytes, int reps, uint32_t* sink,
+                                   int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(shared_read_kernel<8>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, reps, sink);
     return hipGetLastError();
 }
 

@@ -81,6 +81,9 @@ def test_null_and_negative_arguments_are_rejected():
     assert fs.fs_logits(p, 16, 16, None, 16, 1 << 20) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_multinomial(p, None, None, None, 0x1000) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_debug_noise(0, 0, 0, 0, 1, -1, 4, 0x1000) == fs.FS_ERR_INVALID_ARG
+    # the shared-read probe wants whole 32 KiB steps and at least one pass
+    assert fs.fs_debug_shared_read_probe(0x1000, 1000, 1, 0x1000, 8) == fs.FS_ERR_INVALID_ARG
+    assert fs.fs_debug_shared_read_probe(0x1000, 32768, 0, 0x1000, 8) == fs.FS_ERR_INVALID_ARG
 
 
 def test_unsupported_requests_are_reported():
