@@ -271,6 +271,22 @@ def bench_workloads(torch, fs, steps, W_head):
             fs.check(fs.fs_sample_stage1(p, H, W, temp, None, ws), name)
 
         line(name, wl, "flat stage 1 alone (fs_sample_stage1)", timed(flat_stage1))
+
+        # the unfused baseline at this shape: logits written to HBM, then the
+        # two-pass inverse-CDF draw
+        logits = torch.empty((wl.B, wl.V), dtype=torch.float32, device="cuda")
+        lws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_LOGITS), dtype=torch.uint8,
+                          device="cuda")
+        mws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_MULTINOMIAL), dtype=torch.uint8,
+                          device="cuda")
+
+        def unfused(i):
+            p.step = i
+            fs.check(fs.fs_logits(p, H, W, logits, lws), name)
+            fs.check(fs.fs_multinomial(p, logits, temp, None, idx, mws), name)
+
+        line(name, wl, "unfused fs_logits + fs_multinomial", timed(unfused))
+        del logits, lws, mws
         if name == "mid_b64":
             T = fs.fs_num_tiles(p)
             tm = torch.empty((wl.B, T), dtype=torch.float32, device="cuda")

@@ -12,11 +12,12 @@ Workloads (synthetic stand-ins for the pages' Qwen3-class decode LM heads):
                 1000 decode steps (step = Philox counter word 2) for the
                 histogram test
   mid-size      d=4096, V=151936, B in {1, 4, 16, 64}, T=1, last 285 ids
-                masked, grouped records and hierarchical resample
+                masked, grouped records and hierarchical resample; 1000
+                steps of the grouped sample for its histogram test
   compute-lean  d=4096, V=128256, B in {128, 256}, T_b ~ U[0.3, 1.5]; and
                 B in {128, 256} at the headline vocabulary V=151936
   top-k/online  d=5120, V=152064, B=32, top-40 (and top-1000), online merge
-                over 8 chunks of 19008 ids
+                over 8 chunks of 19008 ids (and its histogram over 1000 steps)
   vocab shards  the headline call split into G in {2, 4, 8} shards of W with
                 v_offset = g V / G, as a G-way tensor-parallel rank runs it
 """
@@ -246,6 +247,68 @@ def test_mid_size_masked_grouped(B):
     assert np.array_equal(go[pin], gidx[pin])
     assert_pinned(pin, "grouped")
     check_grouped_unpinned(go, gidx, ti, pin)
+
+
+def test_mid_size_grouped_histogram_1000_steps():
+    """1000 steps of the hierarchical (Group-Gumbel-Max) sample at the
+    mid-size shape, 4 rows, last 285 ids masked: the draws follow softmax(x)
+    over the valid ids (the correctness paragraph's chi-square, p > 0.01)."""
+    wl = WORKLOADS["mid_b4"]
+    Hb = hidden_bf16(wl.B, wl.d)
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()
+    x_in = Inputs(Hb, Wb, temp)
+    t = torch()
+    p = x_in.params(n_valid=wl.n_valid, tile_v=wl.tile_v, seed=PHILOX_SEED)
+    T = fs.fs_num_tiles(p)
+    m = t.empty((wl.B, T), dtype=t.float32, device="cuda")
+    ti = t.empty((wl.B, T), dtype=t.int32, device="cuda")
+    L = t.empty((wl.B, T), dtype=t.float32, device="cuda")
+    idx = t.empty((1000, wl.B), dtype=t.int32, device="cuda")
+    ws = t.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_GROUPED), dtype=t.uint8, device="cuda")
+    for step in range(1000):
+        p.step = step
+        fs.check(fs.fs_sample_grouped(p, x_in.H, x_in.W, x_in.temp, None, m, ti, L, idx[step],
+                                      ws))
+    draws = host(idx)
+    assert np.all((draws >= 0) & (draws < wl.n_valid))
+    x = O.tempered(O.logits_bf16(Hb, Wb), temp, wl.n_valid)
+    pv = chi_square_rows_p([draws[:, b] for b in range(wl.B)], [softmax(x[b]) for b in range(wl.B)])
+    log(f"grouped: pooled chi-square over {wl.B} rows x 1000 steps: p = {pv:.3f}")
+    assert pv > 0.01
+
+
+def test_online_merge_histogram_1000_steps():
+    """1000 steps of the online binary merge over 8 sequential chunks at the
+    top-k shape (d=5120, V=152064, per-row temperatures): chunk records from
+    the grouped entry point, then fs_merge_online; the draws of 8 rows follow
+    softmax(x)."""
+    wl = WORKLOADS["topk_b32"]
+    B = 8
+    Hb = hidden_bf16(wl.B, wl.d)[:B]
+    Wb = weights(wl.V, wl.d)
+    temp = wl.temps()[:B]
+    x_in = Inputs(Hb, Wb, temp)
+    t = torch()
+    chunk = wl.V // wl.chunks
+    p = x_in.params(tile_v=chunk, seed=PHILOX_SEED)
+    C = fs.fs_num_tiles(p)
+    assert C == wl.chunks
+    m = t.empty((B, C), dtype=t.float32, device="cuda")
+    ti = t.empty((B, C), dtype=t.int32, device="cuda")
+    L = t.empty((B, C), dtype=t.float32, device="cuda")
+    A = t.empty(B, dtype=t.float32, device="cuda")
+    idx = t.empty((1000, B), dtype=t.int32, device="cuda")
+    ws = t.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_GROUPED), dtype=t.uint8, device="cuda")
+    for step in range(1000):
+        p.step = step
+        fs.check(fs.fs_sample_grouped(p, x_in.H, x_in.W, x_in.temp, None, m, ti, L, None, ws))
+        fs.check(fs.fs_merge_online(B, C, ti, L, x_in.temp, PHILOX_SEED, step, 0, idx[step], A))
+    draws = host(idx)
+    x = O.tempered(O.logits_bf16(Hb, Wb), temp, None)
+    pv = chi_square_rows_p([draws[:, b] for b in range(B)], [softmax(x[b]) for b in range(B)])
+    log(f"online merge: pooled chi-square over {B} rows x 1000 steps: p = {pv:.3f}")
+    assert pv > 0.01
 
 
 def _sampled_rows(B):
