@@ -123,6 +123,7 @@ Stage1Args stage1_args(const Plan& pl, const fs_params* p, const void* H, const 
     a.ny = pl.grid_y;
     a.xcd_pair = pl.xcd_pair;
     a.P = pl.P;
+    a.rec_cols = 0;
     a.noise = noise_src(pl, p);
     a.flags = p->flags;
     return a;
@@ -327,6 +328,7 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     a.pm = w.pm;
     a.pidx = w.pidx;
     a.pL = w.pL;
+    a.rec_cols = pl.rec_cols;
     // unit records: the ticket order like flat once stage 2 has set up the
     // scheduler block
     a.dyn_k0 = dynamic_k0(pl);
@@ -344,7 +346,7 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     const int workers = pl.stream ? 4 * pl.G : pl.G;
     const int units = pl.stream ? 4 * pl.nmb : pl.nmb;
     const int tile_units = pl.stream ? 4 * pl.tile_mb : pl.tile_mb;
-    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.P, pl.B, pl.T, workers, units,
+    return from_hip(launch_stage2_grouped(w.pm, w.pidx, w.pL, pl.P, pl.rec_cols, pl.B, pl.T, workers, units,
                                           tile_units, temp, p->flags, noise_src(pl, p), tile_max,
                                           tile_idx, tile_logmass, out_idx, w.gsel,
                                           a.dyn_k0 > 0 ? w.sched : nullptr, s));

@@ -157,7 +157,7 @@ template <int VAR, bool MERGE>
 __device__ __forceinline__ void put_record(const Stage1Args& a, int p, const ColCtx& c,
                                            uint64_t best, Lse lse) {
     if (!c.ok) return;
-    const size_t o = (size_t)c.col * a.P + p;
+    const size_t o = a.rec_cols ? (size_t)p * a.rec_cols + c.col : (size_t)c.col * a.P + p;
     float L = c.greedy ? lse.mx : lse_value(lse);
     if constexpr (MERGE) {
         const int32_t old_id = a.pidx[o];

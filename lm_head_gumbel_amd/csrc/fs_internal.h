@@ -84,6 +84,11 @@ struct Stage1Args {
     // + T - 1 for grouped, where (worker w, tile t) is slot w + t; the
     // resident kernel's grouped records: one per 16-row block, slot = block)
     int P;
+    // 0: records row-major [B][P]; else block-major [P][rec_cols] (the
+    // resident kernel's block records: rec_cols = B rounded up to 32, so the
+    // records of a block's 32 columns fill whole 128-byte lines written by
+    // one workgroup)
+    int rec_cols;
     float* pm;
     int32_t* pidx;
     float* pL;
@@ -135,11 +140,12 @@ hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B
                               hipStream_t stream);
 
 // Grouped records: tile t's are the slots w + t of the G ranges of nmb units
-// that meet it, or with gsel (block records, slot = block: nmb blocks, tiles
-// of tile_mb) its blocks; gsel is the per-row [key, count] pair of the
-// sample, cleared by stage 1.  sched as for flat.
+// that meet it (records [B][P]), or with gsel (block records, block-major
+// [nmb][rec_cols], slot = block: nmb blocks, tiles of tile_mb) its blocks;
+// gsel is the per-row [key, count] pair of the sample, cleared by stage 1.
+// sched as for flat.
 hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
-                                 int B, int T, int G, int nmb, int tile_mb, const float* temp,
+                                 int rec_cols, int B, int T, int G, int nmb, int tile_mb, const float* temp,
                                  uint32_t flags, const NoiseSrc& noise, float* tile_max,
                                  int32_t* tile_idx, float* tile_L, int32_t* out_idx,
                                  unsigned long long* gsel, SchedState* sched, hipStream_t stream);

@@ -141,6 +141,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     // grouped on the resident kernel: a record per 16-row block, so that its
     // walk takes the strided (and ticket) order like flat
     pl.unit_rec = variant == kVarGrouped && pl.kind == kResident;
+    pl.rec_cols = pl.unit_rec ? (pl.B + 31) / 32 * 32 : 0;
 
     // 2. batch groups
     const int cols = (pl.kind == kWide || pl.kind == kRows) ? pl.nt
@@ -257,9 +258,11 @@ WsLayout layout(int ws_variant, const Plan& pl, int k) {
     const size_t B = (size_t)pl.B;
     if (ws_variant == FS_VARIANT_FLAT || ws_variant == FS_VARIANT_GROUPED) {
         const size_t P = (size_t)pl.P;
-        w.pm = take(P * B * 4);
-        w.pidx = take(P * B * 4);
-        if (ws_variant == FS_VARIANT_GROUPED) w.pL = take(P * B * 4);
+        // block records: block-major with rec_cols columns per block
+        const size_t cols = ws_variant == FS_VARIANT_GROUPED && pl.rec_cols ? pl.rec_cols : B;
+        w.pm = take(P * cols * 4);
+        w.pidx = take(P * cols * 4);
+        if (ws_variant == FS_VARIANT_GROUPED) w.pL = take(P * cols * 4);
         if (pl.stream) w.part = take(part_bytes(pl));
         if (ws_variant == FS_VARIANT_GROUPED && pl.unit_rec) w.gsel = take(B * 16);
         w.sched = take(kSchedBytes);

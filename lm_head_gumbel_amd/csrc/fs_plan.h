@@ -118,8 +118,10 @@ struct Plan {
     int xcd_pair;
     // resident grouped: one record per 16-row block (slot = block index, the
     // blocks of a tile merged in stage 2) instead of one per (range, tile):
-    // the walk then takes the strided and ticket order of flat
+    // the walk then takes the strided and ticket order of flat; the records
+    // are block-major, rec_cols (B rounded up to 32) per block
     bool unit_rec;
+    int rec_cols;   // 0: records [B][P]
     uint32_t k0, k1;
     bool launchable;   // the grids fit HIP's limits (else FS_ERR_UNSUPPORTED)
 };

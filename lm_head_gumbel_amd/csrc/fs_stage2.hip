@@ -184,7 +184,88 @@ __device__ __forceinline__ TileAcc block_acc(bool ok, int32_t id, float m, float
                    ok && L > -INFINITY ? Lse{L, 1.f} : lse_empty()};
 }
 
-// Records per 16-row block (slot = block).  Tile t goes to rpt = 2^rpt_log2
+// Block records, block-major (record of row b and block s at s C + b), tiles
+// of at most kGrpColBlocks blocks: a thread per (row, tile).  Lanes 0..31 of
+// a wave take 32 consecutive rows of one tile and lanes 32..63 the next tile,
+// so every record load of a wave reads two whole 128-byte lines, and a
+// thread's blocks (at most kGrpColBlocks) are loaded at once and merged in
+// block order.  Workgroup (x, y) takes rows 32 y .. 32 y + 31 and tiles
+// x tpw .. x tpw + tpw - 1 (eight per round).  The row's sample meets over
+// the workgroup's tiles (lanes, then waves through LDS) and then over the
+// workgroups of the row in the row's [key, count] pair of gsel, as below.
+constexpr int kGrpColBlocks = 8;
+
+__global__ __launch_bounds__(256) void stage2_grouped_cols_kernel(
+    const float* pm, const int32_t* pidx, const float* pL, int C, int B, int T, int nmb,
+    int tile_mb, int tpw, const float* temp, uint32_t flags, NoiseSrc noise, float* tile_max,
+    int32_t* tile_idx, float* tile_L, int32_t* out_idx, unsigned long long* gsel,
+    SchedState* sched) {
+    __shared__ uint64_t wbest[4][32];
+    if (sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) mark_scheduler(sched);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int b = blockIdx.y * 32 + (lane & 31);   // < C
+    const bool col_ok = b < B;
+    const int bq = col_ok ? b : 0;
+    const bool greedy = row_is_greedy(temp, bq, flags);
+    const RowKey rk = row_key(noise, bq);
+    const int tslot = wave * 2 + (lane >> 5);   // 0..7
+    const int tend = min(T, ((int)blockIdx.x + 1) * tpw);
+    uint64_t best = pack_key(-INFINITY, -1);
+    for (int t0 = blockIdx.x * tpw; t0 < tend; t0 += 8) {   // uniform
+        const int t = t0 + tslot;
+        const bool ok = col_ok && t < tend;
+        int32_t id[kGrpColBlocks];
+        float m[kGrpColBlocks], L[kGrpColBlocks];
+#pragma unroll
+        for (int j = 0; j < kGrpColBlocks; ++j) {
+            const int s = min(min(t, T - 1) * tile_mb + min(j, tile_mb - 1), nmb - 1);
+            const size_t o = (size_t)s * C + b;
+            id[j] = pidx[o];
+            m[j] = pm[o];
+            L[j] = pL[o];
+        }
+        TileAcc a = block_acc(false, -1, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < kGrpColBlocks; ++j)
+            a = tile_acc_merge(a, block_acc(ok && j < tile_mb && t * tile_mb + j < nmb, id[j], m[j],
+                                            L[j]));
+        if (ok) {
+            const TileRec tr{a.k, greedy ? a.l.mx : lse_value(a.l)};
+            store_tile(tr, b, T, t, tile_max, tile_idx, tile_L);
+            best = key_max(best, group_key(tr, b, t, greedy, rk));
+        }
+    }
+    if (!out_idx) return;   // uniform
+    best = key_max(best, shfl_xor_u64(best, 32));
+    if (lane < 32) wbest[wave][lane] = best;
+    __syncthreads();
+    if (wave == 0 && lane < 32 && col_ok) {
+        best = key_max(key_max(wbest[0][lane], wbest[1][lane]), key_max(wbest[2][lane], wbest[3][lane]));
+        if (gridDim.x == 1) {
+            out_idx[b] = key_index(best);
+        } else {
+            // relaxed device-scope atomics, each waited for before the next
+            // (see stage2_grouped_blocks_kernel)
+            unsigned long long old = __hip_atomic_fetch_max(
+                &gsel[2 * b], (unsigned long long)best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" : "+v"(old));
+            const unsigned long long n = __hip_atomic_fetch_add(
+                &gsel[2 * b + 1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (n == gridDim.x - 1) {
+                unsigned long long zero = 0ull;
+                asm volatile("" : "+v"(zero));
+                const unsigned long long k = __hip_atomic_fetch_max(
+                    &gsel[2 * b], zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                out_idx[b] = key_index(key_max(k, old));
+            }
+        }
+    }
+}
+
+// Records per 16-row block (slot = block), block-major: the record of
+// (row b, block s) at s C + b.  Tiles of more than kGrpColBlocks blocks.
+// Tile t goes to rpt = 2^rpt_log2
 // consecutive threads (rpt: the power of two at or above tile_mb, at most
 // kGrpBlkThreads), thread j of them merging blocks t tile_mb + j len .. + len
 // - 1 (len = 1 unless a tile has more blocks than a workgroup has threads);
@@ -205,7 +286,7 @@ constexpr int kGrpBlkBatch = 8;
 template <bool ONE>   // len == 1
 __global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
     const float* pm, const int32_t* pidx, const float* pL, int P, int B, int T, int nmb,
-    int tile_mb, int rpt_log2, int ppw, const float* temp, uint32_t flags, NoiseSrc noise,
+    int tile_mb, int rpt_log2, int ppw, int C, const float* temp, uint32_t flags, NoiseSrc noise,
     float* tile_max, int32_t* tile_idx, float* tile_L, int32_t* out_idx,
     unsigned long long* gsel, SchedState* sched) {
     __shared__ uint64_t wk[kGrpBlkBatch][kGrpBlkThreads / 64];
@@ -222,7 +303,6 @@ __global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
     const int npass = min((T + tpp - 1) / tpp, ((int)blockIdx.x + 1) * ppw);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const size_t rb = (size_t)b * P;
     uint64_t best = pack_key(-INFINITY, -1);
     for (int p0 = blockIdx.x * ppw; p0 < npass; p0 += kGrpBlkBatch) {   // uniform
         TileAcc r[kGrpBlkBatch];
@@ -237,7 +317,7 @@ __global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
                 const int t = (p0 + q) * tpp + grp;
                 const int s = t * tile_mb + run;
                 ok[q] = p0 + q < npass && t < T && run < tile_mb && s < nmb;
-                const size_t o = rb + (size_t)min(s, nmb - 1);
+                const size_t o = (size_t)min(s, nmb - 1) * C + b;
                 id[q] = pidx[o];
                 m[q] = pm[o];
                 L[q] = pL[o];
@@ -258,7 +338,7 @@ __global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
                     float m[8], L[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const size_t o = rb + (size_t)min(s8 + j, s1 - 1);
+                        const size_t o = (size_t)min(s8 + j, s1 - 1) * C + b;
                         id[j] = pidx[o];
                         m[j] = pm[o];
                         L[j] = pL[o];
@@ -1278,11 +1358,23 @@ hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B
 }
 
 hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
-                                 int B, int T, int G, int nmb, int tile_mb, const float* temp,
+                                 int rec_cols, int B, int T, int G, int nmb, int tile_mb, const float* temp,
                                  uint32_t flags, const NoiseSrc& noise, float* tile_max,
                                  int32_t* tile_idx, float* tile_L, int32_t* out_idx,
                                  unsigned long long* gsel, SchedState* sched, hipStream_t stream) {
-    if (gsel) {
+    if (gsel && tile_mb <= kGrpColBlocks) {
+        // a thread per (row, tile): about two workgroups per compute unit
+        const int cgroups = rec_cols / 32;
+        const int rounds = (T + 7) / 8;
+        const int want = std::max(1, std::min(rounds, (2 * 256 + cgroups - 1) / cgroups));
+        const int tpw = 8 * ((rounds + want - 1) / want);
+        const int chunks = (T + tpw - 1) / tpw;
+        if (chunks > kMaxGridX || cgroups > kMaxGridY || rec_cols % 32 != 0 || rec_cols < B)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(stage2_grouped_cols_kernel, dim3(chunks, cgroups), dim3(256), 0, stream,
+                           pm, pidx, pL, rec_cols, B, T, nmb, tile_mb, tpw, temp, flags, noise,
+                           tile_max, tile_idx, tile_L, out_idx, gsel, sched);
+    } else if (gsel) {
         // rpt: the power of two at or above tile_mb, at most kGrpBlkThreads
         int lg = 0;
         while ((1 << lg) < tile_mb && (2 << lg) <= kGrpBlkThreads) ++lg;
@@ -1298,13 +1390,13 @@ hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const flo
         if ((1 << lg) >= tile_mb)
             hipLaunchKernelGGL(stage2_grouped_blocks_kernel<true>, dim3(chunks, B),
                                dim3(kGrpBlkThreads), 0, stream, pm, pidx, pL, P, B, T, nmb, tile_mb,
-                               lg, ppw, temp, flags, noise, tile_max, tile_idx, tile_L, out_idx,
-                               gsel, sched);
+                               lg, ppw, rec_cols, temp, flags, noise, tile_max, tile_idx, tile_L,
+                               out_idx, gsel, sched);
         else
             hipLaunchKernelGGL(stage2_grouped_blocks_kernel<false>, dim3(chunks, B),
                                dim3(kGrpBlkThreads), 0, stream, pm, pidx, pL, P, B, T, nmb, tile_mb,
-                               lg, ppw, temp, flags, noise, tile_max, tile_idx, tile_L, out_idx,
-                               gsel, sched);
+                               lg, ppw, rec_cols, temp, flags, noise, tile_max, tile_idx, tile_L,
+                               out_idx, gsel, sched);
     } else {
         hipLaunchKernelGGL(stage2_grouped_kernel, dim3(B), dim3(kGrpThreads), 0, stream, pm, pidx,
                            pL, P, B, T, G, nmb, tile_mb, temp, flags, noise, tile_max, tile_idx,

@@ -129,7 +129,10 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
             CHECK(pl.stream == (l.part != kAbsent), "partial sums");
             CHECK((var == kVarGrouped && pl.unit_rec) == (l.gsel != kAbsent), "sample pairs");
             CHECK(l.sched + kSchedBytes == l.total, "scheduler block last");
-            check_layout(l, {{l.pm, P * b * 4}, {l.pidx, P * b * 4}, {l.pL, P * b * 4},
+            // block records are block-major, B rounded up to 32 columns per block
+            CHECK(pl.rec_cols == (pl.unit_rec ? (B + 31) / 32 * 32 : 0), "record columns");
+            const size_t rc = var == kVarGrouped && pl.unit_rec ? (size_t)pl.rec_cols : b;
+            check_layout(l, {{l.pm, P * rc * 4}, {l.pidx, P * rc * 4}, {l.pL, P * rc * 4},
                              {l.part, pl.stream ? part_bytes(pl) : 0}, {l.gsel, b * 16},
                              {l.sched, kSchedBytes}},
                          "records");
