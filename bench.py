@@ -143,6 +143,15 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
         res["unfused_calls_per_s"] = 1.0 / t_base
         res["fused_speedup"] = t_base / t_call
         del logits
+        # for scale: the library GEMM alone (W times H^T into bf16 logits, no
+        # sampling; a plain 2-D product of contiguous operands)
+        Ht = H.t().contiguous()
+        out = torch.empty((V, B), dtype=torch.bfloat16, device="cuda")
+        for i in range(3):
+            torch.mm(W, Ht, out=out)
+        res["library_gemm_us"] = timer.run(lambda i: torch.mm(W, Ht, out=out),
+                                           max(10, steps // 4))[0] * 1e6
+        del out, Ht
     if variants:
         # the same call replayed from a HIP graph: the step lives on the device
         # and the graph advances it, so every replay draws fresh noise
