@@ -115,12 +115,16 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         else if (pl.nmb >= 4)
             pl.kind = kStream;
         // large batches: W rows streamed into registers against all the
-        // workgroup's columns (up to 256), H in chunks through LDS
+        // workgroup's columns (up to 256), H in chunks through LDS; also
+        // where no resident shape holds the hidden size, or only a one-block
+        // shape that would need several batch groups (each reading W again)
         const int nt = p->B <= kRows64.nt    ? kRows64.nt
                        : p->B <= kRows128.nt ? kRows128.nt
                                              : kRows256.nt;
-        if ((variant == kVarFlat || variant == kVarLogits) && p->B > 32 && p->d > 0 &&
-            p->d % (64 * rows_kcs(nt)) == 0) {
+        const bool rows_better =
+            p->B > 32 || !resident_ok || (pl.rcfg.nb == 1 && p->B > 16);
+        if ((variant == kVarFlat || variant == kVarLogits) && rows_better && p->d > 0 &&
+            p->d % (64 * rows_kcs(nt)) == 0 && pl.nmb >= 4) {
             pl.kind = kRows;
             pl.nt = nt;
         }

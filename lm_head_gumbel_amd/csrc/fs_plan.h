@@ -76,10 +76,13 @@ constexpr int topk_store_rows(int nb, int hl) { return hl > 0 ? 640 : 96 * 1024 
 // Instantiated resident shapes (nb, mpi, ks, nw, hk, hl, topk), in order of
 // preference for a given nb and k-step count nw * (hk + hl); topk = 1 where
 // the top-k row store fits in LDS beside the shape's own areas (the kernel
-// source checks this column against its LDS structures).  Each shape fits
-// 256 registers per lane without spilling; hl > 0 keeps the last hl k-steps of
-// each wave's H slice in LDS (d = 5120 with two batch blocks; the 18 + 2 split
-// leaves room in LDS for the top-k row store).
+// source checks this column against its LDS structures).  hl > 0 keeps the
+// last hl k-steps of each wave's H slice in LDS (d = 5120 with two batch
+// blocks; the 18 + 2 split leaves room in LDS for the top-k row store).  Hidden
+// sizes and their shapes: 512, 1024, 2048, 3072 (12 k-steps per wave), 4096,
+// 5120, and with one batch block and four waves of up to 512 registers (H in
+// VGPRs and AGPRs) 6144 and 7168 (48 and 56 k-steps per wave; 8 waves would
+// spill there).
 #define FS_RESIDENT_SHAPES(X) \
     X(1, 2, 4, 8, 16, 0, 1)   \
     X(1, 4, 2, 8, 16, 0, 0)   \
@@ -95,7 +98,11 @@ constexpr int topk_store_rows(int nb, int hl) { return hl > 0 ? 640 : 96 * 1024 
     X(2, 1, 2, 8, 18, 2, 1)   \
     X(2, 2, 4, 8, 8, 0, 0)    \
     X(2, 2, 2, 8, 4, 0, 0)    \
-    X(2, 2, 1, 8, 2, 0, 0)
+    X(2, 2, 1, 8, 2, 0, 0)    \
+    X(2, 1, 2, 8, 12, 0, 1)   \
+    X(1, 2, 2, 8, 12, 0, 1)   \
+    X(1, 2, 4, 4, 48, 0, 1)   \
+    X(1, 2, 4, 4, 56, 0, 1)
 
 bool resident_supported(const ResidentConfig& c, int variant);
 // Preferred instantiated shape for nb batch blocks, nks k-steps and a variant

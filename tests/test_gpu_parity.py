@@ -177,6 +177,16 @@ CASES = [
     (72, 512, 2000, 64, 0, 0, "mixed", True),
     # d = 5120 with two batch blocks: part of each wave's H slice lives in LDS
     (24, 5120, 2000, 128, 3, 16, "mixed", True),
+    # d = 3072 (12 k-steps per wave, two and one batch blocks), d = 6144 and
+    # 7168 (one batch block, four waves; two batch groups above 16 rows)
+    (20, 3072, 3000, 128, 5, 0, "mixed", True),
+    (9, 3072, 1700, 64, 0, 16, "range", False),
+    (9, 6144, 2000, 64, 3, 16, "range", False),
+    (24, 6144, 2500, 128, 0, 0, "mixed", True),
+    (5, 7168, 1500, 256, 0, 0, "mixed", True),
+    # no resident shape at d = 8192: flat and logits take the row-streaming
+    # kernel at any batch (64 columns, most of them padding here)
+    (3, 8192, 2000, 128, 0, 0, "mixed", True),
     # fewer than four vocab blocks: the workgroup-cooperative kernel
     (5, 64, 40, 16, 3, 0, "one", False),
     # B > 32 flat and logits with d % 512 == 0 (64 or 128 columns per
@@ -254,6 +264,7 @@ LARGE_K_CASES = [
     (24, 5120, 2000, 3, 16, "mixed", True, (128, 700)),
     (2, 2048, 1111, 1, 16, "range", True, (1024,)),
     (20, 512, 20000, 5, 0, "range", False, (200, 1024)),
+    (9, 6144, 3000, 2, 0, "mixed", True, (100, 1000)),
 ]
 
 
