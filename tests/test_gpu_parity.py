@@ -219,6 +219,11 @@ CASES = [
     (5, 2048, 20000, 1024, 3, 0, "mixed", True),
     (6, 1024, 40000, 8192, 5, 16, "range", False),
     (3, 512, 30000, 40000, 0, 0, "mixed", True),
+    # resident grouped at a tiny vocabulary: one tile (stage 2 in one
+    # workgroup per 32 rows), and 16 two-block tiles (two workgroups whose
+    # row keys meet through the atomic pair)
+    (3, 512, 100, 128, 0, 0, "mixed", False),
+    (6, 1024, 500, 32, 4, 0, "range", True),
 ]
 
 
