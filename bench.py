@@ -259,7 +259,8 @@ def bench_workloads(torch, fs, steps, W_head):
             cache[(v, d)] = _gpu_weights(torch, v, d)
         return cache[(v, d)]
 
-    for name in ("small_b32", "mid_b64", "large_b128", "large_b256", "topk_b32"):
+    for name in ("small_b1", "small_b8", "small_b32", "mid_b1", "mid_b4", "mid_b16", "mid_b64",
+                 "large_b128", "large_b256", "topk_b32"):
         wl = WORKLOADS[name]
         W = weights(wl.V, wl.d)
         H = _gpu_hidden(torch, wl.B, wl.d)
@@ -296,7 +297,7 @@ def bench_workloads(torch, fs, steps, W_head):
 
         line(name, wl, "unfused fs_logits + fs_multinomial", timed(unfused))
         del logits, lws, mws
-        if name == "mid_b64":
+        if name.startswith("mid_"):
             T = fs.fs_num_tiles(p)
             tm = torch.empty((wl.B, T), dtype=torch.float32, device="cuda")
             ti = torch.empty((wl.B, T), dtype=torch.int32, device="cuda")
@@ -360,6 +361,25 @@ def bench_workloads(torch, fs, steps, W_head):
             line(name, wl, f"online merge over {C} chunks of {chunk} ids "
                  "(fs_sample_grouped + fs_merge_online)", timed(online))
         del H, temp, ws
+
+    # the tiny reference configuration (B=4, d=256, V=4096, tiles of 512, W ~
+    # N(0, 1/d)): a latency line
+    cache.clear()
+    torch.cuda.empty_cache()
+    Wt = _gpu_weights(torch, 4096, 256, std=(1.0 / 256) ** 0.5)
+    Ht = _gpu_hidden(torch, 4, 256)
+    pt = fs.params(4, 256, 4096, tile_v=512, seed=SEED)
+    it = torch.empty(4, dtype=torch.int32, device="cuda")
+    wst = torch.empty(fs.fs_workspace_bytes(pt, fs.FS_VARIANT_FLAT), dtype=torch.uint8,
+                      device="cuda")
+
+    def tiny(i):
+        pt.step = i
+        fs.check(fs.fs_sample(pt, Ht, Wt, None, None, it, None, wst), "tiny")
+
+    wl_t = type("S", (), {"B": 4, "d": 256, "V": 4096})()
+    line("tiny_b4", wl_t, "flat fs_sample (latency)", timed(tiny))
+    del Wt, Ht, wst
 
     # one rank's shard of a G-way vocabulary split (the stage-1 kernel alone)
     cache.clear()
