@@ -16,7 +16,7 @@ from lm_head_gumbel_amd.inputs import (bf16_bits_to_f32, f32_to_bf16_bits, hidde
 from oracle import fs_oracle as O
 from oracle import philox as px
 from gpu_util import (Inputs, TOL_CUT, TOL_GAP, TOL_VALUE, check_grouped_unpinned,
-                      check_index_rows, check_values, log,
+                      check_index_rows, check_values, host, log,
                       run_flat, run_grouped, run_logits, run_merge, run_multinomial, run_topk,
                       run_topp, torch)
 from stats_util import chi_square_p, chi_square_rows_p, softmax
@@ -458,6 +458,36 @@ def test_repeated_calls_bit_identical():
     for u, v in zip(g1, g2):
         assert np.array_equal(np.asarray(u), np.asarray(v))
     assert np.array_equal(run_topk(x, p, 40), run_topk(x, p, 40))
+
+
+@pytest.mark.parametrize("tile_v", [128, 8192])
+def test_grouped_block_records_are_deterministic(tile_v):
+    """The resident kernel's block records on one reused workspace (its last
+    units by ticket, so the workgroup that walks a block changes from call to
+    call), merged per tile in stage 2 by several workgroups whose row keys meet
+    through atomics: every output is identical from call to call and to a
+    call on a fresh workspace."""
+    t = torch()
+    Hb, Wb, temp, allow = make_case(20, 1024, 30000, "mixed", True)
+    x = Inputs(Hb, Wb, temp, allow)
+    p = x.params(seed=SEED, step=5, tile_v=tile_v)
+    T = fs.fs_num_tiles(p)
+    ws = t.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_GROUPED), dtype=t.uint8, device="cuda")
+    outs = []
+    for _ in range(4):
+        m = t.full((x.B, T), 7.0, dtype=t.float32, device="cuda")
+        ti = t.full((x.B, T), -7, dtype=t.int32, device="cuda")
+        L = t.full((x.B, T), 7.0, dtype=t.float32, device="cuda")
+        o = t.full((x.B,), -7, dtype=t.int32, device="cuda")
+        fs.check(fs.fs_sample_grouped(p, x.H, x.W, x.temp, x.allow, m, ti, L, o, ws))
+        t.cuda.synchronize()
+        outs.append([host(m), host(ti), host(L), host(o)])
+    for run in outs[1:]:   # bit for bit, floats compared as their bit patterns
+        for u, v in zip(outs[0], run):
+            assert np.array_equal(u.view(np.int32), v.view(np.int32))
+    fresh = run_grouped(x, p)   # another workspace
+    for u, v in zip(outs[0], fresh):
+        assert np.array_equal(u.astype(np.float64), np.asarray(v, np.float64))
 
 
 def test_online_merge_matches_oracle():
