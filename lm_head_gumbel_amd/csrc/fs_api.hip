@@ -335,7 +335,8 @@ fs_status fs_sample_grouped(const fs_params* p, const void* H, const void* W,
     a.sched = a.dyn_k0 > 0 ? w.sched : nullptr;
     a.gsel = w.gsel;
     hipError_t e =
-        pl.kind == kWide       ? launch_wide(kVarGrouped, a, pl.nt, pl.grid_y, s)
+        pl.kind == kRows       ? launch_rows(kVarGrouped, a, pl.nt, pl.grid_y, s)
+        : pl.kind == kWide     ? launch_wide(kVarGrouped, a, pl.nt, pl.grid_y, s)
         : pl.kind == kResident ? launch_resident(kVarGrouped, a, pl.grid_y, pl.rcfg, s)
         : pl.stream            ? launch_stream(kVarGrouped, a, pl.grid_y, pl.cfg, w.part, true, s)
                                : launch_stage1(kVarGrouped, a, pl.grid_y, pl.cfg, s);

@@ -118,19 +118,23 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
         // workgroup's columns (up to 256), H in chunks through LDS; also
         // where no resident shape holds the hidden size, or only a one-block
         // shape that would need several batch groups (each reading W again)
-        const int nt = p->B <= kRows64.nt    ? kRows64.nt
-                       : p->B <= kRows128.nt ? kRows128.nt
-                                             : kRows256.nt;
+        // (grouped: at most 128 columns per workgroup, more in column groups)
+        const int nt = p->B <= kRows64.nt                                 ? kRows64.nt
+                       : p->B <= kRows128.nt || variant == kVarGrouped ? kRows128.nt
+                                                                         : kRows256.nt;
         const bool rows_better =
             p->B > 32 || !resident_ok || (pl.rcfg.nb == 1 && p->B > 16);
-        if ((variant == kVarFlat || variant == kVarLogits) && rows_better && p->d > 0 &&
-            p->d % (64 * rows_kcs(nt)) == 0 && pl.nmb >= 4) {
+        // (grouped too: a record per 16-row block, as the resident kernel
+        // writes them)
+        if (variant != kVarTopk && rows_better && p->d > 0 && p->d % (64 * rows_kcs(nt)) == 0 &&
+            pl.nmb >= 4) {
             pl.kind = kRows;
             pl.nt = nt;
         }
         // grouped records up to 64 columns: one workgroup per CU, each range
         // meeting at most kWideMaxTiles vocabulary tiles (its slots live in LDS)
-        if (variant == kVarGrouped && p->B > 32 && p->B <= 64 && p->d > 0 && p->d % 128 == 0) {
+        if (variant == kVarGrouped && pl.kind != kRows && p->B > 32 && p->B <= 64 && p->d > 0 &&
+            p->d % 128 == 0) {
             const int g = std::max(1, std::min(pl.nmb, cus));
             const int blocks = ceil_div(pl.nmb, g);   // longest range
             if ((blocks - 1 + pl.tile_mb - 1) / pl.tile_mb + 1 <= kWideMaxTiles &&
@@ -144,7 +148,7 @@ void make_plan(const fs_params* p, int variant, int cus, Plan& pl) {
     pl.cfg = pick_config(pl.stream, p->B);
     // grouped on the resident kernel: a record per 16-row block, so that its
     // walk takes the strided (and ticket) order like flat
-    pl.unit_rec = variant == kVarGrouped && pl.kind == kResident;
+    pl.unit_rec = variant == kVarGrouped && (pl.kind == kResident || pl.kind == kRows);
     pl.rec_cols = pl.unit_rec ? (pl.B + 31) / 32 * 32 : 0;
 
     // 2. batch groups

@@ -54,6 +54,19 @@ __device__ __forceinline__ int rows_tile_row(int wave, int j, int ar) {
     return ((j * 4 + (ar >> 2)) * kRWaves + wave) * 4 + (ar & 3);
 }
 
+// The grouped variant keeps a record per 16-row vocabulary block, so each
+// block of a tile lies in one wave: block j of wave `wave` is the tile's
+// block j kRWaves + wave (tile rows 16 (j kRWaves + wave) ..), and the
+// block's record is one column reduction of that wave's MFMA tile.  Block
+// j = 0 still covers tile rows 0 .. 127.
+template <int VAR>
+__device__ __forceinline__ int rows_row(int wave, int j, int ar) {
+    if constexpr (VAR == kVarGrouped)
+        return (j * kRWaves + wave) * 16 + ar;
+    else
+        return rows_tile_row(wave, j, ar);
+}
+
 // The W ring is refilled in groups of GQ k-steps: after k-step kk with
 // kk % GQ == GQ - 1, the loads of k-steps kk + PF - GQ + 1 .. kk + PF go out
 // back to back, so that each row is read in runs of 64 GQ bytes (whole
@@ -116,7 +129,7 @@ __device__ __forceinline__ bf16x8 load_untracked(const uint16_t* p) {
 // the general epilogue it would not fit in registers).
 template <int RB, int KRA, int KCS, int PF, int GQ, int VAR, bool LEAN>
 __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
-    static_assert(VAR == kVarFlat || VAR == kVarLogits, "variant");
+    static_assert(VAR == kVarFlat || VAR == kVarLogits || VAR == kVarGrouped, "variant");
     static_assert(!LEAN || VAR == kVarFlat, "lean epilogue: flat only");
     static_assert(KRA >= 1 && KRA <= 4 && KCS % PF == 0 && (GQ & (GQ - 1)) == 0 && PF % GQ == 0 &&
                       PF >= 2 * GQ,
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
         const int k = (ks < nks ? ks : ks - nks) * 32 + kg * 8;
 #pragma unroll
         for (int j = 0; j < decltype(jn)::value; ++j) {
-            const int r = min(base + rows_tile_row(wave, j, r16), row_end - 1);
+            const int r = min(base + rows_row<VAR>(wave, j, r16), row_end - 1);
             dst[j] = load_untracked(a.W + (size_t)r * a.d + k);
         }
         if (ld_tile * nks + ld_ks + 1 < nsteps) {   // clamp at the last k-step
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     // one chunk: read from stage `st`, the next chunk goes to `other`
     // (the chunk that ends a tile is always the second of a pair: nch is
     // even).  A tile with at most 128 rows left in the range (`half`) has
-    // rows in block j = 0 only (rows_tile_row): the other blocks' loads,
+    // rows in block j = 0 only (rows_row): the other blocks' loads,
     // MFMAs and noise are skipped.  Such a tile comes last and runs in a loop
     // of its own, entered with no load in flight, where every k-step issues
     // one W load per wave: the waits count JN loads per k-step.
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                     Lse unused = lse_empty();
                     rows_static_for<JN>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
-                        const int rowg = tbase + rows_tile_row(wave, j, 4 * kg);   // 4 consecutive rows
+                        const int rowg = tbase + rows_row<VAR>(wave, j, 4 * kg);   // 4 consecutive rows
                         const bool ok = rowg < row_end;
                         if constexpr (VAR == kVarLogits) {
                             if (cx.ok && ok) {
@@ -339,6 +352,20 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                                 for (int r = 0; r < 4; ++r)
                                     if (rowg + r < a.V) dst[rowg + r] = acc[j][n][r];
                             }
+                        } else if constexpr (VAR == kVarGrouped) {
+                            // the record of block j kRWaves + wave for these
+                            // 16 columns (block-major, slot = the block)
+                            const uint32_t word =
+                                decltype(masked)::value ? allow_word(a, cx, rowg, ok) : ~0u;
+                            float x[4], sc[4];
+                            lane_scores(a, cx, acc[j][n], rowg, ok, word, x, sc);
+                            uint64_t kb = pack_key(-INFINITY, -1);
+                            Lse lb = lse_empty();
+                            fold<kVarGrouped>(kb, lb, x, sc, a.v_offset + rowg);
+                            column_reduce<kVarGrouped>(kb, lb);
+                            const int blk_row = tbase + (j * kRWaves + wave) * 16;
+                            if (lane < 16 && blk_row < row_end)
+                                put_record<kVarGrouped, false>(a, blk_row / kMBlock, cx, kb, lb);
                         } else {
                             const uint32_t word =
                                 decltype(masked)::value ? allow_word(a, cx, rowg, ok) : ~0u;
@@ -377,7 +404,7 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                     int bi = -1;
                     rows_static_for<JN>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
-                        const int rowg = tbase + rows_tile_row(wave, j, 4 * kg);
+                        const int rowg = tbase + rows_row<VAR>(wave, j, 4 * kg);
                         const int gid0 = a.v_offset + rowg;
                         float g[4] = {0.f, 0.f, 0.f, 0.f};
                         if (noisy) {
@@ -410,8 +437,8 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
-            if constexpr (VAR == kVarLogits) {
-                fold_tile(std::false_type{});
+            if constexpr (VAR == kVarLogits || VAR == kVarGrouped) {
+                fold_tile(std::integral_constant<bool, VAR == kVarGrouped>{});
                 // the loop's counted waits assume loads only: stores may
                 // complete out of order with them, so none stays in flight
                 rows_wait_vmcnt<0>();
@@ -446,6 +473,11 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     // the trailing loads (refills past the end) land before the wave goes on
     rows_wait_vmcnt<0>();
 
+    if constexpr (VAR == kVarGrouped) {
+        // stage 2's per-row [key, count] pairs start cleared
+        if (a.gsel && blockIdx.x == 0 && blockIdx.y == 0)
+            for (int b = tid; b < 2 * a.B; b += 64 * kRWaves) a.gsel[b] = 0ull;
+    }
     if constexpr (VAR == kVarFlat) {
         __syncthreads();
         for (int c = tid; c < NT; c += 64 * kRWaves) {
@@ -482,6 +514,13 @@ static hipError_t launch_rows_var(const Stage1Args& a, int nt, int grid_y, hipSt
 
 hipError_t launch_rows(int variant, const Stage1Args& a, int nt, int grid_y, hipStream_t stream) {
     if (variant == kVarFlat) return launch_rows_var<kVarFlat>(a, nt, grid_y, stream);
+    if (variant == kVarGrouped) {
+        // (at 256 columns the grouped epilogue would spill inside the loop:
+        // larger batches take several 128-column groups)
+        if (nt == kRows64.nt) return launch_rows_shape<4, kRows64, kVarGrouped>(a, grid_y, stream);
+        if (nt == kRows128.nt) return launch_rows_shape<8, kRows128, kVarGrouped>(a, grid_y, stream);
+        return hipErrorInvalidValue;
+    }
     if (variant == kVarLogits) return launch_rows_var<kVarLogits>(a, nt, grid_y, stream);
     return hipErrorInvalidValue;
 }

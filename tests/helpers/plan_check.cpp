@@ -93,7 +93,8 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
             CHECK(pl.rcfg.nw * (pl.rcfg.hk + pl.rcfg.hl) == cdiv(d, 32), "resident k-steps");
         }
         if (pl.kind == kRows) {
-            CHECK(var == kVarFlat || var == kVarLogits, "rows variant");
+            CHECK(var == kVarFlat || var == kVarLogits || var == kVarGrouped, "rows variant");
+            CHECK(var != kVarGrouped || pl.nt <= 128, "rows grouped columns");
             CHECK(d % (64 * rows_kcs(pl.nt)) == 0, "rows d %d nt %d", d, pl.nt);
         }
         if (pl.kind == kWide || pl.kind == kRows)
@@ -105,7 +106,8 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
             CHECK(var != kVarGrouped || pl.nt == 64, "wide grouped nt");
         }
         if (pl.kind == kStream) CHECK(pl.G <= std::max(1, pl.nmb / 4), "stream G");
-        CHECK(pl.unit_rec == (var == kVarGrouped && pl.kind == kResident), "block records");
+        CHECK(pl.unit_rec == (var == kVarGrouped && (pl.kind == kResident || pl.kind == kRows)),
+              "block records");
         const bool strided = pl.kind == kResident && (var != kVarGrouped || pl.unit_rec);
         const int64_t nunits = strided ? cdiv(pl.nmb, pl.rcfg.mpi) : pl.nmb;
         CHECK(pl.G <= nunits, "G %d > units %lld", pl.G, (long long)nunits);
@@ -228,6 +230,7 @@ int main() {
     check_case(150, 256, 2000, 0, 128, 256, "rows_b150");
     check_case(256, 256, 70000, 0, 4096, 256, "rows_b256");
     check_case(300, 256, 5000, 0, 64, 256, "rows_b300");
+    check_case(200, 512, 30000, 0, 128, 256, "rows_b200_d512");
 
     // a grid of shapes, extremes included
     const int Bs[] = {1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,

@@ -201,6 +201,9 @@ CASES = [
     (150, 256, 2000, 128, 5, 0, "mixed", True),
     (256, 256, 70000, 4096, 3, 0, "mixed", True),
     (300, 256, 5000, 64, 0, 0, "range", False),
+    # grouped on the row-streaming kernel (a record per 16-row block, each
+    # block in one wave) in two 128-column groups paired on one XCD
+    (200, 512, 30000, 128, 5, 0, "mixed", True),
     # B > 32 with other d: the streaming kernel
     (100, 192, 1700, 64, 0, 16, "range", False),
     # 32 < B <= 64: grouped records from the LDS-tiled kernel too; ranges of

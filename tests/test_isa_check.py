@@ -110,10 +110,11 @@ def test_rows_kernels_pass(tmp_path):
     text = out.read_text()
     assert isa_check.check_text(text, require_untracked=True) == []
     # every instantiation was analysed (3 shapes x lean flat, general flat,
-    # logits), and no loop that issues MFMAs spills: a reload there would
-    # bring a compiler wait for every load in flight
+    # logits; grouped at 64 and 128 columns), and no loop that issues MFMAs
+    # spills: a reload there would bring a compiler wait for every load in
+    # flight
     funcs = isa_check._functions(text.splitlines())
-    assert len(funcs) == 9, [n for n, _ in funcs]
+    assert len(funcs) == 11, [n for n, _ in funcs]
     assert mfma_loop_spills(text) == []
 
 

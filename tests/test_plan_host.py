@@ -57,11 +57,11 @@ def test_plans_and_layouts_under_sanitizers(plan_check):
     # ticket order like flat
     g = plans[("headline_b32", 1)]
     assert (g["unit_rec"], g["P"], g["dyn_k0"]) == ("1", "9496", h["dyn_k0"])
-    assert plans[("mid_b64", 1)]["unit_rec"] == "0"            # the LDS-tiled kernel's ranges
+    assert plans[("mid_b64", 1)]["unit_rec"] == "1"            # block records from the rows kernel
     sw = plans[("sweep_b256", 0)]   # one group of 256 columns, a workgroup per CU
     assert (sw["kind"], sw["nt"], sw["grid_y"], sw["G"]) == ("4", "256", "1", "256")
     assert plans[("sweep_b128", 0)]["nt"] == "128"
-    assert plans[("mid_b64", 1)]["kind"] == "3"               # grouped B = 64 on the LDS kernel
+    assert plans[("mid_b64", 1)]["kind"] == "4"               # grouped B = 64: the rows kernel
     assert plans[("topk_b32", 3)]["rcfg"] == "2,1,2,8,18,2"   # d = 5120: H partly in LDS
     assert plans[("tiny_b4", 0)]["kind"] == "1"                # d = 256: the streaming kernel
     # the parity cases of the row-streaming kernel reach it, flat and logits,
@@ -73,6 +73,13 @@ def test_plans_and_layouts_under_sanitizers(plan_check):
             pl = plans[(name, var)]
             assert (pl["kind"], pl["nt"], pl["grid_y"]) == ("4", str(nt), str(gy)), (name, pl)
     assert plans[("rows_b300", 0)]["xcd"] == "1"
+    # grouped on the row-streaming kernel too (block records), at most 128
+    # columns per workgroup: larger batches in paired column groups
+    for name, nt, gy in [("rows_b33", 64, 1), ("rows_b100", 128, 1), ("rows_b128", 128, 1),
+                         ("rows_b200_d512", 128, 2)]:
+        pl = plans[(name, 1)]
+        assert (pl["kind"], pl["nt"], pl["grid_y"], pl["unit_rec"]) == ("4", str(nt), str(gy), "1"), \
+            (name, pl)
     # ranges of 17 or 18 blocks (272 or 288 rows: a 256-row tile and a short
     # one) and of 25 blocks (400 rows: the last tile of 144 rows runs whole)
     assert plans[("rows_b128", 0)]["G"] == "256"
