@@ -621,7 +621,8 @@ def main():
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": alg_bytes(args.batch) / t_k1 / PEAK_HBM,
                      "traffic": stored_traffic(args.batch),
-                     "kernel": "fs::resident_kernel (flat stage 1)",
+                     "kernel": ("fs::resident_kernel" if args.batch <= 32 else "fs::rows_kernel")
+                               + " (flat stage 1)",
                      "kernel_us": head["stage1_us"], "kernel_per_launch_us": head["stage1"],
                      "bytes_per_launch": alg_bytes(args.batch),
                      "frac_of_read_probe": (alg_bytes(args.batch) / t_k1 / 1e9 / probe["read_GBps"]

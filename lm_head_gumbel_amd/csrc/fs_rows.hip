@@ -103,12 +103,30 @@ struct RowsGeom {
     static_assert(kHL >= 1 && kStage % (1024 * kRWaves) == 0, "H stage");
 };
 
-template <int RB, int KCS>
+// Block records held in LDS until the kernel ends (grouped variant): the
+// first NREC blocks of the row range; the later ones are stored as their
+// tiles end.  A record store inside the loop has to complete before the next
+// counted wait, which drains the W loads in flight with it.
+template <int NT, int NREC>
+struct RowsRecs {
+    float m[NREC][NT];
+    int32_t idx[NREC][NT];
+    float L[NREC][NT];
+};
+struct RowsNoRecs {};
+
+// LDS-held block records: 64 blocks at 64 columns (48 KiB beside the 64 KiB
+// of H stages); none at more columns, whose H stages leave too little room.
+template <int RB, int VAR>
+constexpr int rows_nrec() { return VAR == kVarGrouped && RB == 4 ? 64 : 0; }
+
+template <int RB, int KCS, int NREC>
 struct RowsSmem {
     alignas(1024) char hs0[RowsGeom<RB, KCS>::kStage];   // H stages (two arrays: each
     alignas(1024) char hs1[RowsGeom<RB, KCS>::kStage];   // chunk names its own)
     uint64_t key[kRWaves][RB * 16];   // per-wave column winners
     ColCtxSmem<RB * 16> cols;
+    std::conditional_t<(NREC > 0), RowsRecs<RB * 16, NREC>, RowsNoRecs> recs;
 };
 
 // A 16-byte global load the compiler does not track: the caller waits for it
@@ -138,7 +156,8 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     constexpr int NT = Geo::kNT;
     constexpr int HL = Geo::kHL;
     constexpr int kRMT = kRWaves * KRA * 16;   // rows per tile
-    __shared__ RowsSmem<RB, KCS> sm;
+    constexpr int NREC = rows_nrec<RB, VAR>();
+    __shared__ RowsSmem<RB, KCS, NREC> sm;
 
     // row range w and column group y (see resident_kernel for the XCD pairing)
     int w, y;
@@ -364,8 +383,25 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                             fold<kVarGrouped>(kb, lb, x, sc, a.v_offset + rowg);
                             column_reduce<kVarGrouped>(kb, lb);
                             const int blk_row = tbase + (j * kRWaves + wave) * 16;
-                            if (lane < 16 && blk_row < row_end)
-                                put_record<kVarGrouped, false>(a, blk_row / kMBlock, cx, kb, lb);
+                            const int slot = (blk_row - row0) / kMBlock;   // uniform
+                            if (lane < 16 && blk_row < row_end) {
+                                bool held = false;
+                                if constexpr (NREC > 0) {
+                                    if (slot < NREC) {
+                                        // the values put_record would write,
+                                        // stored at the end of the kernel
+                                        const int32_t id = key_index(kb);
+                                        const int c = n * 16 + lane;
+                                        sm.recs.m[slot][c] = id >= 0 ? key_score(kb) : -INFINITY;
+                                        sm.recs.idx[slot][c] = id;
+                                        sm.recs.L[slot][c] = cx.greedy ? lb.mx : lse_value(lb);
+                                        held = true;
+                                    }
+                                }
+                                if (!held)
+                                    put_record<kVarGrouped, false>(a, blk_row / kMBlock, cx, kb,
+                                                                   lb);
+                            }
                         } else {
                             const uint32_t word =
                                 decltype(masked)::value ? allow_word(a, cx, rowg, ok) : ~0u;
@@ -441,7 +477,9 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
                 fold_tile(std::integral_constant<bool, VAR == kVarGrouped>{});
                 // the loop's counted waits assume loads only: stores may
                 // complete out of order with them, so none stays in flight
-                rows_wait_vmcnt<0>();
+                // (a tile whose block records all stay in LDS stored nothing)
+                if (VAR == kVarLogits || (tbase - row0) / kMBlock + kRMT / kMBlock > NREC)
+                    rows_wait_vmcnt<0>();
             } else if constexpr (LEAN) {
                 fold_lean();
             } else {
@@ -477,6 +515,20 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
         // stage 2's per-row [key, count] pairs start cleared
         if (a.gsel && blockIdx.x == 0 && blockIdx.y == 0)
             for (int b = tid; b < 2 * a.B; b += 64 * kRWaves) a.gsel[b] = 0ull;
+        if constexpr (NREC > 0) {
+            // the block records held in LDS (block-major, as put_record)
+            __syncthreads();
+            const int nheld = min((row_end - row0 + kMBlock - 1) / kMBlock, NREC);
+            for (int e = tid; e < nheld * NT; e += 64 * kRWaves) {
+                const int slot = e / NT, c = e % NT;
+                if (bbase + c < a.B) {
+                    const size_t o = (size_t)(row0 / kMBlock + slot) * a.rec_cols + bbase + c;
+                    a.pm[o] = sm.recs.m[slot][c];
+                    a.pidx[o] = sm.recs.idx[slot][c];
+                    a.pL[o] = sm.recs.L[slot][c];
+                }
+            }
+        }
     }
     if constexpr (VAR == kVarFlat) {
         __syncthreads();

@@ -204,6 +204,10 @@ CASES = [
     # grouped on the row-streaming kernel (a record per 16-row block, each
     # block in one wave) in two 128-column groups paired on one XCD
     (200, 512, 30000, 128, 5, 0, "mixed", True),
+    # grouped at 64 columns, ranges of 68-69 blocks: the first 64 block
+    # records held in LDS to the end of the kernel, the rest stored as their
+    # tiles end (16-block vocabulary tiles mixing both)
+    (40, 512, 280003, 256, 5, 0, "mixed", True),
     # B > 32 with other d: the streaming kernel
     (100, 192, 1700, 64, 0, 16, "range", False),
     # 32 < B <= 64: grouped records from the LDS-tiled kernel too; ranges of
