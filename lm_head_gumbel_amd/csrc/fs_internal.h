@@ -142,8 +142,8 @@ hipError_t launch_stage2_flat(const float* pm, const int32_t* pidx, int P, int B
 // Grouped records: tile t's are the slots w + t of the G ranges of nmb units
 // that meet it (records [B][P]), or with gsel (block records, block-major
 // [nmb][rec_cols], slot = block: nmb blocks, tiles of tile_mb) its blocks;
-// gsel is the per-row [key, count] pair of the sample, cleared by stage 1.
-// sched as for flat.
+// gsel is the per-row [key, count] pair of the sample, cleared by stage 1,
+// at gsel[kGselStride b].  sched as for flat.
 hipError_t launch_stage2_grouped(const float* pm, const int32_t* pidx, const float* pL, int P,
                                  int rec_cols, int B, int T, int G, int nmb, int tile_mb, const float* temp,
                                  uint32_t flags, const NoiseSrc& noise, float* tile_max,

@@ -272,7 +272,7 @@ WsLayout layout(int ws_variant, const Plan& pl, int k) {
         w.pidx = take(P * cols * 4);
         if (ws_variant == FS_VARIANT_GROUPED) w.pL = take(P * cols * 4);
         if (pl.stream) w.part = take(part_bytes(pl));
-        if (ws_variant == FS_VARIANT_GROUPED && pl.unit_rec) w.gsel = take(B * 16);
+        if (ws_variant == FS_VARIANT_GROUPED && pl.unit_rec) w.gsel = take(B * 8 * kGselStride);
         w.sched = take(kSchedBytes);
     } else if (ws_variant == FS_VARIANT_TOPK) {
         const int L = topk_len(pl, k);

@@ -38,6 +38,11 @@ enum Stage1Variant { kVarFlat = 0, kVarGrouped = 1, kVarLogits = 2, kVarTopk = 3
 // for 32 < B <= 64).
 enum Stage1Kind { kCoop = 0, kStream = 1, kResident = 2, kWide = 3, kRows = 4 };
 
+// Grouped block records: stage 2's per-row [key, count] sample pairs, one
+// pair per 128-byte line (row b's at element kGselStride b of the array), so
+// that the atomics of different rows go to different lines.
+constexpr int kGselStride = 16;
+
 // The row-streaming large-batch kernel (fs_rows.hip): workgroups of 64, 128
 // or 256 batch columns (more columns: several column groups), H chunks of KCS
 // k-steps taken in pairs (d a multiple of 64 KCS).
@@ -147,7 +152,7 @@ struct WsLayout {
     size_t sel = kAbsent;                            // top-k selection levels
     size_t mm = kAbsent, ms = kAbsent, mkey = kAbsent;   // multinomial chunk sums
     size_t part = kAbsent;                           // streaming partial sums
-    size_t gsel = kAbsent;                           // grouped block records: [B][2] sample pairs
+    size_t gsel = kAbsent;                           // grouped block records: [B][kGselStride] (a sample pair per line)
     size_t sched = kAbsent;                          // flat/grouped/top-k unit scheduler (last)
     size_t total = 0;
 };

@@ -432,7 +432,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // stage 2's per-row [key, count] pairs start cleared (after the walk:
         // no store is pending during it)
         if (a.gsel && blockIdx.x == 0 && blockIdx.y == 0)
-            for (int b = threadIdx.x; b < 2 * a.B; b += blockDim.x) a.gsel[b] = 0ull;
+            for (int b = threadIdx.x; b < 2 * a.B; b += blockDim.x)
+                a.gsel[kGselStride * (b >> 1) + (b & 1)] = 0ull;
     }
     if (dyn && threadIdx.x == 0) {
         // every ticket of this workgroup has returned (each was read back);

@@ -514,7 +514,8 @@ __global__ __launch_bounds__(64 * kRWaves, 1) void rows_kernel(Stage1Args a) {
     if constexpr (VAR == kVarGrouped) {
         // stage 2's per-row [key, count] pairs start cleared
         if (a.gsel && blockIdx.x == 0 && blockIdx.y == 0)
-            for (int b = tid; b < 2 * a.B; b += 64 * kRWaves) a.gsel[b] = 0ull;
+            for (int b = tid; b < 2 * a.B; b += 64 * kRWaves)
+                a.gsel[kGselStride * (b >> 1) + (b & 1)] = 0ull;
         if constexpr (NREC > 0) {
             // the block records held in LDS (block-major, as put_record)
             __syncthreads();

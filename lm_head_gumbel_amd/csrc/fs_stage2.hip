@@ -248,15 +248,15 @@ __global__ __launch_bounds__(256) void stage2_grouped_cols_kernel(
             // relaxed device-scope atomics, each waited for before the next
             // (see stage2_grouped_blocks_kernel)
             unsigned long long old = __hip_atomic_fetch_max(
-                &gsel[2 * b], (unsigned long long)best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                &gsel[kGselStride * b], (unsigned long long)best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("" : "+v"(old));
             const unsigned long long n = __hip_atomic_fetch_add(
-                &gsel[2 * b + 1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                &gsel[kGselStride * b + 1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (n == gridDim.x - 1) {
                 unsigned long long zero = 0ull;
                 asm volatile("" : "+v"(zero));
                 const unsigned long long k = __hip_atomic_fetch_max(
-                    &gsel[2 * b], zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    &gsel[kGselStride * b], zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 out_idx[b] = key_index(key_max(k, old));
             }
         }
@@ -410,17 +410,17 @@ __global__ __launch_bounds__(kGrpBlkThreads) void stage2_grouped_blocks_kernel(
                 // every maximum in.  (Release and acquire at device scope
                 // would write back and invalidate the whole L2 of the XCD.)
                 unsigned long long old = __hip_atomic_fetch_max(
-                    &gsel[2 * b], (unsigned long long)best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    &gsel[kGselStride * b], (unsigned long long)best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 asm volatile("" : "+v"(old));   // the maximum has returned
                 const unsigned long long n = __hip_atomic_fetch_add(
-                    &gsel[2 * b + 1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    &gsel[kGselStride * b + 1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (n == gridDim.x - 1) {   // every workgroup of the row is in
                     // read back as an atomic where the others were performed
                     // (an opaque operand keeps it from becoming a plain load)
                     unsigned long long zero = 0ull;
                     asm volatile("" : "+v"(zero));
                     const unsigned long long k = __hip_atomic_fetch_max(
-                        &gsel[2 * b], zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        &gsel[kGselStride * b], zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     out_idx[b] = key_index(key_max(k, old));
                 }
             }

@@ -135,7 +135,7 @@ void check_case(int B, int d, int V, int v_offset, int tile_v, int cus, const ch
             CHECK(pl.rec_cols == (pl.unit_rec ? (B + 31) / 32 * 32 : 0), "record columns");
             const size_t rc = var == kVarGrouped && pl.unit_rec ? (size_t)pl.rec_cols : b;
             check_layout(l, {{l.pm, P * rc * 4}, {l.pidx, P * rc * 4}, {l.pL, P * rc * 4},
-                             {l.part, pl.stream ? part_bytes(pl) : 0}, {l.gsel, b * 16},
+                             {l.part, pl.stream ? part_bytes(pl) : 0}, {l.gsel, b * 8 * kGselStride},
                              {l.sched, kSchedBytes}},
                          "records");
             // the multinomial baseline plans with the flat variant
