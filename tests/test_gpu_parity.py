@@ -204,6 +204,9 @@ CASES = [
     # grouped on the row-streaming kernel (a record per 16-row block, each
     # block in one wave) in two 128-column groups paired on one XCD
     (200, 512, 30000, 128, 5, 0, "mixed", True),
+    # grouped at 128 columns, ranges of 17-18 blocks: one full tile and a
+    # half tile
+    (100, 512, 70000, 256, 5, 0, "mixed", True),
     # grouped at 64 columns, ranges of 68-69 blocks: the first 64 block
     # records held in LDS to the end of the kernel, the rest stored as their
     # tiles end (16-block vocabulary tiles mixing both)
