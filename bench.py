@@ -183,9 +183,9 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
             p.step = i
             fs.check(fs.fs_sample_grouped(p, H, W, None, None, tm, ti, tl, idx, gws), "grouped")
 
-        for i in range(3):
+        for i in range(max(3, warmup // 2)):
             grouped(i)
-        res["grouped_calls_per_s"] = 1.0 / timer.run(grouped, max(10, steps // 4))[0]
+        res["grouped_calls_per_s"] = 1.0 / timer.run(grouped, steps)[0]
         k = 40
         kws = torch.empty(fs.fs_workspace_bytes(p, fs.FS_VARIANT_TOPK, k), dtype=torch.uint8,
                           device="cuda")
@@ -194,17 +194,17 @@ def bench_batch(torch, fs, H_all, W, B, steps, warmup, unfused=True, variants=Fa
             p.step = i
             fs.check(fs.fs_sample_topk(p, H, W, None, None, k, idx, kws), "topk")
 
-        for i in range(3):
+        for i in range(max(3, warmup // 2)):
             topk(i)
-        res["topk40_calls_per_s"] = 1.0 / timer.run(topk, max(10, steps // 4))[0]
+        res["topk40_calls_per_s"] = 1.0 / timer.run(topk, steps)[0]
 
         def topp(i):
             p.step = i
             fs.check(fs.fs_sample_topk_topp(p, H, W, None, None, k, 0.9, idx, kws), "topp")
 
-        for i in range(3):
+        for i in range(max(3, warmup // 2)):
             topp(i)
-        res["topk40_topp0.9_calls_per_s"] = 1.0 / timer.run(topp, max(10, steps // 4))[0]
+        res["topk40_topp0.9_calls_per_s"] = 1.0 / timer.run(topp, steps)[0]
     return res
 
 
@@ -230,10 +230,10 @@ def bench_workloads(torch, fs, steps, W_head):
     from lm_head_gumbel_amd.inputs import WORKLOADS
     timer = Timer(torch)
     out = []
-    n = max(10, steps // 4)
+    n = max(10, steps // 2)
 
     def timed(fn):
-        for i in range(3):
+        for i in range(5):
             fn(i)
         t, _, per = timer.run(fn, n)
         return t, per
