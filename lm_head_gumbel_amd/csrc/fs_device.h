@@ -114,13 +114,16 @@ struct Lse {
 };
 __device__ __forceinline__ Lse lse_empty() { return Lse{-INFINITY, 0.f}; }
 __device__ __forceinline__ Lse lse_add(Lse a, float x) {
-    if (!(x > -INFINITY)) return a;
-    if (x > a.mx) {
-        a.sm = a.sm * __expf(a.mx - x) + 1.f;
-        a.mx = x;
-    } else {
-        a.sm += __expf(x - a.mx);
-    }
+    // Without branches, one exponential for both cases: exp(-|x - mx|) is
+    // exp(mx - x) when x is the new maximum and exp(x - mx) otherwise (0 when
+    // a is empty).  A masked x (-inf) leaves a as it is.
+    const bool ok = x > -INFINITY;
+    const float dlt = x - a.mx;
+    const float e = __expf(-fabsf(dlt));
+    const bool up = dlt > 0.f;
+    const float sm = up ? a.sm * e + 1.f : a.sm + e;
+    a.sm = ok ? sm : a.sm;
+    a.mx = ok && up ? x : a.mx;
     return a;
 }
 __device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {

@@ -82,7 +82,12 @@ __device__ __forceinline__ ColCtx col_ctx_load(const ColCtxSmem<N>& s, const Sta
 // for it also waits for every load issued before it.
 __device__ __forceinline__ uint32_t allow_word(const Stage1Args& a, const ColCtx& c, int row0,
                                                bool blk_ok) {
-    return (c.allow_row && blk_ok && row0 < a.V) ? c.allow_row[row0 >> 5] : ~0u;
+    // (read through a global pointer: the row pointer may be null, and as a
+    // generic pointer its read would be a FLAT load, whose wait also drains
+    // every load in flight)
+    typedef __attribute__((address_space(1))) const uint32_t global_u32;
+    return (c.allow_row && blk_ok && row0 < a.V) ? ((const global_u32*)c.allow_row)[row0 >> 5]
+                                                 : ~0u;
 }
 
 // Tempered, masked logits x of four consecutive rows row0..row0+3 (local W
@@ -133,10 +138,11 @@ __device__ __forceinline__ void fold(uint64_t& best, Lse& lse, const float (&x)[
                                      const float (&s)[4], int gid0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        if (x[r] > -INFINITY) {
-            best = key_max(best, pack_key(s[r], gid0 + r));
-            if constexpr (VAR == kVarGrouped) lse = lse_add(lse, x[r]);
-        }
+        // (selects, no branch: a masked row offers the empty key, and
+        // lse_add leaves the state as it is for x = -inf)
+        const uint64_t k = x[r] > -INFINITY ? pack_key(s[r], gid0 + r) : pack_key(-INFINITY, -1);
+        best = key_max(best, k);
+        if constexpr (VAR == kVarGrouped) lse = lse_add(lse, x[r]);
     }
 }
 
