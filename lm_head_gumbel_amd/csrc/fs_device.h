@@ -127,10 +127,14 @@ __device__ __forceinline__ Lse lse_add(Lse a, float x) {
     return a;
 }
 __device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
-    if (!(b.mx > -INFINITY)) return a;
-    if (!(a.mx > -INFINITY)) return b;
-    if (a.mx >= b.mx) return Lse{a.mx, a.sm + b.sm * __expf(b.mx - a.mx)};
-    return Lse{b.mx, b.sm + a.sm * __expf(a.mx - b.mx)};
+    // Without branches: the larger state's sum plus the smaller one's scaled
+    // by exp(-|a.mx - b.mx|); an empty state yields the other one.
+    const bool ge = a.mx >= b.mx;
+    const float e = __expf(-fabsf(a.mx - b.mx));
+    const Lse hi = ge ? a : b, lo = ge ? b : a;
+    Lse r{hi.mx, hi.sm + lo.sm * e};
+    r = a.mx > -INFINITY ? r : b;
+    return b.mx > -INFINITY ? r : a;
 }
 __device__ __forceinline__ float lse_value(Lse a) {
     return (a.mx > -INFINITY) ? a.mx + __logf(a.sm) : -INFINITY;
