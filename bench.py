@@ -464,14 +464,19 @@ def cpu_baseline(torch, H_all, W, B, seconds):
 
 
 def hbm_probe(torch, fs, W):
-    """Practical HBM ceiling: a plain streaming read of the W buffer and a copy
-    of 1 GiB, each timed with HIP events (GB/s of bytes moved)."""
+    """Practical HBM ceiling: a streaming read of the W buffer (plain loads, and
+    nontemporal loads, whose streaming policy reads faster) and a copy of 1 GiB,
+    each timed with HIP events (GB/s of bytes moved)."""
     nbytes = W.numel() * 2
     sink = torch.empty(256 * 256, dtype=torch.int32, device="cuda")
     timer = Timer(torch)
     for i in range(3):
         fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256), "read probe")
     t_read = timer.run(lambda i: fs.check(fs.fs_debug_read_probe(W, nbytes, sink, 256)), 20)[0]
+    for i in range(3):
+        fs.check(fs.fs_debug_read_probe_nt(W, nbytes, sink, 256), "read probe (nt)")
+    t_read_nt = timer.run(lambda i: fs.check(fs.fs_debug_read_probe_nt(W, nbytes, sink, 256)),
+                          20)[0]
     n = 1 << 30
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
@@ -490,7 +495,8 @@ def hbm_probe(torch, fs, W):
         t_l2 = timer.run(lambda i: fs.check(
             fs.fs_debug_shared_read_probe(W, l2b, reps, sink2, grid)), 20)[0]
         l2[f"grid{grid}_GBps"] = grid * reps * l2b / t_l2 / 1e9
-    return {"read_GBps": nbytes / t_read / 1e9, "copy_GBps": 2 * n / t_copy / 1e9,
+    return {"read_GBps": nbytes / t_read / 1e9, "read_nt_GBps": nbytes / t_read_nt / 1e9,
+            "copy_GBps": 2 * n / t_copy / 1e9,
             "read_grid": 256, "copy_grid": 1024, "copy_bytes": n,
             "l2_shared_read": dict(l2, bytes=l2b, reps=reps,
                                    per_cu_bytes_per_clk_at_2_4GHz=max(l2.values()) * 1e9 / 256 / 2.4e9)}
@@ -626,7 +632,9 @@ def main():
                      "kernel_us": head["stage1_us"], "kernel_per_launch_us": head["stage1"],
                      "bytes_per_launch": alg_bytes(args.batch),
                      "frac_of_read_probe": (alg_bytes(args.batch) / t_k1 / 1e9 / probe["read_GBps"]
-                                            if probe else None)},
+                                            if probe else None),
+                     "frac_of_read_probe_nt": (alg_bytes(args.batch) / t_k1 / 1e9
+                                               / probe["read_nt_GBps"] if probe else None)},
         "hbm_probe": probe,
         "cpu_baseline": cpu,
         "unfused_calls_per_s": head.get("unfused_calls_per_s"),

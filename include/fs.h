@@ -272,6 +272,13 @@ fs_status fs_debug_noise(uint64_t seed, uint32_t step, uint32_t stream_id, int32
 fs_status fs_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
                               void* stream);
 
+/* fs_debug_read_probe_nt -- the same read with nontemporal loads (the
+ * streaming cache policy, `nt` on the global loads): each instruction reads
+ * whole 128-byte lines, and this variant reaches a higher HBM read rate than
+ * the plain one.  Same arguments and errors as fs_debug_read_probe. */
+fs_status fs_debug_read_probe_nt(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                                 void* stream);
+
 /* fs_debug_shared_read_probe -- every one of `grid` workgroups of 256
  * threads reads all `bytes` (a positive multiple of 32768) at `src` (16-byte
  * aligned) `reps` (>= 1) times with 16-byte loads, each workgroup starting at

@@ -80,6 +80,7 @@ _SIGS = {
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                       ctypes.c_int32, _P, _P, _P]),
     "fs_debug_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
+    "fs_debug_read_probe_nt": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
     "fs_debug_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, ctypes.c_int32, _P]),
     "fs_debug_shared_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, _P,
                                                   ctypes.c_int32, _P]),
@@ -224,6 +225,10 @@ def fs_debug_noise(seed, step, stream_id, b0, nb, i0, ni, words=None, gumbel=Non
 
 def fs_debug_read_probe(src, nbytes, sink, grid, stream=None):
     return lib().fs_debug_read_probe(_ptr(src), nbytes, _ptr(sink), grid, _stream(stream))
+
+
+def fs_debug_read_probe_nt(src, nbytes, sink, grid, stream=None):
+    return lib().fs_debug_read_probe_nt(_ptr(src), nbytes, _ptr(sink), grid, _stream(stream))
 
 
 def fs_debug_shared_read_probe(src, nbytes, reps, sink, grid, stream=None):

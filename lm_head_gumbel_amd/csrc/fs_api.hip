@@ -462,7 +462,18 @@ fs_status fs_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, int
     if (!aligned16(src)) return FS_ERR_UNSUPPORTED;
     DeviceInfo dev;
     if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
-    return from_hip(launch_read_probe(src, bytes, sink, grid, static_cast<hipStream_t>(stream)));
+    return from_hip(
+        launch_read_probe(src, bytes, sink, grid, false, static_cast<hipStream_t>(stream)));
+}
+
+fs_status fs_debug_read_probe_nt(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                                 void* stream) {
+    if (!src || !sink || grid < 1 || bytes % 16 != 0) return FS_ERR_INVALID_ARG;
+    if (!aligned16(src)) return FS_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    if (!current_device(dev)) return FS_ERR_UNSUPPORTED;
+    return from_hip(
+        launch_read_probe(src, bytes, sink, grid, true, static_cast<hipStream_t>(stream)));
 }
 
 fs_status fs_debug_shared_read_probe(const void* src, size_t bytes, int32_t reps, uint32_t* sink,

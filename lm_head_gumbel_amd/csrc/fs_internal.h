@@ -197,7 +197,7 @@ hipError_t launch_debug_noise(uint32_t k0, uint32_t k1, uint32_t step, uint32_t 
                               int b0, int nb, int64_t i0, int ni, uint32_t* words, float* gumbel,
                               hipStream_t stream);
 
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, bool nt,
                              hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, int grid, hipStream_t stream);
 // bytes a multiple of 32 KiB

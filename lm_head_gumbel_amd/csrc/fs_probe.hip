@@ -9,8 +9,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
 
 // Each thread reads `unroll` 16-byte words per trip of a grid-stride loop and
-// folds them into one word, written once per thread so nothing is elided.
-template <int UNROLL>
+// folds them into one word, written once per thread so nothing is elided.  NT:
+// nontemporal loads (the streaming cache policy).
+template <bool NT>
+__device__ __forceinline__ u32x4 probe_load(const u32x4* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load((const global_u32x4*)p);
+    else
+        return *(const global_u32x4*)p;
+}
+
+template <int UNROLL, bool NT>
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* src, size_t n16,
                                                          uint32_t* sink) {
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -20,12 +29,12 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* src, size_
     for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
         u32x4 v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = *(const global_u32x4*)(src + i + u * stride);
+        for (int u = 0; u < UNROLL; ++u) v[u] = probe_load<NT>(src + i + u * stride);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < n16; i += stride) {
-        const u32x4 v = *(const global_u32x4*)(src + i);
+        const u32x4 v = probe_load<NT>(src + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     sink[tid] = acc;
@@ -61,10 +70,14 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4* dst, const u32x4* src,
         dst[i] = *(const global_u32x4*)(src + i);
 }
 
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, bool nt,
                              hipStream_t stream) {
-    hipLaunchKernelGGL(read_probe_kernel<8>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const u32x4*>(src), bytes / 16, sink);
+    if (nt)
+        hipLaunchKernelGGL((read_probe_kernel<8, true>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const u32x4*>(src), bytes / 16, sink);
+    else
+        hipLaunchKernelGGL((read_probe_kernel<8, false>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const u32x4*>(src), bytes / 16, sink);
     return hipGetLastError();
 }
 

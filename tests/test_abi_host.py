@@ -84,6 +84,11 @@ def test_null_and_negative_arguments_are_rejected():
     # the shared-read probe wants whole 32 KiB steps and at least one pass
     assert fs.fs_debug_shared_read_probe(0x1000, 1000, 1, 0x1000, 8) == fs.FS_ERR_INVALID_ARG
     assert fs.fs_debug_shared_read_probe(0x1000, 32768, 0, 0x1000, 8) == fs.FS_ERR_INVALID_ARG
+    # both read probes want whole 16-byte words, a sink and a grid
+    for probe in (fs.fs_debug_read_probe, fs.fs_debug_read_probe_nt):
+        assert probe(0x1000, 1000, 0x1000, 8) == fs.FS_ERR_INVALID_ARG
+        assert probe(0x1000, 1024, None, 8) == fs.FS_ERR_INVALID_ARG
+        assert probe(0x1000, 1024, 0x1000, 0) == fs.FS_ERR_INVALID_ARG
 
 
 def test_unsupported_requests_are_reported():
