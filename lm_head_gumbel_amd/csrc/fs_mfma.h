@@ -19,6 +19,12 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *(const global_u32x4*)(p));
 }
 
+// The same with the streaming (nontemporal) cache policy: for a stream read
+// once in whole 128-byte lines per instruction.
+__device__ __forceinline__ bf16x8 load_bf16x8_nt(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const global_u32x4*)(p)));
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }

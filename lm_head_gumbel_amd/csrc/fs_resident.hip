@@ -64,6 +64,121 @@ __device__ __forceinline__ void mfma_w(f32x4 (&acc)[MPI][NB], const WStage<MPI, 
     }
 }
 
+// Whole-line W loads (stages of an even number KS of k-steps).  The k-steps
+// of a stage come in pairs, and one instruction reads the pair's 128-byte
+// line of 8 rows of a block: lane l reads row 8 h + (l & 7) of the block (h,
+// the instruction's half of the block), bytes 16 (l >> 3) .. of the line.  As
+// an MFMA A operand that lane is row (l & 7) + 8 ((l >> 3) & 1), k-slots
+// 8 (l >> 4) ..: rows 0-7 hold the line's even 16-byte pieces of the half's
+// eight rows, rows 8-15 their odd pieces.  Two MFMAs take them apart: the
+// operand with the odd pieces zeroed against H's even pieces, and with the
+// even pieces zeroed against its odd pieces (H slot group g of a pair holds
+// pieces 2 g and 2 g + 1: h_pair_k), both into the half's accumulator, whose
+// rows r and r + 8 then hold the two partial sums of the half's row r
+// (combine_halves).  A 16-byte piece per lane of a whole line per instruction
+// streams HBM faster than a 64-byte piece of each of 16 rows, and the
+// streaming cache policy helps it further (it slows the 64-byte pieces).
+template <int MPI, int KS>
+__device__ __forceinline__ void load_w_lines(WStage<MPI, KS>& s, const uint16_t* (&wrow)[MPI][2],
+                                             int it, int ks0, int lane, int d) {
+#pragma unroll
+    for (int p = 0; p < KS / 2; ++p) {
+        const int k = (ks0 + it * KS + 2 * p) * 32 + (lane >> 3) * 8;
+        const int kc = k < d ? k : d - 8;   // the matching H fragment is zero
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) s.w[j][2 * p + h] = load_bf16x8_nt(wrow[j][h] + kc);
+    }
+}
+
+// Element offset (from k-step 0 of the wave's slice) of this lane's H piece
+// for k-slot group `kg` in k-step ks of the whole-line layout: k-steps 2 q and
+// 2 q + 1 hold the even and odd 16-byte pieces of the pair's 64 k.
+__device__ __forceinline__ int h_pair_k(int ks, int kg) {
+    return (ks & ~1) * 32 + kg * 16 + (ks & 1) * 8;
+}
+
+// The A operand of one whole-line load split by piece parity.
+__device__ __forceinline__ void split_pieces(bf16x8 a, uint32_t even, bf16x8& ae, bf16x8& ao) {
+    const u32x4 v = __builtin_bit_cast(u32x4, a);
+    ae = __builtin_bit_cast(bf16x8, v & even);
+    ao = __builtin_bit_cast(bf16x8, v & ~even);
+}
+
+template <int NB, int MPI, int KS, int HK>
+__device__ __forceinline__ void mfma_w_lines(f32x4 (&acc)[MPI][2][NB], const WStage<MPI, KS>& s,
+                                             const bf16x8 (&h)[NB][HK], int it, uint32_t even) {
+#pragma unroll
+    for (int p = 0; p < KS / 2; ++p) {
+        const int ks = it * KS + 2 * p + 1 < HK ? it * KS + 2 * p : HK - 2;
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                bf16x8 ae, ao;
+                split_pieces(s.w[j][2 * p + hh], even, ae, ao);
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    acc[j][hh][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, h[n][ks],
+                                                                            acc[j][hh][n], 0, 0, 0);
+                    acc[j][hh][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, h[n][ks + 1],
+                                                                            acc[j][hh][n], 0, 0, 0);
+                }
+            }
+    }
+}
+
+template <int NB, int MPI, int KS, int HK>
+__device__ __forceinline__ void mfma_w_lines_lds(f32x4 (&acc)[MPI][2][NB],
+                                                 const WStage<MPI, KS>& s, const bf16x8* hl,
+                                                 int it, uint32_t even) {
+#pragma unroll
+    for (int p = 0; p < KS / 2; ++p) {
+        const int q = it * KS + 2 * p - HK;
+        bf16x8 he[NB], ho[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            he[n] = hl[(q * NB + n) * 64];
+            ho[n] = hl[((q + 1) * NB + n) * 64];
+        }
+#pragma unroll
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                bf16x8 ae, ao;
+                split_pieces(s.w[j][2 * p + hh], even, ae, ao);
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    acc[j][hh][n] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, he[n], acc[j][hh][n], 0, 0, 0);
+                    acc[j][hh][n] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, ho[n], acc[j][hh][n], 0, 0, 0);
+                }
+            }
+    }
+}
+
+// The block's tile in the usual MFMA output layout from the two halves'
+// accumulators: lanes 0-31 of half h hold its rows' even-piece sums and lanes
+// 32-63 their odd-piece sums, so one swap of lanes 32-63 of half 0 with lanes
+// 0-31 of half 1 and an add leave rows 0-7 of the block (half 0) in lanes
+// 0-31 and rows 8-15 (half 1) in lanes 32-63.
+__device__ __forceinline__ f32x4 combine_halves(f32x4 a0, f32x4 a1) {
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // (the elements are copied out first: a bit cast of a vector element
+        // in place read element 0 for every i)
+        const float x0 = a0[i], x1 = a1[i];
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x0),
+                                                         __builtin_bit_cast(uint32_t, x1), false,
+                                                         false);
+        r[i] = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+    }
+    return r;
+}
+
 // MFMAs of stage `it` with the H fragments in LDS: k-step it * KS + kk - HK of
 // hl ([HL][NB] fragments, 64 lanes each, this lane's entry).
 template <int NB, int MPI, int KS, int HK>
@@ -140,6 +255,8 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                   "stages are processed in pairs");
     constexpr int HT = HK + HL;   // k-steps per wave
     constexpr int NIT = HT / KS;
+    // whole-line W loads (load_w_lines) where the stages hold pairs of k-steps
+    constexpr bool FL = KS % 2 == 0;
     __shared__ ResidentSmem<NB, MPI, NW> sm;
     using HlPart = typename std::conditional<(HL > 0), HlSmem<NB, NW, (HL > 0 ? HL : 1)>, NoHl>::type;
     __shared__ HlPart hls;
@@ -228,13 +345,14 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             const uint16_t* hrow = a.H + (size_t)(b < a.B ? b : a.B - 1) * a.d;
 #pragma unroll
             for (int s = 0; s < HK; ++s) {
-                const int k = (ks0 + s) * 32 + kg * 8;
+                const int k = FL ? ks0 * 32 + h_pair_k(s, kg) : (ks0 + s) * 32 + kg * 8;
                 hres[n][s] = load_bf16x8(k < a.d ? hrow + k : zero);
             }
             if constexpr (HL > 0) {
 #pragma unroll
                 for (int s = 0; s < HL; ++s) {
-                    const int k = (ks0 + HK + s) * 32 + kg * 8;
+                    const int k =
+                        FL ? ks0 * 32 + h_pair_k(HK + s, kg) : (ks0 + HK + s) * 32 + kg * 8;
                     hls.h[wave][s][n][lane] = load_bf16x8(k < a.d ? hrow + k : zero);
                 }
             }
@@ -245,13 +363,37 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
     const int ncol = wave % NB;
     const ColCtx cc = col_ctx(a, bbase + ncol * 16 + r16);
     WStage<MPI, KS> sa, sb;
-    const uint16_t* wrow[MPI];
-    const uint16_t* wnext[MPI];
+    // rows of this lane's loads: row r16 of each block, or (whole lines)
+    // rows lane & 7 and 8 + (lane & 7)
+    const uint16_t* wrow[MPI][FL ? 2 : 1];
+    const uint16_t* wnext[MPI][FL ? 2 : 1];
+    auto rows_of = [&](const uint16_t* (&dst)[MPI][FL ? 2 : 1], const Group& gr)
+                       __attribute__((always_inline)) {
+        const uint16_t* t[MPI];
+#pragma unroll
+        for (int h = 0; h < (FL ? 2 : 1); ++h) {
+            group_rows<MPI>(t, a.W, gr, FL ? 8 * h + (lane & 7) : r16, a.V, a.d);
+#pragma unroll
+            for (int j = 0; j < MPI; ++j) dst[j][h] = t[j];
+        }
+    };
+    auto load_stage = [&](WStage<MPI, KS>& st, const uint16_t* (&rows)[MPI][FL ? 2 : 1], int it)
+                          __attribute__((always_inline)) {
+        if constexpr (FL) {
+            load_w_lines<MPI, KS>(st, rows, it, ks0, lane, a.d);
+        } else {
+            const uint16_t* t[MPI];
+#pragma unroll
+            for (int j = 0; j < MPI; ++j) t[j] = rows[j][0];
+            load_w<MPI, KS>(st, t, it, ks0, kg, a.d);
+        }
+    };
+    const uint32_t even = ((lane >> 3) & 1) ? 0u : ~0u;   // whole lines: even pieces
     // (groups never end at a tile: records are per block)
     constexpr int kNoSeg = INT32_MAX / 2;
     Group cur = group_at<MPI>(mb0, mb1, kNoSeg);
-    group_rows<MPI>(wrow, a.W, cur, r16, a.V, a.d);
-    load_w<MPI, KS>(sa, wrow, 0, ks0, kg, a.d);
+    rows_of(wrow, cur);
+    load_stage(sa, wrow, 0);
 
     uint64_t best = pack_key(-INFINITY, -1);
     Lse lse = lse_empty();
@@ -270,7 +412,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         // after the last group the prefetch re-reads this group's first stage
         // (cache hits, never used), keeping every load unconditional
         const Group nxt = more ? group_at<MPI>(gnext, mb1, kNoSeg) : cur;
-        group_rows<MPI>(wnext, a.W, nxt, r16, a.V, a.d);
+        rows_of(wnext, nxt);
         // the ticket for the unit of group i + 2 (top-k: only while the row
         // store has room for it)
         const bool take = grabbing && more && gi + 2 >= a.dyn_k0 &&
@@ -279,30 +421,41 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
             ticket = (unsigned int)__hip_atomic_fetch_add(&a.sched->word, 1ull, __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT);
 
-        f32x4 acc[MPI][NB];
+        // (whole lines: an accumulator per half block)
+        f32x4 acc[MPI][FL ? 2 : 1][NB];
 #pragma unroll
         for (int j = 0; j < MPI; ++j)
 #pragma unroll
-            for (int n = 0; n < NB; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < (FL ? 2 : 1); ++h)
+#pragma unroll
+                for (int n = 0; n < NB; ++n) acc[j][h][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto mfma_stage = [&](const WStage<MPI, KS>& st, int it) __attribute__((always_inline)) {
+            if constexpr (FL) {
+                if (HL == 0 || it * KS < HK)
+                    mfma_w_lines<NB, MPI, KS, HK>(acc, st, hres, it, even);
+                else
+                    mfma_w_lines_lds<NB, MPI, KS, HK>(acc, st, hl, it, even);
+            } else {
+                f32x4 (&a1)[MPI][NB] = *reinterpret_cast<f32x4 (*)[MPI][NB]>(&acc[0][0][0]);
+                if (HL == 0 || it * KS < HK)
+                    mfma_w<NB, MPI, KS, HK>(a1, st, hres, it);
+                else
+                    mfma_w_lds<NB, MPI, KS, HK>(a1, st, hl, it);
+            }
+        };
         // sched_barrier keeps the prefetch ahead of the MFMAs it overlaps
 #pragma unroll
         for (int it = 0; it < NIT; it += 2) {
-            load_w<MPI, KS>(sb, wrow, it + 1, ks0, kg, a.d);
+            load_stage(sb, wrow, it + 1);
             __builtin_amdgcn_sched_barrier(0);
-            if (HL == 0 || it * KS < HK)
-                mfma_w<NB, MPI, KS, HK>(acc, sa, hres, it);
-            else
-                mfma_w_lds<NB, MPI, KS, HK>(acc, sa, hl, it);
+            mfma_stage(sa, it);
             __builtin_amdgcn_sched_barrier(0);
             if (it + 2 < NIT)
-                load_w<MPI, KS>(sa, wrow, it + 2, ks0, kg, a.d);
+                load_stage(sa, wrow, it + 2);
             else
-                load_w<MPI, KS>(sa, wnext, 0, ks0, kg, a.d);
+                load_stage(sa, wnext, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (HL == 0 || (it + 1) * KS < HK)
-                mfma_w<NB, MPI, KS, HK>(acc, sb, hres, it + 1);
-            else
-                mfma_w_lds<NB, MPI, KS, HK>(acc, sb, hl, it + 1);
+            mfma_stage(sb, it + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -310,7 +463,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
 #pragma unroll
         for (int j = 0; j < MPI; ++j)
 #pragma unroll
-            for (int n = 0; n < NB; ++n) sm.red[buf][wave][j][n][lane] = acc[j][n];
+            for (int n = 0; n < NB; ++n)
+                sm.red[buf][wave][j][n][lane] =
+                    FL ? combine_halves(acc[j][0][n], acc[j][FL ? 1 : 0][n]) : acc[j][0][n];
         if (take && threadIdx.x == 0) {   // this group's ticket, back by now
             const int u = a.dyn_k0 * a.G + (int)ticket;
             sm.next_unit[buf] = u < nunits ? u : -1;
@@ -426,7 +581,9 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
         if (!more) break;
         cur = nxt;
 #pragma unroll
-        for (int j = 0; j < MPI; ++j) wrow[j] = wnext[j];
+        for (int j = 0; j < MPI; ++j)
+#pragma unroll
+            for (int h = 0; h < (FL ? 2 : 1); ++h) wrow[j][h] = wnext[j][h];
     }
     if constexpr (VAR == kVarGrouped) {
         // stage 2's per-row [key, count] pairs start cleared (after the walk:
