@@ -502,15 +502,32 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                     for (int r = 0; r < 4; ++r)
                         if (row0 + r < a.V) dst[row0 + r] = v[r];
                 }
-            } else if constexpr (VAR == kVarTopk) {
-                float x[4];
-                lane_x(a, cc, v, row0, true, allow_word(a, cc, row0, true), x);
-                *reinterpret_cast<uint4*>(&tk.u[ncol * 16 + r16][(stored + j) * kMBlock + 4 * kg]) =
-                    uint4{topk_order(x[0]), topk_order(x[1]), topk_order(x[2]), topk_order(x[3])};
             } else {
+                // The allow word is read only when a mask is given, in a copy
+                // of the epilogue of its own: where both cases shared one
+                // copy, the wait for that read was on the common path, and a
+                // wait for one load waits for every load issued before it,
+                // the next group's prefetch included.
+                auto scores = [&](auto masked, float (&x)[4], float (&s)[4])
+                                  __attribute__((always_inline)) {
+                    const uint32_t word =
+                        decltype(masked)::value ? allow_word(a, cc, row0, true) : ~0u;
+                    if constexpr (VAR == kVarTopk)
+                        lane_x(a, cc, v, row0, true, word, x);
+                    else
+                        lane_scores(a, cc, v, row0, true, word, x, s);
+                };
                 float x[4], s[4];
-                lane_scores(a, cc, v, row0, true, x, s);
-                if constexpr (VAR == kVarGrouped) {
+                if (a.allow)   // uniform
+                    scores(std::true_type{}, x, s);
+                else
+                    scores(std::false_type{}, x, s);
+                if constexpr (VAR == kVarTopk) {
+                    *reinterpret_cast<uint4*>(
+                        &tk.u[ncol * 16 + r16][(stored + j) * kMBlock + 4 * kg]) =
+                        uint4{topk_order(x[0]), topk_order(x[1]), topk_order(x[2]),
+                              topk_order(x[3])};
+                } else if constexpr (VAR == kVarGrouped) {
                     // the block's record for these 16 columns: this wave alone
                     // holds them (no barrier), into the store's next slot
                     uint64_t kb = pack_key(-INFINITY, -1);
