@@ -555,3 +555,23 @@ def test_flat_histogram_chi_square():
     ptk = chi_square_p(np.concatenate(top), pk)
     log(f"chi-square p: top-8 {ptk:.3f}")
     assert ptk > 0.01
+
+
+def test_read_probes_read_every_word_once():
+    """Both HBM read probes (plain and nontemporal loads) read each 32-bit word
+    of the buffer exactly once: the XOR over the sink equals the XOR of the
+    buffer's words, with a grid-stride tail (a size that is not a multiple of
+    the grid's loads per trip)."""
+    t = torch()
+    rng = np.random.default_rng(7)
+    nbytes = (1 << 20) + 48 * 16
+    words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = t.from_numpy(words.view(np.int32).copy()).cuda()
+    want = np.bitwise_xor.reduce(words)
+    for grid in (8, 37):
+        for probe in (fs.fs_debug_read_probe, fs.fs_debug_read_probe_nt):
+            sink = t.zeros(grid * 256, dtype=t.int32, device="cuda")
+            fs.check(probe(buf, nbytes, sink, grid), probe.__name__)
+            t.cuda.synchronize()
+            got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+            assert got == want, (probe.__name__, grid)
