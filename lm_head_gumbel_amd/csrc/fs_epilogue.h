@@ -107,6 +107,11 @@ __device__ __forceinline__ void lane_x(const Stage1Args& a, const ColCtx& c, f32
 }
 
 // x as above and the noisy scores s = x + Gumbel (s = x for greedy columns).
+// UKEY: calls with one key (no per-row seeds) take the key from the call, so
+// that its schedule of round keys stays on the scalar unit (the per-column
+// copy would take vector adds); a kernel whose registers are short keeps the
+// per-column key.
+template <bool UKEY = false>
 __device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c, f32x4 v,
                                             int row0, bool blk_ok, uint32_t word, float (&x)[4],
                                             float (&s)[4]) {
@@ -115,9 +120,15 @@ __device__ __forceinline__ void lane_scores(const Stage1Args& a, const ColCtx& c
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = x[r];
     if (!c.greedy && blk_ok && c.ok) {
-        const uint4 rw = philox4x32_10(
-            make_uint4((uint32_t)gid0 >> 2, (uint32_t)c.col, c.key.step, kStreamToken), c.key.k0,
-            c.key.k1);
+        const uint4 ctr = make_uint4((uint32_t)gid0 >> 2, (uint32_t)c.col, c.key.step, kStreamToken);
+        uint4 rw;
+        if (UKEY && a.noise.seeds == nullptr) {   // uniform
+            uint32_t k0 = a.noise.k0, k1 = a.noise.k1;
+            asm volatile("" : "+s"(k0), "+s"(k1));
+            rw = philox4x32_10(ctr, k0, k1);
+        } else {
+            rw = philox4x32_10(ctr, c.key.k0, c.key.k1);
+        }
         s[0] += gumbel_from_word(rw.x);
         s[1] += gumbel_from_word(rw.y);
         s[2] += gumbel_from_word(rw.z);

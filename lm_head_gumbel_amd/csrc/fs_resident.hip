@@ -515,7 +515,7 @@ __global__ __launch_bounds__(64 * NW) void resident_kernel(Stage1Args a) {
                     if constexpr (VAR == kVarTopk)
                         lane_x(a, cc, v, row0, true, word, x);
                     else
-                        lane_scores(a, cc, v, row0, true, word, x, s);
+                        lane_scores<true>(a, cc, v, row0, true, word, x, s);
                 };
                 float x[4], s[4];
                 if (a.allow)   // uniform
